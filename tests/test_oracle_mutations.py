@@ -1,0 +1,114 @@
+"""Planted mistakes in copies of the oracle must fail its pins (CPU only).
+
+Each case copies the oracle package to a temporary directory, changes one
+line the way a plausible slip would (a dropped term, a wrong sign or index,
+a max for a sum), imports the copy and runs the pin that should catch it.
+"""
+
+import importlib.util
+import os
+import shutil
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+
+
+def _mutant(tmp_path, name, fname, old, new):
+    dst = tmp_path / name
+    shutil.copytree(ORACLE_DIR, dst)
+    path = dst / fname
+    src = path.read_text()
+    assert src.count(old) == 1, (fname, old)
+    path.write_text(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location(name, dst / "__init__.py", submodule_search_locations=[str(dst)])
+    mod = importlib.util.module_from_spec(spec)
+    sys.modules[name] = mod
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _pin_budget(orc):
+    return orc.budget(512, 1, 20, 16) == 26 and all(
+        orc.budget(L, 1, 20, 64) * 20 >= L for L in range(0, 3000))
+
+
+def _pin_select(orc):
+    sc = np.array([0.5, 0.9, 0.9, 0.1, 0.0, 0.0], dtype=np.float32)
+    ok = orc.select(sc, 6, 1, 2, 2).tolist() == [1, 4, 5]
+    rng = np.random.default_rng(2)
+    sc = rng.integers(0, 20, size=900).astype(np.float32) / 4
+    cand = np.arange(900 - 64)
+    order = np.lexsort((cand, -sc[:900 - 64].astype(np.float64)))
+    ref = np.sort(np.concatenate([order[:orc.budget(900, 1, 20, 64) - 64], np.arange(900 - 64, 900)]))
+    return ok and np.array_equal(orc.select(sc, 900, 1, 20, 64), ref)
+
+
+def _pin_verify(orc):
+    from s3r_inputs import get_config, make_batch
+    cfg = get_config(1, B=1, Hq=4, Hkv=2, D=16, k=3, lengths=("fixed", 50))
+    bt = make_batch(cfg, parts=("kv", "q"))
+    S = int(bt.seq_len[0])
+    o, lse, sc = orc.verify(bt.q_verify[0], bt.k_pages, bt.v_pages, bt.block_table[0], S, 3, float(bt.scale))
+    K = np.stack([orc.gather(bt.k_pages, bt.block_table[0], kv, np.arange(S)) for kv in range(2)])
+    V = np.stack([orc.gather(bt.v_pages, bt.block_table[0], kv, np.arange(S)) for kv in range(2)])
+    q = torch.tensor(bt.q_verify[0].astype(np.float64)).permute(1, 0, 2)
+    Kt, Vt = torch.tensor(K).repeat_interleave(2, 0), torch.tensor(V).repeat_interleave(2, 0)
+    mask = torch.arange(S)[None, :] <= (torch.arange(4)[:, None] + S - 4)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, Kt, Vt, attn_mask=mask, scale=float(bt.scale))
+    ok_o = np.allclose(o.transpose(1, 0, 2), ref.numpy(), rtol=1e-10, atol=1e-12)
+    ok_sum = np.allclose(sc.sum(axis=1), 2 * 4, rtol=1e-12)
+    return ok_o and ok_sum
+
+
+def _pin_decode(orc):
+    from s3r_inputs import get_config, make_batch
+    cfg = get_config(1, B=1, Hq=4, Hkv=2, D=16, k=2, lengths=("fixed", 40))
+    bt = make_batch(cfg, parts=("kv", "q"))
+    L = 40
+    idx = [np.arange(L), np.arange(L)]
+    o, lse = orc.sparse_decode(bt.q_draft[1, 0], bt.k_pages, bt.v_pages, bt.block_table[0], idx, L, L, L + 2, float(bt.scale))
+    K = np.stack([orc.gather(bt.k_pages, bt.block_table[0], kv, np.arange(L + 2)) for kv in range(2)])
+    V = np.stack([orc.gather(bt.v_pages, bt.block_table[0], kv, np.arange(L + 2)) for kv in range(2)])
+    q = torch.tensor(bt.q_draft[1, 0].astype(np.float64))[:, None, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, torch.tensor(K).repeat_interleave(2, 0), torch.tensor(V).repeat_interleave(2, 0), scale=float(bt.scale))
+    return np.allclose(o, ref[:, 0].numpy(), rtol=1e-10, atol=1e-12)
+
+
+def _pin_sampling(orc):
+    from tests.test_oracle_sampling import _chi2_run
+    import importlib
+    mod = importlib.import_module(orc.__name__ + ".sampling")
+    return min(_chi2_run(mod.spec_decide, n=100_000)) > 1e-3
+
+
+MUTANTS = [
+    ("budget.py", "frac = -((-s_num * L) // s_den)", "frac = (s_num * L) // s_den", _pin_budget),
+    ("budget.py", "return min(L, max(newest, frac))", "return min(L, newest + frac)", _pin_budget),
+    ("select.py", "key=lambda j: (-vals[j], j)", "key=lambda j: (-vals[j], -j)", _pin_select),
+    ("select.py", "key=lambda j: (-vals[j], j)", "key=lambda j: (vals[j], j)", _pin_select),
+    ("attention.py", "last = seq_len - (k + 1) + i", "last = seq_len - (k + 1) + i - 1", _pin_verify),
+    ("attention.py", "scores[kv, :last + 1] += p", "scores[kv, :last + 1] = np.maximum(scores[kv, :last + 1], p)", _pin_verify),
+    ("attention.py", "logits = float(scale) * (K @ q)", "logits = K @ q", _pin_verify),
+    ("attention.py", "for h in range(kv * G, (kv + 1) * G):", "for h in range(kv, kv + G):", _pin_verify),
+    ("attention.py", "kv = h // G\n        pos", "kv = h % Hkv\n        pos", _pin_decode),
+    ("attention.py", "np.arange(L, cur, dtype=np.int64)])", "np.arange(L, cur - 1, dtype=np.int64)])", _pin_decode),
+    ("sampling.py", "if p >= q or float(u[i]) * q < p:", "if p >= q or float(u[i]) * p < q:", _pin_sampling),
+    ("sampling.py", "tokens[k] = invcdf(p_rows[k], u[k])", "tokens[k] = invcdf(p_rows[k - 1], u[k])", _pin_sampling),
+]
+
+
+def test_unmutated_oracle_passes_pins():
+    import oracle
+    assert _pin_budget(oracle) and _pin_select(oracle) and _pin_verify(oracle) and _pin_decode(oracle)
+
+
+@pytest.mark.parametrize("case", range(len(MUTANTS)))
+def test_mutant_is_caught(tmp_path, case):
+    fname, old, new, pin = MUTANTS[case]
+    mod = _mutant(tmp_path, f"oracle_mutant_{case}", fname, old, new)
+    assert not pin(mod)
