@@ -1,0 +1,239 @@
+/*
+ * s3r.h - C ABI of the S3R (self-sparse speculative rollouts) attention and
+ * sampling step on AMD Instinct MI355X (gfx950).
+ *
+ * One round of the method for a batch of sequences is four calls on one
+ * stream:
+ *   s3r_select              keep the newest window plus the positions the last
+ *                           verification attended to most (budget s * L);
+ *   s3r_sparse_decode_attn  one draft step: single-query attention over the
+ *                           kept positions plus this round's positions
+ *                           (called k times per round);
+ *   s3r_verify_attn         dense attention of the k + 1 block queries over
+ *                           the complete paged cache, causal inside the block;
+ *                           also emits the next round's selector scores;
+ *   s3r_spec_sample         exact speculative sampling: accept each draft with
+ *                           probability min(1, p/q), else draw the correction
+ *                           from the normalised residual max(0, p - q); a fully
+ *                           accepted round adds a bonus token drawn from p.
+ *
+ * Sources (web pages about the method, cited by title and section):
+ *   [news]      "Long-context RL training stops waiting on autoregressive
+ *               rollouts: sparse self-drafting plus full-attention verification
+ *               lifts throughput 1.39x" (ai4snews), Interpretation;
+ *   [listing]   "S^3R: Fast and Faithful RL Rollouts via Self-Sparse Speculative
+ *               Decoding" (thelatestinai paper page), Abstract, Tables 4-7;
+ *   [explainer] "S3R - Self-sparse speculative rollouts for RL - What does it
+ *               mean?" (learnaivisually), Jargon and the mechanism paragraphs.
+ *
+ * Conventions shared by all calls
+ *   - Every pointer argument is DEVICE memory owned by the caller, except the
+ *     s3r_paged_kv descriptor itself, which is a HOST struct read during the
+ *     call (its pointer members are device pointers). The library never
+ *     allocates or frees memory and keeps no state between calls.
+ *   - Calls are asynchronous on `stream`; a call returns after enqueuing its
+ *     kernels. Outputs are valid once the stream reaches that point.
+ *   - Per-sequence values live in device arrays; host scalars give the shape
+ *     bounds (max_*, *_cap) used for validation, grid and workspace sizing.
+ *     Device values beyond the host bounds are undefined behaviour.
+ *   - The workspace of a call is caller memory of at least the size the
+ *     matching *_workspace_bytes() returns; its content on entry does not
+ *     matter and on exit is unspecified. Concurrent calls must not share one.
+ *   - Identical inputs give bit-identical outputs (no float atomics; fixed
+ *     reduction orders).
+ *   - Status codes: S3R_ERR_INVALID_ARG for null required pointers,
+ *     non-positive sizes, Hq not a multiple of Hkv, k outside [0, 15],
+ *     capacities smaller than the host bounds require, or an invalid budget
+ *     ratio; S3R_ERR_UNSUPPORTED for page_size != 16, head_dim not 64 or 128,
+ *     or shapes a kernel does not cover (listed per call); S3R_ERR_WORKSPACE
+ *     for a workspace smaller than required; S3R_ERR_HIP when a kernel launch
+ *     fails. On any error nothing is enqueued.
+ *
+ * Paged KV cache layout: k_pages and v_pages are
+ * [num_pages][num_kv_heads][page_size][head_dim] in `dtype`; position j of
+ * sequence b is slot j % page_size of physical page
+ * block_table[b * max_pages_per_seq + j / page_size]. Query head h reads KV
+ * head h / (Hq / Hkv) (grouped-query attention).
+ */
+#ifndef S3R_H
+#define S3R_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  S3R_OK = 0,
+  S3R_ERR_INVALID_ARG = 1,
+  S3R_ERR_UNSUPPORTED = 2,
+  S3R_ERR_WORKSPACE = 3,
+  S3R_ERR_HIP = 4
+} s3r_status;
+
+typedef enum { S3R_F32 = 0, S3R_BF16 = 1 } s3r_dtype;
+
+typedef struct {
+  const void* k_pages;          /* device, [num_pages][num_kv_heads][page_size][head_dim] */
+  const void* v_pages;          /* device, same layout as k_pages */
+  const int32_t* block_table;   /* device, [B][max_pages_per_seq] physical page ids */
+  int32_t num_pages;
+  int32_t max_pages_per_seq;
+  int32_t num_kv_heads;
+  int32_t head_dim;             /* 64 or 128 */
+  int32_t page_size;            /* 16 */
+  int32_t dtype;                /* s3r_dtype of K, V and the queries */
+} s3r_paged_kv;
+
+/* Human-readable name of a status code (static string). */
+const char* s3r_status_string(s3r_status status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t s3r_version(void);
+
+/*
+ * Selection budget for a context of L committed positions (host helper):
+ * min(L, max(min(window, L), ceil(s_num * L / s_den))). [explainer], Jargon,
+ * "Sparse attention budget": a fraction s of the cached positions (0.05 by
+ * default) made of the newest positions plus the most attended ones; the
+ * ratio is exact integers and the newest window counts inside the budget.
+ * Returns -1 on invalid arguments (L < 0, s_den <= 0, s_num < 0,
+ * s_num > s_den, window < 0). Use it to size nsel_cap from a host bound.
+ */
+int32_t s3r_budget(int32_t L, int32_t s_num, int32_t s_den, int32_t window);
+
+/*
+ * s3r_select - newest window plus top-scoring older positions, per (sequence,
+ * KV head). [explainer], mechanism paragraph: the drafter reads the newest
+ * positions plus the top-scoring ones from the verifier's last attention pass,
+ * refreshed after every round; [news], Interpretation: drafting selects a
+ * small set of historical KV entries using attention scores.
+ *
+ *   scores    device f32 [B][Hkv][score_stride]: score of position j of each
+ *             (sequence, KV head); only j < ctx_len[b] is read. NaN scores are
+ *             undefined behaviour; +inf ranks highest; -0.0 equals +0.0.
+ *   ctx_len   device i32 [B]: committed context L_b, 1 <= L_b <= max_ctx_len.
+ *   s_num/s_den, window: budget as in s3r_budget (0 <= s_num <= s_den).
+ *   idx       device i32 [B][Hkv][nsel_cap] output: the n_sel[b] kept positions
+ *             in ascending order (window [L_b - min(window, L_b), L_b) plus the
+ *             top n_sel - window older positions by score, ties to the lower
+ *             position). Entries at and beyond n_sel[b] are not written.
+ *   n_sel     device i32 [B] output: s3r_budget(L_b, s_num, s_den, window).
+ *   nsel_cap  >= s3r_budget(max_ctx_len, ...) (INVALID_ARG otherwise);
+ *   score_stride >= max_ctx_len.
+ * No workspace. UNSUPPORTED: none.
+ */
+s3r_status s3r_select(const float* scores, int32_t score_stride, const int32_t* ctx_len,
+                      int32_t B, int32_t Hkv, int32_t max_ctx_len, int32_t s_num, int32_t s_den,
+                      int32_t window, int32_t* idx, int32_t nsel_cap, int32_t* n_sel,
+                      hipStream_t stream);
+
+/*
+ * s3r_sparse_decode_attn - one sparse draft step. [news], Interpretation:
+ * drafting uses the policy's own weights and attends to the selected KV
+ * entries; [explainer], mechanism paragraph: k fast draft steps from the
+ * sticky-noted pages.
+ *
+ * For sequence b and query head h (KV head kv = h / (Hq / Hkv)) the attended
+ * set is S = idx[b][kv][0 .. n_sel[b]) united with [sel_len[b], cur_len[b])
+ * (this round's positions, the querying token's own included), and
+ *   out[b][h] = softmax(scale * q[b][h] . K_S) V_S,
+ *   lse[b][h] = log sum_S exp(scale * q[b][h] . K_j)  (natural log).
+ * An empty S gives out = 0 and lse = -inf.
+ *
+ *   q         device [B][Hq][head_dim] in kv->dtype.
+ *   idx, nsel_cap, n_sel: as written by s3r_select (positions < sel_len[b]).
+ *   sel_len   device i32 [B]: L_b, the context length the selection used.
+ *   cur_len   device i32 [B]: L_b + j at draft step j (1..k); K/V of positions
+ *             [L_b, cur_len) must already be in the cache.
+ *   max_attend host bound on n_sel[b] + cur_len[b] - sel_len[b] (>= 1).
+ *   out       device f32 [B][Hq][head_dim]; lse device f32 [B][Hq] or NULL.
+ *   ws        workspace of s3r_sparse_decode_workspace_bytes(B, Hq, head_dim,
+ *             max_attend) bytes.
+ * UNSUPPORTED: Hq / Hkv > 16.
+ */
+size_t s3r_sparse_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head_dim, int32_t max_attend);
+s3r_status s3r_sparse_decode_attn(const void* q, const s3r_paged_kv* kv, const int32_t* idx,
+                                  int32_t nsel_cap, const int32_t* n_sel, const int32_t* sel_len,
+                                  const int32_t* cur_len, int32_t B, int32_t Hq, float scale,
+                                  int32_t max_attend, float* out, float* lse, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
+
+/*
+ * s3r_verify_attn - dense block verification. [news], Interpretation:
+ * verification recomputes the proposed block against the complete historical
+ * KV cache; [listing], Abstract: responses are generated through
+ * full-attention verification.
+ *
+ * The block is the last k + 1 positions of each sequence's cache: row i
+ * (0..k) sits at position P_i = seq_len[b] - (k + 1) + i and attends to
+ * [0, P_i]:
+ *   out[b][i][h] = softmax(scale * q[b][i][h] . K_[0,P_i]) V_[0,P_i],
+ *   lse[b][i][h] = the natural-log normaliser of that row.
+ * Scores for the next selection (reading adopted: a sum over the G query
+ * heads of the KV head and over all k + 1 rows of each row's normalised
+ * probability):
+ *   scores[b][kv][j] = sum_{h in group(kv)} sum_{i : j <= P_i} prob_{b,i,h}(j)
+ * for j < seq_len[b]; entries at and beyond seq_len[b] are not written. The
+ * scores of one (b, kv) sum to G (k + 1).
+ *
+ *   q         device [B][k+1][Hq][head_dim] in kv->dtype.
+ *   seq_len   device i32 [B]: cache length including the block,
+ *             k + 1 <= seq_len[b] <= max_seq_len.
+ *   out       device f32 [B][k+1][Hq][head_dim]; lse device f32 [B][k+1][Hq]
+ *             or NULL; scores device f32 [B][Hkv][score_stride] or NULL
+ *             (score_stride >= max_seq_len when scores is not NULL).
+ *   ws        workspace of s3r_verify_workspace_bytes(...) bytes.
+ * UNSUPPORTED: (k + 1) * Hq / Hkv > 64 rows per KV head.
+ */
+size_t s3r_verify_workspace_bytes(int32_t B, int32_t k, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                  int32_t dtype, int32_t max_seq_len);
+s3r_status s3r_verify_attn(const void* q, const s3r_paged_kv* kv, const int32_t* seq_len,
+                           int32_t B, int32_t k, int32_t Hq, float scale, int32_t max_seq_len,
+                           float* out, float* lse, float* scores, int32_t score_stride, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/*
+ * s3r_spec_sample - exact speculative sampling with caller-supplied uniforms.
+ * [explainer], Jargon "Exact speculative sampling" and the draft/verify
+ * illustration (first mismatch replaced, the rest discarded); [news],
+ * Interpretation (accept candidates or draw from the residual); [listing],
+ * Table 7 caption (a fully accepted round yields k + 1 tokens).
+ *
+ * For each sequence b, in float64 from the float32 logits:
+ *   p_i = softmax(target_logits[b][i] / T), i = 0..k;
+ *   q_i = softmax(draft_logits[b][i] / T), i = 0..k-1;
+ *   draft i (x = draft_tokens[b][i]) is accepted iff p_i(x) >= q_i(x) or
+ *   uniforms[b][i] * q_i(x) < p_i(x); at the first reject i* the correction
+ *   is drawn from max(0, p_i* - q_i*) (from p_i* if that residual is all zero);
+ *   if every draft is accepted the bonus is drawn from p_k. Draws use the
+ *   inverse CDF in token order with the single uniform uniforms[b][k]:
+ *   y = min{y : sum_{y' <= y} w(y') > u * sum(w)} (the last y with w > 0 if
+ *   rounding leaves none). T = 0 is greedy: accept iff x is the first argmax
+ *   of target row i; correction and bonus are that argmax.
+ *
+ *   target_logits device f32 [B][k+1][V]; draft_logits device f32 [B][k][V]
+ *   (may be NULL when k = 0); draft_tokens device i32 [B][k] in [0, V);
+ *   uniforms device f32 [B][k+1] in [0, 1); temperature >= 0 (host).
+ *   tokens    device i32 [B][k+1] output: the n_out[b] emitted tokens, then -1.
+ *   n_out     device i32 [B] output: accepted drafts + 1.
+ *   accepted  device i8 [B][k] output or NULL: 1 accepted, 0 the first
+ *             reject, -1 not reached.
+ *   ws        workspace of s3r_spec_sample_workspace_bytes(B, k, V) bytes.
+ */
+size_t s3r_spec_sample_workspace_bytes(int32_t B, int32_t k, int32_t V);
+s3r_status s3r_spec_sample(const float* target_logits, const float* draft_logits,
+                           const int32_t* draft_tokens, const float* uniforms, int32_t B,
+                           int32_t k, int32_t V, float temperature, int32_t* tokens,
+                           int32_t* n_out, int8_t* accepted, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* S3R_H */

@@ -48,7 +48,13 @@ def gather(pages: np.ndarray, bt_row: np.ndarray, kv_head: int, positions) -> np
 
 
 def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
-    """softmax(scale * K q) V and its log-sum-exp (natural log)."""
+    """softmax(scale * K q) V and its log-sum-exp (natural log).
+
+    An empty set (a degenerate budget of zero with no draft positions yet)
+    gives a zero output and -inf (reading: the sum over no positions).
+    """
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[1]), -np.inf, np.zeros(0)
     logits = float(scale) * (K @ q)
     m = logits.max()
     e = np.exp(logits - m)

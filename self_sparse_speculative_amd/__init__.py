@@ -1,0 +1,25 @@
+"""S3R (self-sparse speculative rollouts) attention-and-sampling step on MI355X.
+
+The product is libs3r.so (HIP kernels for gfx950 behind the C ABI in
+include/s3r.h); this package builds it (``build.py``) and binds it
+(``s3r.py``). Importing the package does not load the library; the first
+call does, and raises if it has not been built.
+"""
+
+from .s3r import (  # noqa: F401
+    EXPORTED,
+    PagedKV,
+    S3RError,
+    Workspace,
+    budget,
+    lib_path,
+    load,
+    select,
+    sparse_decode_attn,
+    sparse_decode_workspace_bytes,
+    spec_sample,
+    spec_sample_workspace_bytes,
+    status_string,
+    verify_attn,
+    verify_workspace_bytes,
+)

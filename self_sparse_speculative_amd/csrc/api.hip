@@ -1,0 +1,149 @@
+// C ABI of the S3R library: argument validation, workspace sizing and
+// dispatch to the kernels. Every entry point validates all host-side
+// arguments before enqueuing anything and returns a status code.
+
+#include <math.h>
+
+#include "../../include/s3r.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kMaxK = 15;
+constexpr int kMaxRows = 64;
+
+bool kv_ok(const s3r_paged_kv* kv) {
+  return kv != nullptr && kv->k_pages != nullptr && kv->v_pages != nullptr &&
+         kv->block_table != nullptr && kv->num_pages >= 1 && kv->max_pages_per_seq >= 1 &&
+         kv->num_kv_heads >= 1 && kv->head_dim >= 1 && kv->page_size >= 1 &&
+         (kv->dtype == S3R_F32 || kv->dtype == S3R_BF16);
+}
+
+s3r_status kv_supported(const s3r_paged_kv* kv) {
+  if (kv->page_size != 16) return S3R_ERR_UNSUPPORTED;
+  if (kv->head_dim != 64 && kv->head_dim != 128) return S3R_ERR_UNSUPPORTED;
+  return S3R_OK;
+}
+
+s3r_status from_hip(hipError_t e) { return e == hipSuccess ? S3R_OK : S3R_ERR_HIP; }
+
+long long budget_ll(long long L, long long s_num, long long s_den, long long window) {
+  const long long newest = window < L ? window : L;
+  const long long frac = (s_num * L + s_den - 1) / s_den;
+  long long n = newest > frac ? newest : frac;
+  return n < L ? n : L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* s3r_status_string(s3r_status status) {
+  switch (status) {
+    case S3R_OK: return "S3R_OK";
+    case S3R_ERR_INVALID_ARG: return "S3R_ERR_INVALID_ARG: invalid argument";
+    case S3R_ERR_UNSUPPORTED: return "S3R_ERR_UNSUPPORTED: shape or dtype without a kernel";
+    case S3R_ERR_WORKSPACE: return "S3R_ERR_WORKSPACE: workspace too small";
+    case S3R_ERR_HIP: return "S3R_ERR_HIP: kernel launch failed";
+  }
+  return "S3R: unknown status";
+}
+
+int32_t s3r_version(void) { return 100; }
+
+int32_t s3r_budget(int32_t L, int32_t s_num, int32_t s_den, int32_t window) {
+  if (L < 0 || s_den <= 0 || s_num < 0 || s_num > s_den || window < 0) return -1;
+  return (int32_t)budget_ll(L, s_num, s_den, window);
+}
+
+s3r_status s3r_select(const float* scores, int32_t score_stride, const int32_t* ctx_len, int32_t B,
+                      int32_t Hkv, int32_t max_ctx_len, int32_t s_num, int32_t s_den,
+                      int32_t window, int32_t* idx, int32_t nsel_cap, int32_t* n_sel,
+                      hipStream_t stream) {
+  if (!scores || !ctx_len || !idx || !n_sel) return S3R_ERR_INVALID_ARG;
+  if (B < 1 || Hkv < 1 || max_ctx_len < 1 || B > 65535 || Hkv > 65535) return S3R_ERR_INVALID_ARG;
+  if (s_den <= 0 || s_num < 0 || s_num > s_den || window < 0) return S3R_ERR_INVALID_ARG;
+  if (score_stride < max_ctx_len) return S3R_ERR_INVALID_ARG;
+  if (nsel_cap < 1 || nsel_cap < budget_ll(max_ctx_len, s_num, s_den, window)) return S3R_ERR_INVALID_ARG;
+  return from_hip(s3r::launch_select(scores, score_stride, ctx_len, B, Hkv, max_ctx_len, s_num,
+                                     s_den, window, idx, nsel_cap, n_sel, stream));
+}
+
+size_t s3r_sparse_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head_dim, int32_t max_attend) {
+  if (B < 1 || Hq < 1 || head_dim < 1 || max_attend < 1) return 0;
+  return s3r::decode_workspace_bytes(B, Hq, head_dim, max_attend);
+}
+
+s3r_status s3r_sparse_decode_attn(const void* q, const s3r_paged_kv* kv, const int32_t* idx,
+                                  int32_t nsel_cap, const int32_t* n_sel, const int32_t* sel_len,
+                                  const int32_t* cur_len, int32_t B, int32_t Hq, float scale,
+                                  int32_t max_attend, float* out, float* lse, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  if (!q || !kv_ok(kv) || !idx || !n_sel || !sel_len || !cur_len || !out) return S3R_ERR_INVALID_ARG;
+  if (B < 1 || Hq < 1 || nsel_cap < 1 || max_attend < 1 || B > 65535) return S3R_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return S3R_ERR_INVALID_ARG;
+  const int Hkv = kv->num_kv_heads;
+  if (Hq % Hkv != 0 || Hkv > 65535) return S3R_ERR_INVALID_ARG;
+  s3r_status st = kv_supported(kv);
+  if (st != S3R_OK) return st;
+  const int G = Hq / Hkv;
+  if (!s3r::decode_supported(kv->dtype, kv->head_dim, G)) return S3R_ERR_UNSUPPORTED;
+  const size_t need = s3r::decode_workspace_bytes(B, Hq, kv->head_dim, max_attend);
+  if (ws_bytes < need || (need > 0 && ws == nullptr)) return S3R_ERR_WORKSPACE;
+  return from_hip(s3r::launch_sparse_decode(kv->dtype, kv->head_dim, G, q, kv->k_pages, kv->v_pages,
+                                            kv->block_table, kv->max_pages_per_seq, Hkv, idx,
+                                            nsel_cap, n_sel, sel_len, cur_len, B, scale,
+                                            max_attend, out, lse, ws, stream));
+}
+
+size_t s3r_verify_workspace_bytes(int32_t B, int32_t k, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                  int32_t dtype, int32_t max_seq_len) {
+  if (B < 1 || k < 0 || k > kMaxK || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || head_dim < 1 ||
+      max_seq_len < 1)
+    return 0;
+  return s3r::verify_plan(B, k, Hq, Hkv, head_dim, dtype, max_seq_len).bytes;
+}
+
+s3r_status s3r_verify_attn(const void* q, const s3r_paged_kv* kv, const int32_t* seq_len,
+                           int32_t B, int32_t k, int32_t Hq, float scale, int32_t max_seq_len,
+                           float* out, float* lse, float* scores, int32_t score_stride, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  if (!q || !kv_ok(kv) || !seq_len || !out) return S3R_ERR_INVALID_ARG;
+  if (B < 1 || B > 65535 || Hq < 1 || k < 0 || k > kMaxK || max_seq_len < k + 1) return S3R_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return S3R_ERR_INVALID_ARG;
+  const int Hkv = kv->num_kv_heads;
+  if (Hq % Hkv != 0 || Hkv > 65535) return S3R_ERR_INVALID_ARG;
+  if ((long long)kv->max_pages_per_seq * kv->page_size < max_seq_len) return S3R_ERR_INVALID_ARG;
+  if (scores != nullptr && score_stride < max_seq_len) return S3R_ERR_INVALID_ARG;
+  s3r_status st = kv_supported(kv);
+  if (st != S3R_OK) return st;
+  if ((k + 1) * (Hq / Hkv) > kMaxRows) return S3R_ERR_UNSUPPORTED;
+  const size_t need = s3r::verify_plan(B, k, Hq, Hkv, kv->head_dim, kv->dtype, max_seq_len).bytes;
+  if (ws_bytes < need || ws == nullptr) return S3R_ERR_WORKSPACE;
+  return from_hip(s3r::launch_verify(kv->dtype, kv->head_dim, q, kv->k_pages, kv->v_pages,
+                                     kv->block_table, kv->max_pages_per_seq, Hkv, seq_len, B, k,
+                                     Hq, scale, max_seq_len, out, lse, scores, score_stride, ws,
+                                     stream));
+}
+
+size_t s3r_spec_sample_workspace_bytes(int32_t B, int32_t k, int32_t V) {
+  if (B < 1 || k < 0 || k > kMaxK || V < 1) return 0;
+  return s3r::sample_workspace_bytes(B, k, V);
+}
+
+s3r_status s3r_spec_sample(const float* target_logits, const float* draft_logits,
+                           const int32_t* draft_tokens, const float* uniforms, int32_t B,
+                           int32_t k, int32_t V, float temperature, int32_t* tokens,
+                           int32_t* n_out, int8_t* accepted, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  if (!target_logits || !uniforms || !tokens || !n_out) return S3R_ERR_INVALID_ARG;
+  if (B < 1 || B > 65535 || V < 1 || k < 0 || k > kMaxK) return S3R_ERR_INVALID_ARG;
+  if (k > 0 && (!draft_logits || !draft_tokens)) return S3R_ERR_INVALID_ARG;
+  if (!(temperature >= 0.f) || !isfinite(temperature)) return S3R_ERR_INVALID_ARG;
+  const size_t need = s3r::sample_workspace_bytes(B, k, V);
+  if (ws_bytes < need || ws == nullptr) return S3R_ERR_WORKSPACE;
+  return from_hip(s3r::launch_spec_sample(target_logits, draft_logits, draft_tokens, uniforms, B, k,
+                                          V, temperature, tokens, n_out, accepted, ws, stream));
+}
+
+}  // extern "C"

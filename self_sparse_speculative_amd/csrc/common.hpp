@@ -1,0 +1,46 @@
+// Shared device helpers for the S3R kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace s3r {
+
+constexpr int kWave = 64;
+constexpr int kPage = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+// Low and high bfloat16 of a packed 32-bit word.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bfloat16, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_xor(T v, int mask) {
+  return __shfl_xor(v, mask, kWave);
+}
+
+__device__ __forceinline__ float fmax_nan_free(float a, float b) { return a > b ? a : b; }
+
+// Exponent base 2 that returns 0 for -inf inputs (v_exp_f32 already does).
+__device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Ordered split of [0, n) into `parts` contiguous chunks of `chunk` elements.
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace s3r

@@ -1,0 +1,338 @@
+// s3r_sparse_decode_attn kernels: one sparse draft step.
+//
+// [news] "Long-context RL training stops waiting on autoregressive rollouts...",
+// Interpretation: drafting uses the policy's own weights over a small set of
+// selected historical KV entries. [explainer] "S3R - Self-sparse speculative
+// rollouts for RL - What does it mean?", mechanism paragraph: k fast draft
+// steps read only the selected positions.
+//
+// The step is a gather: every attended position costs one K row and one V row
+// (2 * head_dim * element bytes) and the work per byte is G multiply-adds per
+// element, so it is bound by HBM gather bandwidth, not by arithmetic. Layout
+// of the work:
+//   * grid (split, KV head, sequence); a split is a fixed chunk of the
+//     attended list (selected positions first, then this round's positions);
+//   * 16 lanes share one position row (each lane loads head_dim/16 contiguous
+//     elements, 16 B for bf16 x 128), so one wave gathers 4 rows per load and
+//     one workgroup (4 waves) keeps 16 position streams in flight;
+//   * the G query heads of the KV head are served by the same gathered rows;
+//   * the 16-lane dot products are reduced with DPP (quad_perm, row_ror), the
+//     softmax is online per position stream in base 2, and the streams are
+//     merged with shuffles and LDS at the end of the split;
+//   * a second small kernel merges the splits (log-sum-exp weights) in split
+//     order, so results are deterministic.
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace s3r {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecStreams = kDecThreads / 16;  // position streams per workgroup
+constexpr int kDecUnroll = 4;                  // positions per stream per step
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each row of 16 lanes; every lane of the row receives the sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x124>(v);  // row_ror:4
+  v += dpp<0x128>(v);  // row_ror:8
+  return v;
+}
+
+template <typename T, int EPL>
+struct RowLoad;
+
+template <>
+struct RowLoad<bf16_t, 8> {  // 16 B
+  uint4 raw;
+  __device__ __forceinline__ void load(const bf16_t* p) { raw = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void to_f32(float* f) const {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16lo(w[i]);
+      f[2 * i + 1] = bf16hi(w[i]);
+    }
+  }
+};
+
+template <>
+struct RowLoad<bf16_t, 4> {  // 8 B
+  uint2 raw;
+  __device__ __forceinline__ void load(const bf16_t* p) { raw = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void to_f32(float* f) const {
+    f[0] = bf16lo(raw.x);
+    f[1] = bf16hi(raw.x);
+    f[2] = bf16lo(raw.y);
+    f[3] = bf16hi(raw.y);
+  }
+};
+
+template <>
+struct RowLoad<float, 4> {  // 16 B
+  float4 raw;
+  __device__ __forceinline__ void load(const float* p) { raw = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void to_f32(float* f) const {
+    f[0] = raw.x;
+    f[1] = raw.y;
+    f[2] = raw.z;
+    f[3] = raw.w;
+  }
+};
+
+template <>
+struct RowLoad<float, 8> {  // 32 B
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void to_f32(float* f) const {
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ float elem_f32(const T* p, int i);
+template <>
+__device__ __forceinline__ float elem_f32<float>(const float* p, int i) { return p[i]; }
+template <>
+__device__ __forceinline__ float elem_f32<bf16_t>(const bf16_t* p, int i) { return bf16_to_f32(p[i]); }
+
+// Partial record per (sequence, query head, split): [m, l, acc[D]] with
+// m the running maximum in base 2 and acc the unnormalised output.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
+    const T* __restrict__ q, const T* __restrict__ kp, const T* __restrict__ vp,
+    const int* __restrict__ bt, int max_pages, int Hkv, const int* __restrict__ idx, int nsel_cap,
+    const int* __restrict__ n_sel, const int* __restrict__ sel_len, const int* __restrict__ cur_len,
+    float scale_log2, int chunk, int nsplit, float* __restrict__ part) {
+  constexpr int EPL = D / 16;
+  __shared__ float red[kDecThreads / kWave][G][D + 2];
+
+  const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane & 15;
+  const int stream = wave * 4 + (lane >> 4);
+  const int ns = n_sel[b], L = sel_len[b], cur = cur_len[b];
+  const int total = ns + (cur - L);
+  const int p0 = split * chunk;
+  if (p0 >= total) return;
+  const int p1 = min(total, p0 + chunk);
+  const int Hq = Hkv * G;
+
+  float qv[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const T* qp = q + ((size_t)b * Hq + kv * G + g) * D + sub * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[g][e] = elem_f32<T>(qp, e) * scale_log2;
+  }
+  float m[G], l[G], acc[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = kNegInf;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+  }
+
+  const int* idx_row = idx + ((size_t)b * Hkv + kv) * nsel_cap;
+  const int* bt_row = bt + (size_t)b * max_pages;
+  const size_t head_stride = (size_t)kPage * D;
+
+  for (int j0 = p0 + stream; j0 < p1; j0 += kDecStreams * kDecUnroll) {
+    int pos[kDecUnroll];
+    bool ok[kDecUnroll];
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const int j = j0 + u * kDecStreams;
+      ok[u] = j < p1;
+      const int jj = ok[u] ? j : j0;
+      pos[u] = jj < ns ? idx_row[jj] : L + (jj - ns);
+    }
+    RowLoad<T, EPL> kr[kDecUnroll], vr[kDecUnroll];
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const int page = bt_row[pos[u] >> 4];
+      const size_t off = ((size_t)page * Hkv + kv) * head_stride + (size_t)(pos[u] & 15) * D + sub * EPL;
+      kr[u].load(kp + off);
+      vr[u].load(vp + off);
+    }
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      if (!ok[u]) break;
+      float kf[EPL], vf[EPL];
+      kr[u].to_f32(kf);
+      vr[u].to_f32(vf);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s = fmaf(qv[g][e], kf[e], s);
+        s = row16_sum(s);
+        const float mn = fmaxf(m[g], s);
+        const float a = exp2f_fast(m[g] - mn);  // m = -inf -> 0
+        const float p = exp2f_fast(s - mn);
+        l[g] = l[g] * a + p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e] * a);
+        m[g] = mn;
+      }
+    }
+  }
+
+  // Merge the 4 position streams of each wave (lanes 16 and 32 apart).
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int mask = 16; mask <= 32; mask <<= 1) {
+      const float mo = __shfl_xor(m[g], mask, kWave);
+      const float lo = __shfl_xor(l[g], mask, kWave);
+      const float mn = fmaxf(m[g], mo);
+      const float base = mn == kNegInf ? 0.f : mn;
+      const float a = exp2f_fast(m[g] - base), c = exp2f_fast(mo - base);
+      l[g] = l[g] * a + lo * c;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float ao = __shfl_xor(acc[g][e], mask, kWave);
+        acc[g][e] = acc[g][e] * a + ao * c;
+      }
+      m[g] = mn;
+    }
+  }
+  // Merge the waves through LDS.
+  if (lane < 16) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (sub == 0) {
+        red[wave][g][D] = m[g];
+        red[wave][g][D + 1] = l[g];
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) red[wave][g][sub * EPL + e] = acc[g][e];
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < G * D; t += kDecThreads) {
+    const int g = t / D, d = t % D;
+    float M = kNegInf;
+    for (int w = 0; w < kDecThreads / kWave; ++w) M = fmaxf(M, red[w][g][D]);
+    const float base = M == kNegInf ? 0.f : M;
+    float Ls = 0.f, A = 0.f;
+    for (int w = 0; w < kDecThreads / kWave; ++w) {
+      const float c = exp2f_fast(red[w][g][D] - base);
+      Ls += red[w][g][D + 1] * c;
+      A += red[w][g][d] * c;
+    }
+    float* rec = part + (((size_t)b * Hq + kv * G + g) * nsplit + split) * (D + 2);
+    rec[2 + d] = A;
+    if (d == 0) {
+      rec[0] = M;
+      rec[1] = Ls;
+    }
+  }
+}
+
+// Merge the splits of one (sequence, query head) in split order.
+template <int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(
+    const float* __restrict__ part, const int* __restrict__ n_sel, const int* __restrict__ sel_len,
+    const int* __restrict__ cur_len, int Hq, int chunk, int nsplit, float* __restrict__ out,
+    float* __restrict__ lse) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int total = n_sel[b] + (cur_len[b] - sel_len[b]);
+  const int used = total > 0 ? min(nsplit, ceil_div(total, chunk)) : 0;
+  const float* rec = part + ((size_t)b * Hq + h) * nsplit * (D + 2);
+  float M = kNegInf;
+  for (int c = 0; c < used; ++c) M = fmaxf(M, rec[c * (D + 2)]);
+  const float base = M == kNegInf ? 0.f : M;
+  float Ls = 0.f, A = 0.f;
+  for (int c = 0; c < used; ++c) {
+    const float w = exp2f_fast(rec[c * (D + 2)] - base);
+    Ls += rec[c * (D + 2) + 1] * w;
+    A += rec[c * (D + 2) + 2 + d] * w;
+  }
+  out[((size_t)b * Hq + h) * D + d] = Ls > 0.f ? A / Ls : 0.f;
+  if (lse != nullptr && d == 0) lse[(size_t)b * Hq + h] = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : kNegInf;
+}
+
+int decode_nsplit(int max_attend) { return ceil_div(max_attend < 1 ? 1 : max_attend, kDecChunk); }
+
+size_t decode_workspace_bytes(int B, int Hq, int D, int max_attend) {
+  return (size_t)B * Hq * decode_nsplit(max_attend) * (D + 2) * sizeof(float);
+}
+
+template <typename T, int D, int G>
+static hipError_t launch_decode_t(const void* q, const void* kp, const void* vp, const int* bt,
+                                  int max_pages, int Hkv, const int* idx, int nsel_cap,
+                                  const int* n_sel, const int* sel_len, const int* cur_len, int B,
+                                  float scale_log2, int nsplit, float* part, float* out, float* lse,
+                                  hipStream_t stream) {
+  hipLaunchKernelGGL((sparse_decode_kernel<T, D, G>), dim3(nsplit, Hkv, B), dim3(kDecThreads), 0,
+                     stream, (const T*)q, (const T*)kp, (const T*)vp, bt, max_pages, Hkv, idx,
+                     nsel_cap, n_sel, sel_len, cur_len, scale_log2, kDecChunk, nsplit, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(Hkv * G, B), dim3(D), 0, stream, part, n_sel,
+                     sel_len, cur_len, Hkv * G, kDecChunk, nsplit, out, lse);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_decode_d(int G, const void* q, const void* kp, const void* vp,
+                                  const int* bt, int max_pages, int Hkv, const int* idx,
+                                  int nsel_cap, const int* n_sel, const int* sel_len,
+                                  const int* cur_len, int B, float scale_log2, int nsplit,
+                                  float* part, float* out, float* lse, hipStream_t stream) {
+#define S3R_DEC_CASE(GG)                                                                       \
+  case GG:                                                                                     \
+    return launch_decode_t<T, D, GG>(q, kp, vp, bt, max_pages, Hkv, idx, nsel_cap, n_sel,      \
+                                     sel_len, cur_len, B, scale_log2, nsplit, part, out, lse, \
+                                     stream);
+  switch (G) {
+    S3R_DEC_CASE(1)
+    S3R_DEC_CASE(2)
+    S3R_DEC_CASE(4)
+    S3R_DEC_CASE(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef S3R_DEC_CASE
+}
+
+bool decode_supported(int dtype, int D, int G) {
+  (void)dtype;
+  return (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4 || G == 8);
+}
+
+hipError_t launch_sparse_decode(int dtype, int D, int G, const void* q, const void* kp,
+                                const void* vp, const int* bt, int max_pages, int Hkv,
+                                const int* idx, int nsel_cap, const int* n_sel, const int* sel_len,
+                                const int* cur_len, int B, float scale, int max_attend, float* out,
+                                float* lse, void* ws, hipStream_t stream) {
+  const int nsplit = decode_nsplit(max_attend);
+  const float sl2 = scale * kLog2e;
+  float* part = (float*)ws;
+  if (dtype == 1) {
+    if (D == 128)
+      return launch_decode_d<bf16_t, 128>(G, q, kp, vp, bt, max_pages, Hkv, idx, nsel_cap, n_sel,
+                                          sel_len, cur_len, B, sl2, nsplit, part, out, lse, stream);
+    return launch_decode_d<bf16_t, 64>(G, q, kp, vp, bt, max_pages, Hkv, idx, nsel_cap, n_sel,
+                                       sel_len, cur_len, B, sl2, nsplit, part, out, lse, stream);
+  }
+  if (D == 128)
+    return launch_decode_d<float, 128>(G, q, kp, vp, bt, max_pages, Hkv, idx, nsel_cap, n_sel,
+                                       sel_len, cur_len, B, sl2, nsplit, part, out, lse, stream);
+  return launch_decode_d<float, 64>(G, q, kp, vp, bt, max_pages, Hkv, idx, nsel_cap, n_sel,
+                                    sel_len, cur_len, B, sl2, nsplit, part, out, lse, stream);
+}
+
+}  // namespace s3r

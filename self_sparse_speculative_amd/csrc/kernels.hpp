@@ -1,0 +1,50 @@
+// Internal launcher declarations shared by the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace s3r {
+
+// bfloat16 element that converts to float (generic kernels).
+struct BF16Val {
+  uint16_t bits;
+  __device__ __forceinline__ operator float() const { return __uint_as_float((uint32_t)bits << 16); }
+};
+
+constexpr int kSelLdsKeysMax = 32768;  // keys held in LDS (128 KB); longer contexts re-read global
+constexpr int kDecChunk = 256;         // attended positions per draft split
+constexpr int kVerChunkMfma = 1024;    // context positions per verify split (bf16 x 128 path)
+constexpr int kVerChunkGeneric = 256;  // context positions per verify split (generic path)
+constexpr int kSmpChunks = 64;         // vocabulary chunks of the final draw
+
+hipError_t launch_select(const float* scores, int stride, const int* ctx_len, int B, int Hkv,
+                         int max_ctx_len, int s_num, int s_den, int window, int* idx, int nsel_cap,
+                         int* n_sel, hipStream_t stream);
+
+bool decode_supported(int dtype, int D, int G);
+size_t decode_workspace_bytes(int B, int Hq, int D, int max_attend);
+hipError_t launch_sparse_decode(int dtype, int D, int G, const void* q, const void* kp,
+                                const void* vp, const int* bt, int max_pages, int Hkv,
+                                const int* idx, int nsel_cap, const int* n_sel, const int* sel_len,
+                                const int* cur_len, int B, float scale, int max_attend, float* out,
+                                float* lse, void* ws, hipStream_t stream);
+
+struct VerifyPlan {
+  int G, R, NT, RP, chunk, nsplit, ntile_cap;
+  bool mfma;
+  size_t off_part_o, off_part_ml, off_lse2, off_sc_max, off_sc_val, bytes;
+};
+VerifyPlan verify_plan(int B, int k, int Hq, int Hkv, int D, int dtype, int max_seq_len);
+hipError_t launch_verify(int dtype, int D, const void* q, const void* kp, const void* vp,
+                         const int* bt, int max_pages, int Hkv, const int* seq_len, int B, int k,
+                         int Hq, float scale, int max_seq_len, float* out, float* lse,
+                         float* scores, int score_stride, void* ws, hipStream_t stream);
+
+size_t sample_workspace_bytes(int B, int k, int V);
+hipError_t launch_spec_sample(const float* zt, const float* zd, const int* dtok, const float* u,
+                              int B, int k, int V, float temperature, int* tokens, int* n_out,
+                              int8_t* accepted, void* ws, hipStream_t stream);
+
+}  // namespace s3r

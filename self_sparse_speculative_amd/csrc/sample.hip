@@ -1,0 +1,362 @@
+// s3r_spec_sample kernels: exact speculative sampling from caller uniforms.
+//
+// [explainer] "S3R - Self-sparse speculative rollouts for RL - What does it
+// mean?", Jargon "Exact speculative sampling" and the draft/verify
+// illustration: accepted drafts are kept, the first mismatch is replaced by a
+// corrected token, the rest is discarded. [news] "Long-context RL training
+// stops waiting on autoregressive rollouts...", Interpretation: accept
+// candidates or draw from the residual distribution. [listing] "S^3R: Fast
+// and Faithful RL Rollouts via Self-Sparse Speculative Decoding", Table 7
+// caption: a fully accepted round yields k + 1 tokens.
+//
+// The step reads 2k + 1 logit rows per sequence (vocabulary-sized), so it is
+// an HBM stream. All probabilities are formed in float64 from the float32
+// logits, because the inverse-CDF draw compares a cumulative sum over the
+// whole vocabulary with u * Z and adjacent boundaries are only ~Z/V apart.
+//   1. row_stats_kernel  (2k+1 rows x B): max, first argmax and the float64
+//      normaliser sum exp((z - max) / T), one pass with per-thread online
+//      rescaling, fixed-order tree merge;
+//   2. decide_kernel     (B): ratio tests in order, first reject, token
+//      counts; greedy (T = 0) finishes here;
+//   3. chunk_sum_kernel  (chunks x B): float64 sums of the draw weights
+//      (residual max(0, p - q) or p) per vocabulary chunk, plus sums of p for
+//      the all-zero-residual fallback;
+//   4. final_draw_kernel (B): locate u * Z among the chunk sums, then an
+//      ordered block scan inside that chunk finds the first token whose
+//      cumulative weight exceeds u * Z.
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace s3r {
+
+constexpr int kSmpThreads = 256;
+constexpr int kSmpWaves = kSmpThreads / kWave;
+
+struct SampleWs {
+  float* smax;    // [B][2k+1]
+  double* ssum;   // [B][2k+1]
+  int* sarg;      // [B][2k+1]
+  int* desc;      // [B]: -1 done, else istar | (resid << 8)
+  double* csum;   // [B][kSmpChunks][2]
+};
+
+static size_t align256s(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static SampleWs sample_ws(void* ws, int B, int k, size_t* bytes_out) {
+  const size_t nr = (size_t)B * (2 * k + 1);
+  size_t off = 0;
+  SampleWs w;
+  char* base = (char*)ws;
+  w.smax = (float*)(base + off);
+  off = align256s(off + nr * sizeof(float));
+  w.ssum = (double*)(base + off);
+  off = align256s(off + nr * sizeof(double));
+  w.sarg = (int*)(base + off);
+  off = align256s(off + nr * sizeof(int));
+  w.desc = (int*)(base + off);
+  off = align256s(off + (size_t)B * sizeof(int));
+  w.csum = (double*)(base + off);
+  off = align256s(off + (size_t)B * kSmpChunks * 2 * sizeof(double));
+  if (bytes_out) *bytes_out = off;
+  return w;
+}
+
+size_t sample_workspace_bytes(int B, int k, int V) {
+  (void)V;
+  size_t bytes = 0;
+  sample_ws(nullptr, B, k, &bytes);
+  return bytes;
+}
+
+__device__ __forceinline__ const float* logit_row(const float* zt, const float* zd, int b, int r, int k, int V) {
+  return r <= k ? zt + ((size_t)b * (k + 1) + r) * V : zd + ((size_t)b * k + (r - k - 1)) * V;
+}
+
+// (max, sum, argmax) triple; sum is relative to max.
+struct Stat {
+  float m;
+  double s;
+  int i;
+};
+
+__device__ __forceinline__ Stat stat_merge(Stat a, Stat b, double invT, bool greedy) {
+  Stat r;
+  r.m = fmaxf(a.m, b.m);
+  r.i = a.m > b.m ? a.i : (b.m > a.m ? b.i : min(a.i, b.i));
+  if (greedy) {
+    r.s = 0.0;
+  } else {
+    const double sa = a.m == kNegInf ? 0.0 : a.s * exp(((double)a.m - (double)r.m) * invT);
+    const double sb = b.m == kNegInf ? 0.0 : b.s * exp(((double)b.m - (double)r.m) * invT);
+    r.s = sa + sb;
+  }
+  return r;
+}
+
+__device__ __forceinline__ void stat_add(Stat& st, float z, int y, double invT, bool greedy) {
+  if (z > st.m) {
+    if (!greedy) st.s = (st.m == kNegInf ? 0.0 : st.s * exp(((double)st.m - (double)z) * invT)) + 1.0;
+    st.m = z;
+    st.i = y;
+  } else if (!greedy) {
+    st.s += exp(((double)z - (double)st.m) * invT);
+  }
+}
+
+__global__ __launch_bounds__(kSmpThreads) void row_stats_kernel(
+    const float* __restrict__ zt, const float* __restrict__ zd, int k, int V, double invT, int greedy,
+    float* __restrict__ smax, double* __restrict__ ssum, int* __restrict__ sarg) {
+  __shared__ float sh_m[kSmpThreads];
+  __shared__ double sh_s[kSmpThreads];
+  __shared__ int sh_i[kSmpThreads];
+  const int r = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const float* z = logit_row(zt, zd, b, r, k, V);
+  Stat st = {kNegInf, 0.0, 0x7fffffff};
+  const bool gr = greedy != 0;
+  if ((V & 3) == 0) {
+    const float4* z4 = reinterpret_cast<const float4*>(z);
+    const int n4 = V >> 2;
+    for (int t = tid; t < n4; t += kSmpThreads) {
+      const float4 v = z4[t];
+      stat_add(st, v.x, 4 * t, invT, gr);
+      stat_add(st, v.y, 4 * t + 1, invT, gr);
+      stat_add(st, v.z, 4 * t + 2, invT, gr);
+      stat_add(st, v.w, 4 * t + 3, invT, gr);
+    }
+  } else {
+    for (int y = tid; y < V; y += kSmpThreads) stat_add(st, z[y], y, invT, gr);
+  }
+  sh_m[tid] = st.m;
+  sh_s[tid] = st.s;
+  sh_i[tid] = st.i;
+  __syncthreads();
+  for (int half = kSmpThreads / 2; half > 0; half >>= 1) {
+    if (tid < half) {
+      Stat a = {sh_m[tid], sh_s[tid], sh_i[tid]};
+      Stat c = {sh_m[tid + half], sh_s[tid + half], sh_i[tid + half]};
+      Stat m = stat_merge(a, c, invT, gr);
+      sh_m[tid] = m.m;
+      sh_s[tid] = m.s;
+      sh_i[tid] = m.i;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const size_t o = (size_t)b * (2 * k + 1) + r;
+    smax[o] = sh_m[0];
+    ssum[o] = sh_s[0];
+    sarg[o] = sh_i[0];
+  }
+}
+
+__device__ __forceinline__ double prob(float z, float m, double s, double invT) {
+  return exp(((double)z - (double)m) * invT) / s;
+}
+
+__global__ __launch_bounds__(kWave) void decide_kernel(
+    const float* __restrict__ zt, const float* __restrict__ zd, const int* __restrict__ dtok,
+    const float* __restrict__ u, int k, int V, double invT, int greedy,
+    const float* __restrict__ smax, const double* __restrict__ ssum, const int* __restrict__ sarg,
+    int* __restrict__ tokens, int* __restrict__ n_out, int8_t* __restrict__ accepted,
+    int* __restrict__ desc) {
+  const int b = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  const size_t so = (size_t)b * (2 * k + 1);
+  int istar = k;
+  for (int i = 0; i < k; ++i) {
+    const int x = dtok[(size_t)b * k + i];
+    bool acc;
+    if (greedy) {
+      acc = x == sarg[so + i];
+    } else {
+      const double p = prob(zt[((size_t)b * (k + 1) + i) * V + x], smax[so + i], ssum[so + i], invT);
+      const double qq = prob(zd[((size_t)b * k + i) * V + x], smax[so + k + 1 + i], ssum[so + k + 1 + i], invT);
+      acc = (p >= qq) || ((double)u[(size_t)b * (k + 1) + i] * qq < p);
+    }
+    if (accepted) accepted[(size_t)b * k + i] = acc ? 1 : 0;
+    if (!acc) {
+      istar = i;
+      break;
+    }
+    tokens[(size_t)b * (k + 1) + i] = x;
+  }
+  if (accepted)
+    for (int i = istar + 1; i < k; ++i) accepted[(size_t)b * k + i] = -1;
+  for (int j = istar + 1; j <= k; ++j) tokens[(size_t)b * (k + 1) + j] = -1;
+  n_out[b] = istar + 1;
+  if (greedy) {
+    tokens[(size_t)b * (k + 1) + istar] = sarg[so + istar];
+    desc[b] = -1;
+  } else {
+    desc[b] = istar | ((istar < k ? 1 : 0) << 8);
+  }
+}
+
+__global__ __launch_bounds__(kSmpThreads) void chunk_sum_kernel(
+    const float* __restrict__ zt, const float* __restrict__ zd, int k, int V, double invT,
+    const float* __restrict__ smax, const double* __restrict__ ssum, const int* __restrict__ desc,
+    double* __restrict__ csum) {
+  __shared__ double sh[2][kSmpThreads];
+  const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int dsc = desc[b];
+  if (dsc < 0) return;
+  const int istar = dsc & 0xff;
+  const bool resid = (dsc >> 8) != 0;
+  const int csz = ceil_div(V, kSmpChunks);
+  const int y0 = c * csz, y1 = min(V, y0 + csz);
+  const size_t so = (size_t)b * (2 * k + 1);
+  const float* zr = zt + ((size_t)b * (k + 1) + istar) * V;
+  const float* dr = resid ? zd + ((size_t)b * k + istar) * V : nullptr;
+  const float mt = smax[so + istar];
+  const double st = ssum[so + istar];
+  const float md = resid ? smax[so + k + 1 + istar] : 0.f;
+  const double sd = resid ? ssum[so + k + 1 + istar] : 1.0;
+  double aw = 0.0, ap = 0.0;
+  for (int y = y0 + tid; y < y1; y += kSmpThreads) {
+    const double p = prob(zr[y], mt, st, invT);
+    double w = p;
+    if (resid) w = fmax(0.0, p - prob(dr[y], md, sd, invT));
+    aw += w;
+    ap += p;
+  }
+  sh[0][tid] = aw;
+  sh[1][tid] = ap;
+  __syncthreads();
+  for (int half = kSmpThreads / 2; half > 0; half >>= 1) {
+    if (tid < half) {
+      sh[0][tid] += sh[0][tid + half];
+      sh[1][tid] += sh[1][tid + half];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    csum[((size_t)b * kSmpChunks + c) * 2] = sh[0][0];
+    csum[((size_t)b * kSmpChunks + c) * 2 + 1] = sh[1][0];
+  }
+}
+
+__global__ __launch_bounds__(kSmpThreads) void final_draw_kernel(
+    const float* __restrict__ zt, const float* __restrict__ zd, const float* __restrict__ u, int k,
+    int V, double invT, const float* __restrict__ smax, const double* __restrict__ ssum,
+    const int* __restrict__ desc, const double* __restrict__ csum, int* __restrict__ tokens) {
+  __shared__ int sh_chunk, sh_usep, sh_found, sh_lastpos;
+  __shared__ double sh_carry, sh_t;
+  __shared__ double wtot[kSmpWaves];
+  __shared__ int wfound[kSmpWaves], wlast[kSmpWaves];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int dsc = desc[b];
+  if (dsc < 0) return;
+  const int istar = dsc & 0xff;
+  const bool resid0 = (dsc >> 8) != 0;
+  const double* cs = csum + (size_t)b * kSmpChunks * 2;
+  if (tid == 0) {
+    double Z = 0.0;
+    for (int c = 0; c < kSmpChunks; ++c) Z += cs[2 * c];
+    int usep = 0;
+    if (!(Z > 0.0)) {  // all-zero residual: draw from p
+      usep = 1;
+      Z = 0.0;
+      for (int c = 0; c < kSmpChunks; ++c) Z += cs[2 * c + 1];
+    }
+    const double t = (double)u[(size_t)b * (k + 1) + k] * Z;
+    double cum = 0.0;
+    int chunk = -1;
+    double carry = 0.0;
+    for (int c = 0; c < kSmpChunks; ++c) {
+      const double after = cum + cs[2 * c + usep];
+      if (after > t) {
+        chunk = c;
+        carry = cum;
+        break;
+      }
+      cum = after;
+    }
+    if (chunk < 0) {  // rounding left no crossing: last chunk with weight
+      for (int c = kSmpChunks - 1; c >= 0; --c)
+        if (cs[2 * c + usep] > 0.0) { chunk = c; break; }
+      carry = -__builtin_huge_val();  // never crosses; the last positive weight is taken
+    }
+    sh_chunk = chunk;
+    sh_usep = usep;
+    sh_carry = carry;
+    sh_t = t;
+    sh_found = -1;
+    sh_lastpos = -1;
+  }
+  __syncthreads();
+  const int chunk = sh_chunk;
+  const bool resid = resid0 && !sh_usep;
+  const double t = sh_t;
+  const int csz = ceil_div(V, kSmpChunks);
+  const int y0 = chunk * csz, y1 = min(V, y0 + csz);
+  const size_t so = (size_t)b * (2 * k + 1);
+  const float* zr = zt + ((size_t)b * (k + 1) + istar) * V;
+  const float* dr = resid ? zd + ((size_t)b * k + istar) * V : nullptr;
+  const float mt = smax[so + istar];
+  const double st = ssum[so + istar];
+  const float md = resid ? smax[so + k + 1 + istar] : 0.f;
+  const double sd = resid ? ssum[so + k + 1 + istar] : 1.0;
+  for (int base = y0; base < y1; base += kSmpThreads) {
+    const int y = base + tid;
+    double w = 0.0;
+    if (y < y1) {
+      w = prob(zr[y], mt, st, invT);
+      if (resid) w = fmax(0.0, w - prob(dr[y], md, sd, invT));
+    }
+    // inclusive scan inside the wave, then across waves
+    double incl = w;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const double v = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += v;
+    }
+    if (lane == kWave - 1) wtot[wave] = incl;
+    const uint64_t pos_mask = __ballot(w > 0.0);
+    if (lane == 0) wlast[wave] = pos_mask ? base + wave * kWave + 63 - __clzll(pos_mask) : -1;
+    __syncthreads();
+    double before = sh_carry;
+    for (int ww = 0; ww < wave; ++ww) before += wtot[ww];
+    const double cum = before + incl;
+    const uint64_t hit = __ballot(y < y1 && cum > t);
+    if (lane == 0) wfound[wave] = hit ? base + wave * kWave + __ffsll((unsigned long long)hit) - 1 : -1;
+    __syncthreads();
+    if (tid == 0) {
+      for (int ww = 0; ww < kSmpWaves; ++ww) {
+        if (wlast[ww] >= 0) sh_lastpos = wlast[ww];
+        if (sh_found < 0 && wfound[ww] >= 0) sh_found = wfound[ww];
+      }
+      double tot = 0.0;
+      for (int ww = 0; ww < kSmpWaves; ++ww) tot += wtot[ww];
+      sh_carry += tot;
+    }
+    __syncthreads();
+    if (sh_found >= 0) break;
+  }
+  if (tid == 0) tokens[(size_t)b * (k + 1) + istar] = sh_found >= 0 ? sh_found : sh_lastpos;
+}
+
+hipError_t launch_spec_sample(const float* zt, const float* zd, const int* dtok, const float* u,
+                              int B, int k, int V, float temperature, int* tokens, int* n_out,
+                              int8_t* accepted, void* ws, hipStream_t stream) {
+  SampleWs w = sample_ws(ws, B, k, nullptr);
+  const int greedy = temperature == 0.f;
+  const double invT = greedy ? 0.0 : 1.0 / (double)temperature;
+  hipLaunchKernelGGL(row_stats_kernel, dim3(2 * k + 1, B), dim3(kSmpThreads), 0, stream, zt, zd, k,
+                     V, invT, greedy, w.smax, w.ssum, w.sarg);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decide_kernel, dim3(B), dim3(kWave), 0, stream, zt, zd, dtok, u, k, V, invT,
+                     greedy, w.smax, w.ssum, w.sarg, tokens, n_out, accepted, w.desc);
+  e = hipGetLastError();
+  if (e != hipSuccess || greedy) return e;
+  hipLaunchKernelGGL(chunk_sum_kernel, dim3(kSmpChunks, B), dim3(kSmpThreads), 0, stream, zt, zd, k,
+                     V, invT, w.smax, w.ssum, w.desc, w.csum);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(final_draw_kernel, dim3(B), dim3(kSmpThreads), 0, stream, zt, zd, u, k, V, invT,
+                     w.smax, w.ssum, w.desc, w.csum, tokens);
+  return hipGetLastError();
+}
+
+}  // namespace s3r

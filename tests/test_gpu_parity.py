@@ -1,0 +1,337 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle.
+
+Bars: selection indices / counts and sampled tokens / decisions bit-exact;
+attention max-abs 1e-5 for float32 inputs; 2e-2 relative per output vector
+for bfloat16 K/V with float32 accumulation; scores 1e-5 abs (float32) and
+2e-2 of the per-(sequence, KV head) maximum (bfloat16).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import self_sparse_speculative_amd as s3r
+from s3r_inputs import get_config, make_batch
+from tests.gpu_util import (nsel_cap, rel_err_rows, run_draft_steps, run_sample, run_select, run_verify,
+                            to_dev)
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-2
+
+_cache = {}
+
+
+def _batch(key, cid, parts=("kv", "q", "scores", "logits"), **ov):
+    if key not in _cache:
+        cfg = get_config(cid, **ov)
+        print(f"[gen] {key}: {cfg.name} B={cfg.B} parts={parts}", flush=True)
+        b = make_batch(cfg, parts=parts)
+        _cache[key] = (cfg, b, to_dev(b))
+    return _cache[key]
+
+
+def _oracle_idx(cfg, batch, scores, b, kv):
+    return oracle.select(scores[b, kv], int(batch.ctx_len[b]), cfg.s_num, cfg.s_den, cfg.window)
+
+
+def _check_select(cfg, batch, scores_np, idx, n_sel, units):
+    idx = idx.cpu().numpy()
+    n_sel = n_sel.cpu().numpy()
+    for b, kv in units:
+        ref = _oracle_idx(cfg, batch, scores_np, b, kv)
+        assert n_sel[b] == len(ref), (b, kv)
+        assert np.array_equal(idx[b, kv, :n_sel[b]], ref), (b, kv)
+
+
+# ----------------------------------------------------------------- select
+
+@pytest.mark.parametrize("key,cid,ov", [
+    ("c1", 1, {}),
+    ("c2s", 2, {"B": 16}),
+    ("c3s", 3, {"B": 12}),
+    ("c5s", 5, {"B": 6}),
+])
+def test_select_matches_oracle(key, cid, ov):
+    cfg, batch, t = _batch(key + "-sel", cid, parts=("scores",), **ov)
+    idx, n_sel = run_select(cfg, batch, t)
+    torch.cuda.synchronize()
+    units = [(b, kv) for b in range(cfg.B) for kv in range(cfg.Hkv)]
+    _check_select(cfg, batch, batch.scores, idx, n_sel, units)
+
+
+def test_select_edge_cases():
+    cfg = get_config(2, B=7, Hkv=2)
+    rng = np.random.default_rng(7)
+    L = np.array([1, 5, 64, 65, 200, 40000, 1000], dtype=np.int32)  # window 64; 40000 > LDS key capacity
+    stride = int(L.max())
+    sc = np.zeros((7, 2, stride), np.float32)
+    sc[0] = 0.0
+    sc[1, :, :5] = [-0.0, 0.0, -0.0, 0.0, 1.0]
+    sc[2, 0, :64] = rng.integers(0, 3, 64)
+    sc[3, 0, :65] = np.inf
+    sc[3, 1, :65] = -np.inf
+    sc[4, :, :200] = rng.integers(0, 4, (2, 200)).astype(np.float32)  # heavy ties
+    sc[4, 1, 7] = -0.0
+    sc[5, :, :40000] = rng.random((2, 40000)).astype(np.float32)
+    sc[5, 0, 100:200] = 0.5  # ties in the long row
+    sc[6, :, :1000] = (rng.integers(0, 2, (2, 1000)) * 2 - 1) * np.float32(1e-38)  # denormal-range signs
+    dev = torch.device("cuda")
+    for s_num, s_den in [(1, 20), (1, 2), (1, 1), (0, 1), (7, 9)]:
+        nc = s3r.budget(stride, s_num, s_den, cfg.window)
+        idx, n_sel = s3r.select(torch.from_numpy(sc).to(dev), torch.from_numpy(L).to(dev), stride, s_num, s_den,
+                                cfg.window, nsel_cap=max(1, nc))
+        torch.cuda.synchronize()
+        idx, n_sel = idx.cpu().numpy(), n_sel.cpu().numpy()
+        for b in range(7):
+            for kv in range(2):
+                ref = oracle.select(sc[b, kv], int(L[b]), s_num, s_den, cfg.window)
+                assert n_sel[b] == len(ref)
+                assert np.array_equal(idx[b, kv, :n_sel[b]], ref), (s_num, s_den, b, kv)
+
+
+# ----------------------------------------------------------------- draft
+
+def _draft_case(cfg, batch, t, steps, seqs, tol, absolute):
+    idx, n_sel = run_select(cfg, batch, t)
+    outs = run_draft_steps(cfg, batch, t, idx, n_sel)
+    torch.cuda.synchronize()
+    idx_np, ns = idx.cpu().numpy(), n_sel.cpu().numpy()
+    worst = 0.0
+    for j in steps:
+        o, lse = outs[j - 1][0].cpu().numpy(), outs[j - 1][1].cpu().numpy()
+        for b in seqs:
+            L = int(batch.ctx_len[b])
+            ro, rl = oracle.sparse_decode(batch.q_draft[j - 1, b], batch.k_pages, batch.v_pages, batch.block_table[b],
+                                          idx_np[b], int(ns[b]), L, L + j, float(batch.scale))
+            if absolute:
+                err = float(np.abs(o[b] - ro).max())
+            else:
+                err = rel_err_rows(o[b], ro)
+            worst = max(worst, err)
+            assert err <= tol, (j, b, err)
+            assert np.abs(lse[b] - rl).max() <= (1e-5 if absolute else 2e-3), (j, b)
+    print(f"draft worst error {worst:.3g}")
+
+
+def test_draft_c1_f32():
+    cfg, batch, t = _batch("c1", 1)
+    _draft_case(cfg, batch, t, range(1, cfg.k + 1), range(cfg.B), TOL_F32, True)
+
+
+@pytest.mark.parametrize("key,cid,ov", [("c2d", 2, {"B": 6}), ("c3d", 3, {"B": 5})])
+def test_draft_bf16(key, cid, ov):
+    cfg, batch, t = _batch(key, cid, **ov)
+    _draft_case(cfg, batch, t, [1, cfg.k], range(cfg.B), TOL_BF16, False)
+
+
+def test_draft_full_budget_is_dense():
+    cfg, batch, t = _batch("c2full", 2, B=3, lengths=("uniform", 300, 700), s_num=1, s_den=1)
+    idx, n_sel = run_select(cfg, batch, t)
+    outs = run_draft_steps(cfg, batch, t, idx, n_sel)
+    torch.cuda.synchronize()
+    for j in (1, cfg.k):
+        o = outs[j - 1][0].cpu().numpy()
+        for b in range(cfg.B):
+            L = int(batch.ctx_len[b])
+            ro, _ = oracle.dense_decode(batch.q_draft[j - 1, b], batch.k_pages, batch.v_pages, batch.block_table[b],
+                                        L + j, float(batch.scale))
+            assert rel_err_rows(o[b], ro) <= TOL_BF16
+
+
+# ----------------------------------------------------------------- verify
+
+def _verify_case(cfg, batch, t, seqs, absolute):
+    out, lse, sc = run_verify(cfg, batch, t)
+    torch.cuda.synchronize()
+    out, lse, sc = out.cpu().numpy(), lse.cpu().numpy(), sc.cpu().numpy()
+    worst_o = worst_s = 0.0
+    for b in seqs:
+        S = int(batch.seq_len[b])
+        ro, rl, rs = oracle.verify(batch.q_verify[b], batch.k_pages, batch.v_pages, batch.block_table[b], S, cfg.k,
+                                   float(batch.scale))
+        if absolute:
+            eo = float(np.abs(out[b] - ro).max())
+            es = float(np.abs(sc[b, :, :S] - rs).max())
+            assert eo <= TOL_F32 and es <= TOL_F32, (b, eo, es)
+            assert np.abs(lse[b] - rl).max() <= TOL_F32
+        else:
+            eo = rel_err_rows(out[b], ro)
+            es = float((np.abs(sc[b, :, :S] - rs).max(axis=1) / rs.max(axis=1)).max())
+            assert eo <= TOL_BF16 and es <= TOL_BF16, (b, eo, es)
+            assert np.abs(lse[b] - rl).max() <= 2e-3
+        np.testing.assert_allclose(sc[b, :, :S].sum(axis=1), cfg.G * (cfg.k + 1), rtol=1e-3)
+        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+    print(f"verify worst out error {worst_o:.3g}, scores error {worst_s:.3g}")
+
+
+def test_verify_c1_f32():
+    cfg, batch, t = _batch("c1", 1)
+    _verify_case(cfg, batch, t, range(cfg.B), True)
+
+
+@pytest.mark.parametrize("key,cid,ov", [
+    ("c2v", 2, {"B": 4}),                       # G=2, 14 rows (one row tile)
+    ("c3v", 3, {"B": 3}),                       # G=4, 28 rows (two row tiles)
+    ("c5k2", 5, {"B": 2, "k": 2, "lengths": ("uniform", 900, 3000)}),   # 12 rows
+    ("c5k8", 5, {"B": 2, "k": 8, "lengths": ("uniform", 900, 3000)}),   # 36 rows (three row tiles)
+    ("c3k15", 3, {"B": 2, "k": 15, "lengths": ("uniform", 100, 2100)}),  # 64 rows (four row tiles)
+])
+def test_verify_bf16(key, cid, ov):
+    cfg, batch, t = _batch(key, cid, parts=("kv", "q"), **ov)
+    _verify_case(cfg, batch, t, range(cfg.B), False)
+
+
+def test_verify_generic_bf16_d64_and_f32_d128():
+    for key, ov in [("g64", {"D": 64, "dtype": "bf16"}), ("g128", {"D": 128, "dtype": "f32"})]:
+        cfg, batch, t = _batch(key, 1, parts=("kv", "q", "scores"), B=2, Hq=8, Hkv=2,
+                               lengths=("uniform", 300, 600), **ov)
+        _verify_case(cfg, batch, t, range(cfg.B), ov["dtype"] == "f32")
+        _draft_case(cfg, batch, t, [1, cfg.k], range(cfg.B), TOL_F32 if ov["dtype"] == "f32" else TOL_BF16,
+                    ov["dtype"] == "f32")
+
+
+def test_ragged_short_contexts():
+    L = [1, 2, 15, 16, 17, 33, 63, 64, 65, 1000]
+    cfg = get_config(3, B=len(L))
+    batch = make_batch(cfg, lengths=np.array(L, np.int32))
+    t = to_dev(batch)
+    _verify_case(cfg, batch, t, range(cfg.B), False)
+    _draft_case(cfg, batch, t, [1, cfg.k], range(cfg.B), TOL_BF16, False)
+    idx, n_sel = run_select(cfg, batch, t)
+    torch.cuda.synchronize()
+    _check_select(cfg, batch, batch.scores, idx, n_sel, [(b, kv) for b in range(cfg.B) for kv in range(cfg.Hkv)])
+
+
+# ----------------------------------------------------------------- sampling
+
+def _check_sample(cfg, batch, toks, nout, acc, T, seqs):
+    toks, nout, acc = toks.cpu().numpy(), nout.cpu().numpy(), acc.cpu().numpy()
+    for b in seqs:
+        rt, rn, ra = oracle.spec_sample(batch.zt[b], batch.zd[b], batch.d[b], batch.u[b], T)
+        assert nout[b] == rn, b
+        assert np.array_equal(toks[b], rt), (b, toks[b], rt)
+        assert np.array_equal(acc[b], ra), b
+
+
+@pytest.mark.parametrize("key,cid,ov", [("c1", 1, {}), ("c2smp", 2, {"B": 64}), ("c5smp", 5, {"B": 32, "noise_std": 0.6})])
+def test_spec_sample_bit_exact(key, cid, ov):
+    parts = ("kv", "q", "scores", "logits") if key == "c1" else ("logits",)
+    cfg, batch, t = _batch(key, cid, parts=parts, **ov)
+    toks, nout, acc = run_sample(cfg, batch, t)
+    torch.cuda.synchronize()
+    _check_sample(cfg, batch, toks, nout, acc, batch.temperature, range(cfg.B))
+    print(f"mean tokens per round {nout.float().mean().item():.3f}")
+
+
+def test_spec_sample_greedy_and_identical():
+    cfg, batch, t = _batch("c2smp", 2, parts=("logits",), B=64)
+    toks, nout, acc = run_sample(cfg, batch, t, temperature=0.0)
+    torch.cuda.synchronize()
+    _check_sample(cfg, batch, toks, nout, acc, np.float32(0.0), range(cfg.B))
+    zt = t["zt"]
+    toks, nout, acc = s3r.spec_sample(zt, zt[:, :cfg.k].contiguous(), t["d"], t["u"], 1.0)
+    torch.cuda.synchronize()
+    assert (nout.cpu().numpy() == cfg.k + 1).all()
+    assert (acc.cpu().numpy() == 1).all()
+
+
+def test_spec_sample_chi_square_on_gpu():
+    from scipy import stats
+    V, k, n = 16, 3, 400_000
+    rng = np.random.default_rng(5)
+    zt1 = (1.5 * rng.standard_normal((k + 1, V))).astype(np.float32)
+    zd1 = (zt1[:k] + rng.standard_normal((k, V))).astype(np.float32)
+    P = [oracle.softmax_t(zt1[i], 1.0) for i in range(k + 1)]
+    Q = [oracle.softmax_t(zd1[i], 1.0) for i in range(k)]
+    d = np.stack([np.minimum(np.searchsorted(np.cumsum(Q[i]), rng.random(n) * np.cumsum(Q[i])[-1], side="right"), V - 1)
+                  for i in range(k)], axis=1).astype(np.int32)
+    u = ((rng.integers(0, 1 << 32, size=(n, k + 1), dtype=np.uint64) >> np.uint64(8)).astype(np.float32)
+         * np.float32(2.0 ** -24))
+    dev = torch.device("cuda")
+    step = 50_000  # batch per call (the ABI takes at most 65535 sequences)
+    zt = torch.from_numpy(np.broadcast_to(zt1, (step, k + 1, V)).copy()).to(dev)
+    zd = torch.from_numpy(np.broadcast_to(zd1, (step, k, V)).copy()).to(dev)
+    toks, nout = [], []
+    for c in range(0, n, step):
+        tk, no, _ = s3r.spec_sample(zt, zd, torch.from_numpy(d[c:c + step]).to(dev),
+                                    torch.from_numpy(u[c:c + step]).to(dev), 1.0)
+        toks.append(tk.cpu().numpy())
+        nout.append(no.cpu().numpy())
+    toks, nout = np.concatenate(toks), np.concatenate(nout)
+    for i in range(k + 1):
+        sel = nout > i
+        counts = np.bincount(toks[sel, i], minlength=V)
+        pv = stats.chisquare(counts, P[i] * sel.sum()).pvalue
+        assert pv > 1e-3, (i, pv)
+
+
+# ----------------------------------------------------------------- robustness
+
+def test_determinism_and_poisoned_workspace():
+    cfg, batch, t = _batch("c2v", 2, parts=("kv", "q"), B=4)
+    results = []
+    for trial in range(2):
+        ws = s3r.Workspace()
+        for name, nb in [("verify", s3r.verify_workspace_bytes(cfg.B, cfg.k, cfg.Hq, cfg.Hkv, cfg.D, 1,
+                                                               int(batch.seq_len.max())))]:
+            ws.get(name, nb).fill_(0xFF)  # NaN patterns everywhere
+        out, lse, sc = s3r.verify_attn(t["q_verify"], t["kv"], t["seq_len"], cfg.k, float(batch.scale),
+                                       int(batch.seq_len.max()), ws=ws)
+        torch.cuda.synchronize()
+        results.append((out.cpu().numpy(), lse.cpu().numpy(), sc.cpu().numpy()))
+    assert np.array_equal(results[0][0], results[1][0]) and np.array_equal(results[0][1], results[1][1])
+    for b in range(cfg.B):
+        S = int(batch.seq_len[b])  # entries at and beyond seq_len are not written
+        assert np.array_equal(results[0][2][b, :, :S], results[1][2][b, :, :S])
+        assert np.isfinite(results[0][2][b, :, :S]).all()
+    assert np.isfinite(results[0][0]).all()
+
+
+def test_invalid_arguments_raise():
+    cfg, batch, t = _batch("c1", 1)
+    with pytest.raises(s3r.S3RError):
+        s3r.select(t["scores"], t["ctx_len"], int(batch.ctx_len.max()), 1, 0, 16)
+    with pytest.raises(s3r.S3RError):
+        s3r.verify_attn(t["q_verify"], t["kv"], t["seq_len"], cfg.k, float(batch.scale), 3)
+
+
+# ----------------------------------------------------------------- full size, sampled
+
+@pytest.mark.slow
+def test_full_size_24k_round_sampled():
+    """The benchmark's launch configuration (Qwen3-8B shapes, B=128, 24K context, s=0.05, k=6):
+    select on all units is checked on a sample, draft and verify on sampled sequences, sampling
+    on every sequence."""
+    cfg, batch, t = _batch("c5full", 5)
+    idx, n_sel = run_select(cfg, batch, t)
+    outs = run_draft_steps(cfg, batch, t, idx, n_sel)
+    vout, vlse, vsc = run_verify(cfg, batch, t)
+    toks, nout, acc = run_sample(cfg, batch, t)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    units = [(int(rng.integers(cfg.B)), int(rng.integers(cfg.Hkv))) for _ in range(24)]
+    _check_select(cfg, batch, batch.scores, idx, n_sel, units)
+    idx_np, ns = idx.cpu().numpy(), n_sel.cpu().numpy()
+    for b in [0, 77]:
+        L = int(batch.ctx_len[b])
+        for j in (1, cfg.k):
+            ro, _ = oracle.sparse_decode(batch.q_draft[j - 1, b], batch.k_pages, batch.v_pages, batch.block_table[b],
+                                         idx_np[b], int(ns[b]), L, L + j, float(batch.scale))
+            assert rel_err_rows(outs[j - 1][0][b].cpu().numpy(), ro) <= TOL_BF16
+    vout, vsc = vout.cpu().numpy(), vsc.cpu().numpy()
+    for b in [5]:
+        S = int(batch.seq_len[b])
+        ro, rl, rs = oracle.verify(batch.q_verify[b], batch.k_pages, batch.v_pages, batch.block_table[b], S, cfg.k,
+                                   float(batch.scale))
+        assert rel_err_rows(vout[b], ro) <= TOL_BF16
+        assert (np.abs(vsc[b, :, :S] - rs).max(axis=1) / rs.max(axis=1)).max() <= TOL_BF16
+    _check_sample(cfg, batch, toks, nout, acc, batch.temperature, range(cfg.B))
+    # the verify scores feed the next selection: bit-exact on the same array
+    idx2, n2 = run_select(cfg, batch, t, scores=torch.from_numpy(vsc).cuda())
+    torch.cuda.synchronize()
+    _check_select(cfg, batch, vsc, idx2, n2, units[:8])
