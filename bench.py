@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seqs", type=int, default=24, help="sequences in the oracle's timed CPU sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline (profiling runs)")
+    ap.add_argument("--copy-gib", type=float, default=2.0,
+                    help="size of the device-to-device copy timed as the HBM reference (0 to skip)")
     return ap.parse_args()
 
 
@@ -221,6 +223,32 @@ def main():
 
     traffic = load_traffic(os.path.join(ROOT, "self_sparse_speculative_amd", "csrc", "verify.hip"))
     value = verified / (ms_step * 1e-3)
+    copy_gbs = read_gbs = None
+    if args.copy_gib > 0:
+        # plain device copy of known size: the HBM reference (and the calibration kernel of the
+        # byte counters); read + write bytes per copy / time
+        n = int(args.copy_gib * (1 << 30)) // 4
+        src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        c0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        copy_gbs = 2 * n * 4 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        # read-only reference: a full reduction over the same buffer
+        acc = src.sum()
+        c0.record()
+        for _ in range(5):
+            acc = src.sum()
+        c1.record()
+        torch.cuda.synchronize()
+        read_gbs = n * 4 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        del src, dst, acc
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
@@ -269,6 +297,8 @@ def main():
                     "spec_sample": round(smp_bytes / (t_smp * 1e-3) / 1e9, 1)},
             "draft_plus_verify_kv_GBs": round(kv_bytes / (kv_ms * 1e-3) / 1e9, 1),
             "draft_plus_verify_frac_of_hbm_peak": round(kv_bytes / (kv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "device_copy_GBs": None if copy_gbs is None else round(copy_gbs, 1),
+            "device_read_GBs": None if read_gbs is None else round(read_gbs, 1),
             "round_algorithmic_bytes": kv_bytes + sel_bytes + smp_bytes,
             "round_frac_of_hbm_peak": round((kv_bytes + sel_bytes + smp_bytes) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         },

@@ -29,7 +29,7 @@ namespace s3r {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecStreams = kDecThreads / 16;  // position streams per workgroup
-constexpr int kDecUnroll = 4;                  // positions per stream per step
+constexpr int kDecUnroll = 8;                  // positions per stream per step
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -116,6 +116,7 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     float scale_log2, int chunk, int nsplit, float* __restrict__ part) {
   constexpr int EPL = D / 16;
   __shared__ float red[kDecThreads / kWave][G][D + 2];
+  __shared__ int rows[kDecChunk];  // cache row (page, KV head, slot) of each attended position
 
   const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -146,29 +147,28 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
 
   const int* idx_row = idx + ((size_t)b * Hkv + kv) * nsel_cap;
   const int* bt_row = bt + (size_t)b * max_pages;
-  const size_t head_stride = (size_t)kPage * D;
+  // Resolve the split's positions to cache rows once: position -> page -> row.
+  for (int j = p0 + tid; j < p1; j += kDecThreads) {
+    const int pos = j < ns ? idx_row[j] : L + (j - ns);
+    rows[j - p0] = (bt_row[pos >> 4] * Hkv + kv) * kPage + (pos & 15);
+  }
+  __syncthreads();
 
   for (int j0 = p0 + stream; j0 < p1; j0 += kDecStreams * kDecUnroll) {
-    int pos[kDecUnroll];
     bool ok[kDecUnroll];
+    RowLoad<T, EPL> kr[kDecUnroll], vr[kDecUnroll];
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
       const int j = j0 + u * kDecStreams;
       ok[u] = j < p1;
-      const int jj = ok[u] ? j : j0;
-      pos[u] = jj < ns ? idx_row[jj] : L + (jj - ns);
-    }
-    RowLoad<T, EPL> kr[kDecUnroll], vr[kDecUnroll];
-#pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u) {
-      const int page = bt_row[pos[u] >> 4];
-      const size_t off = ((size_t)page * Hkv + kv) * head_stride + (size_t)(pos[u] & 15) * D + sub * EPL;
+      const size_t off = (size_t)rows[(ok[u] ? j : j0) - p0] * D + sub * EPL;
       kr[u].load(kp + off);
       vr[u].load(vp + off);
     }
+    // Branch-free update (a position past the split end gets logit -inf), so
+    // every load above stays in flight together.
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
-      if (!ok[u]) break;
       float kf[EPL], vf[EPL];
       kr[u].to_f32(kf);
       vr[u].to_f32(vf);
@@ -177,10 +177,11 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
         float s = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) s = fmaf(qv[g][e], kf[e], s);
-        s = row16_sum(s);
+        s = ok[u] ? row16_sum(s) : kNegInf;
         const float mn = fmaxf(m[g], s);
-        const float a = exp2f_fast(m[g] - mn);  // m = -inf -> 0
-        const float p = exp2f_fast(s - mn);
+        const float base = mn == kNegInf ? 0.f : mn;
+        const float a = exp2f_fast(m[g] - base);  // m = -inf -> 0
+        const float p = exp2f_fast(s - base);     // s = -inf -> 0
         l[g] = l[g] * a + p;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e] * a);

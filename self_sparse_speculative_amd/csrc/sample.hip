@@ -43,6 +43,36 @@ struct SampleWs {
 
 static size_t align256s(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Float64 exponential, table-driven (Tang, "Table-driven implementation of the
+// exponential function in IEEE floating-point arithmetic", ACM TOMS 1989):
+// x = (32 m + j) ln2/32 + r with |r| <= ln2/64, exp(x) = 2^m 2^(j/32) (1 + p(r)),
+// p the degree-6 Taylor polynomial of expm1 (truncation < 4e-18). The 32 table
+// entries 2^(j/32) are computed once per workgroup with the library exp2.
+// Relative error ~1e-15 for the arguments used here (x <= 0).
+struct Exp64Table {
+  double t[32];
+};
+
+__device__ __forceinline__ void exp64_init(Exp64Table& tab) {
+  if (threadIdx.x < 32) tab.t[threadIdx.x] = exp2((double)threadIdx.x / 32.0);
+  __syncthreads();
+}
+
+__device__ __forceinline__ double exp64(double x, const Exp64Table& tab) {
+  x = fmax(x, -1000.0);
+  const double kf = rint(x * (32.0 / 0.6931471805599453));
+  const int ki = (int)kf;
+  const double r = fma(-kf, 0.6931471805599453 / 32.0, x);
+  double p = fma(r, 1.0 / 720.0, 1.0 / 120.0);
+  p = fma(r, p, 1.0 / 24.0);
+  p = fma(r, p, 1.0 / 6.0);
+  p = fma(r, p, 0.5);
+  p = fma(r, p, 1.0);
+  p = p * r;
+  const double s = tab.t[ki & 31];
+  return ldexp(fma(s, p, s), ki >> 5);
+}
+
 static SampleWs sample_ws(void* ws, int B, int k, size_t* bytes_out) {
   const size_t nr = (size_t)B * (2 * k + 1);
   size_t off = 0;
@@ -80,52 +110,59 @@ struct Stat {
   int i;
 };
 
-__device__ __forceinline__ Stat stat_merge(Stat a, Stat b, double invT, bool greedy) {
+__device__ __forceinline__ Stat stat_merge(Stat a, Stat b, double invT, bool greedy, const Exp64Table& tab) {
   Stat r;
   r.m = fmaxf(a.m, b.m);
   r.i = a.m > b.m ? a.i : (b.m > a.m ? b.i : min(a.i, b.i));
   if (greedy) {
     r.s = 0.0;
   } else {
-    const double sa = a.m == kNegInf ? 0.0 : a.s * exp(((double)a.m - (double)r.m) * invT);
-    const double sb = b.m == kNegInf ? 0.0 : b.s * exp(((double)b.m - (double)r.m) * invT);
+    const double sa = a.m == kNegInf ? 0.0 : a.s * exp64(((double)a.m - (double)r.m) * invT, tab);
+    const double sb = b.m == kNegInf ? 0.0 : b.s * exp64(((double)b.m - (double)r.m) * invT, tab);
     r.s = sa + sb;
   }
   return r;
 }
 
-__device__ __forceinline__ void stat_add(Stat& st, float z, int y, double invT, bool greedy) {
-  if (z > st.m) {
-    if (!greedy) st.s = (st.m == kNegInf ? 0.0 : st.s * exp(((double)st.m - (double)z) * invT)) + 1.0;
-    st.m = z;
-    st.i = y;
-  } else if (!greedy) {
-    st.s += exp(((double)z - (double)st.m) * invT);
+// Online update with one element, branch-free: if z raises the maximum the
+// running sum is rescaled by exp((m - z) / T) and z contributes 1, otherwise z
+// contributes exp((z - m) / T); both use exp(-|z - m| / T).
+__device__ __forceinline__ void stat_add(Stat& st, float z, int y, double invT, bool greedy,
+                                         const Exp64Table& tab) {
+  const bool up = z > st.m;
+  if (!greedy) {
+    const double e = exp64(-fabs((double)z - (double)st.m) * invT, tab);  // m = -inf -> 0
+    st.s = up ? fma(st.s, e, 1.0) : st.s + e;
   }
+  st.i = up ? y : st.i;
+  st.m = up ? z : st.m;
 }
 
+template <bool GREEDY>
 __global__ __launch_bounds__(kSmpThreads) void row_stats_kernel(
-    const float* __restrict__ zt, const float* __restrict__ zd, int k, int V, double invT, int greedy,
+    const float* __restrict__ zt, const float* __restrict__ zd, int k, int V, double invT,
     float* __restrict__ smax, double* __restrict__ ssum, int* __restrict__ sarg) {
   __shared__ float sh_m[kSmpThreads];
   __shared__ double sh_s[kSmpThreads];
   __shared__ int sh_i[kSmpThreads];
+  __shared__ Exp64Table tab;
+  exp64_init(tab);
   const int r = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const float* z = logit_row(zt, zd, b, r, k, V);
   Stat st = {kNegInf, 0.0, 0x7fffffff};
-  const bool gr = greedy != 0;
+  constexpr bool gr = GREEDY;
   if ((V & 3) == 0) {
     const float4* z4 = reinterpret_cast<const float4*>(z);
     const int n4 = V >> 2;
     for (int t = tid; t < n4; t += kSmpThreads) {
       const float4 v = z4[t];
-      stat_add(st, v.x, 4 * t, invT, gr);
-      stat_add(st, v.y, 4 * t + 1, invT, gr);
-      stat_add(st, v.z, 4 * t + 2, invT, gr);
-      stat_add(st, v.w, 4 * t + 3, invT, gr);
+      stat_add(st, v.x, 4 * t, invT, gr, tab);
+      stat_add(st, v.y, 4 * t + 1, invT, gr, tab);
+      stat_add(st, v.z, 4 * t + 2, invT, gr, tab);
+      stat_add(st, v.w, 4 * t + 3, invT, gr, tab);
     }
   } else {
-    for (int y = tid; y < V; y += kSmpThreads) stat_add(st, z[y], y, invT, gr);
+    for (int y = tid; y < V; y += kSmpThreads) stat_add(st, z[y], y, invT, gr, tab);
   }
   sh_m[tid] = st.m;
   sh_s[tid] = st.s;
@@ -135,7 +172,7 @@ __global__ __launch_bounds__(kSmpThreads) void row_stats_kernel(
     if (tid < half) {
       Stat a = {sh_m[tid], sh_s[tid], sh_i[tid]};
       Stat c = {sh_m[tid + half], sh_s[tid + half], sh_i[tid + half]};
-      Stat m = stat_merge(a, c, invT, gr);
+      Stat m = stat_merge(a, c, invT, gr, tab);
       sh_m[tid] = m.m;
       sh_s[tid] = m.s;
       sh_i[tid] = m.i;
@@ -150,8 +187,8 @@ __global__ __launch_bounds__(kSmpThreads) void row_stats_kernel(
   }
 }
 
-__device__ __forceinline__ double prob(float z, float m, double s, double invT) {
-  return exp(((double)z - (double)m) * invT) / s;
+__device__ __forceinline__ double prob(float z, float m, double s, double invT, const Exp64Table& tab) {
+  return exp64(((double)z - (double)m) * invT, tab) / s;
 }
 
 __global__ __launch_bounds__(kWave) void decide_kernel(
@@ -160,6 +197,8 @@ __global__ __launch_bounds__(kWave) void decide_kernel(
     const float* __restrict__ smax, const double* __restrict__ ssum, const int* __restrict__ sarg,
     int* __restrict__ tokens, int* __restrict__ n_out, int8_t* __restrict__ accepted,
     int* __restrict__ desc) {
+  __shared__ Exp64Table tab;
+  exp64_init(tab);
   const int b = blockIdx.x;
   if (threadIdx.x != 0) return;
   const size_t so = (size_t)b * (2 * k + 1);
@@ -170,8 +209,8 @@ __global__ __launch_bounds__(kWave) void decide_kernel(
     if (greedy) {
       acc = x == sarg[so + i];
     } else {
-      const double p = prob(zt[((size_t)b * (k + 1) + i) * V + x], smax[so + i], ssum[so + i], invT);
-      const double qq = prob(zd[((size_t)b * k + i) * V + x], smax[so + k + 1 + i], ssum[so + k + 1 + i], invT);
+      const double p = prob(zt[((size_t)b * (k + 1) + i) * V + x], smax[so + i], ssum[so + i], invT, tab);
+      const double qq = prob(zd[((size_t)b * k + i) * V + x], smax[so + k + 1 + i], ssum[so + k + 1 + i], invT, tab);
       acc = (p >= qq) || ((double)u[(size_t)b * (k + 1) + i] * qq < p);
     }
     if (accepted) accepted[(size_t)b * k + i] = acc ? 1 : 0;
@@ -198,9 +237,11 @@ __global__ __launch_bounds__(kSmpThreads) void chunk_sum_kernel(
     const float* __restrict__ smax, const double* __restrict__ ssum, const int* __restrict__ desc,
     double* __restrict__ csum) {
   __shared__ double sh[2][kSmpThreads];
+  __shared__ Exp64Table tab;
   const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int dsc = desc[b];
   if (dsc < 0) return;
+  exp64_init(tab);
   const int istar = dsc & 0xff;
   const bool resid = (dsc >> 8) != 0;
   const int csz = ceil_div(V, kSmpChunks);
@@ -214,9 +255,9 @@ __global__ __launch_bounds__(kSmpThreads) void chunk_sum_kernel(
   const double sd = resid ? ssum[so + k + 1 + istar] : 1.0;
   double aw = 0.0, ap = 0.0;
   for (int y = y0 + tid; y < y1; y += kSmpThreads) {
-    const double p = prob(zr[y], mt, st, invT);
+    const double p = prob(zr[y], mt, st, invT, tab);
     double w = p;
-    if (resid) w = fmax(0.0, p - prob(dr[y], md, sd, invT));
+    if (resid) w = fmax(0.0, p - prob(dr[y], md, sd, invT, tab));
     aw += w;
     ap += p;
   }
@@ -244,9 +285,11 @@ __global__ __launch_bounds__(kSmpThreads) void final_draw_kernel(
   __shared__ double sh_carry, sh_t;
   __shared__ double wtot[kSmpWaves];
   __shared__ int wfound[kSmpWaves], wlast[kSmpWaves];
+  __shared__ Exp64Table tab;
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int dsc = desc[b];
   if (dsc < 0) return;
+  exp64_init(tab);
   const int istar = dsc & 0xff;
   const bool resid0 = (dsc >> 8) != 0;
   const double* cs = csum + (size_t)b * kSmpChunks * 2;
@@ -301,8 +344,8 @@ __global__ __launch_bounds__(kSmpThreads) void final_draw_kernel(
     const int y = base + tid;
     double w = 0.0;
     if (y < y1) {
-      w = prob(zr[y], mt, st, invT);
-      if (resid) w = fmax(0.0, w - prob(dr[y], md, sd, invT));
+      w = prob(zr[y], mt, st, invT, tab);
+      if (resid) w = fmax(0.0, w - prob(dr[y], md, sd, invT, tab));
     }
     // inclusive scan inside the wave, then across waves
     double incl = w;
@@ -342,8 +385,12 @@ hipError_t launch_spec_sample(const float* zt, const float* zd, const int* dtok,
   SampleWs w = sample_ws(ws, B, k, nullptr);
   const int greedy = temperature == 0.f;
   const double invT = greedy ? 0.0 : 1.0 / (double)temperature;
-  hipLaunchKernelGGL(row_stats_kernel, dim3(2 * k + 1, B), dim3(kSmpThreads), 0, stream, zt, zd, k,
-                     V, invT, greedy, w.smax, w.ssum, w.sarg);
+  if (greedy)
+    hipLaunchKernelGGL(row_stats_kernel<true>, dim3(2 * k + 1, B), dim3(kSmpThreads), 0, stream, zt, zd,
+                       k, V, invT, w.smax, w.ssum, w.sarg);
+  else
+    hipLaunchKernelGGL(row_stats_kernel<false>, dim3(2 * k + 1, B), dim3(kSmpThreads), 0, stream, zt,
+                       zd, k, V, invT, w.smax, w.ssum, w.sarg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decide_kernel, dim3(B), dim3(kWave), 0, stream, zt, zd, dtok, u, k, V, invT,

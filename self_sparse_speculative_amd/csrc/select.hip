@@ -7,9 +7,10 @@
 //
 // One workgroup per (KV head, sequence). The candidate scores are mapped to
 // order-preserving 32-bit keys (-0.0 folded onto +0.0) and held in LDS; a
-// 4-pass 8-bit radix select finds the threshold key T and how many keys equal
-// to T are needed; an ordered pass with wave ballots then writes every key
-// above T plus the lowest-position keys equal to T, in position order.
+// 4-pass 8-bit radix select (wave-aggregated histogram atomics) finds the
+// threshold key T and how many keys equal to T are needed; an ordered pass
+// with wave ballots over per-wave segments then writes every key above T plus
+// the lowest-position keys equal to T, in position order.
 // Everything is integer work on the keys, so the result is exact.
 
 #include "common.hpp"
@@ -26,15 +27,32 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Add 1 to hist[digit] for every lane with `take`, aggregating lanes that share
+// a digit: a few rounds serve the most common digits with one atomic each (the
+// leading float bits of scores are highly repetitive), then the remaining
+// lanes add individually.
+__device__ __forceinline__ void hist_add(uint32_t* hist, bool take, uint32_t digit, int lane) {
+  uint64_t pending = __ballot(take);
+#pragma unroll 1
+  for (int round = 0; round < 4 && pending != 0ull; ++round) {
+    const int leader = __ffsll((unsigned long long)pending) - 1;
+    const uint32_t d = __shfl(digit, leader, kWave);
+    const uint64_t same = __ballot(take && digit == d) & pending;
+    if (lane == leader) atomicAdd(&hist[d], (uint32_t)__popcll(same));
+    pending &= ~same;
+  }
+  if ((pending >> lane) & 1ull) atomicAdd(&hist[digit], 1u);
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ scores, int stride, const int* __restrict__ ctx_len, int Hkv,
     int s_num, int s_den, int window, int* __restrict__ idx, int nsel_cap, int* __restrict__ n_sel,
     int lds_keys) {
   extern __shared__ uint32_t keys[];
   __shared__ uint32_t hist[256];
-  __shared__ int wave_tot[2][kSelWaves];
+  __shared__ int wave_cnt[2][kSelWaves];
   __shared__ uint32_t bc_digit;
-  __shared__ int bc_remaining;
+  __shared__ int bc_remaining, bc_count;
 
   const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -54,7 +72,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const float* row = scores + ((long long)b * Hkv + kv) * stride;
   const bool in_lds = ncand <= lds_keys;
   if (in_lds) {
-    for (int j = tid; j < ncand; j += kSelThreads) keys[j] = score_key(row[j]);
+    // 8 loads in flight per thread
+    constexpr int U = 8;
+    for (int j0 = tid; j0 < ncand; j0 += U * kSelThreads) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * kSelThreads;
+        v[u] = j < ncand ? row[j] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * kSelThreads;
+        if (j < ncand) keys[j] = score_key(v[u]);
+      }
+    }
   }
   __syncthreads();
 
@@ -64,9 +96,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int t = tid; t < 256; t += kSelThreads) hist[t] = 0u;
     __syncthreads();
-    for (int j = tid; j < ncand; j += kSelThreads) {
-      const uint32_t kk = in_lds ? keys[j] : score_key(row[j]);
-      if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
+    for (int base = wave * kWave; base < ncand; base += kSelThreads) {
+      const int j = base + lane;
+      const bool valid = j < ncand;
+      const uint32_t kk = valid ? (in_lds ? keys[j] : score_key(row[j])) : 0u;
+      hist_add(hist, valid && (kk & pmask) == prefix, (kk >> shift) & 255u, lane);
     }
     __syncthreads();
     if (wave == 0) {
@@ -78,8 +112,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         c[e] = hist[255 - 4 * lane - e];
         own += c[e];
       }
-      // exclusive prefix over lanes of `own` (counts of higher digits)
-      uint32_t incl = own;
+      uint32_t incl = own;  // inclusive prefix over lanes (counts of higher digits)
 #pragma unroll
       for (int off = 1; off < kWave; off <<= 1) {
         const uint32_t v = __shfl_up(incl, off, kWave);
@@ -93,6 +126,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
           if (cum + c[e] >= (uint32_t)remaining) {
             bc_digit = 255u - 4u * lane - e;
             bc_remaining = remaining - (int)cum;
+            bc_count = (int)c[e];
             break;
           }
           cum += c[e];
@@ -103,46 +137,53 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     prefix |= bc_digit << shift;
     pmask |= 255u << shift;
     remaining = bc_remaining;
+    const bool whole_bucket = bc_count == remaining;
     __syncthreads();
+    if (whole_bucket) break;  // every key of the bucket is kept: lower digits decide nothing
   }
-  const uint32_t T = prefix;     // threshold key
-  const int need_eq = remaining; // keys equal to T that are kept (lowest positions first)
+  // Keys are compared on the resolved prefix bits: above the prefix is kept,
+  // equal to it is kept in position order while fewer than need_eq precede.
+  const uint32_t T = prefix;
+  const int need_eq = remaining;
 
-  // Ordered compaction: keep key > T, and key == T while fewer than need_eq
-  // equal keys precede it.
+  // Ordered compaction. Each wave owns one contiguous segment of positions:
+  // pass A counts keys above T and equal to T per segment, one barrier
+  // publishes the counts, pass B writes the kept positions in order.
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  int carry_eq = 0, carry_sel = 0;
-  for (int base = 0; base < ncand; base += kSelThreads) {
-    const int j = base + tid;
-    const bool valid = j < ncand;
+  const int seg = ceil_div(ceil_div(ncand, kSelWaves), kWave) * kWave;
+  const int s0 = wave * seg, s1 = min(ncand, s0 + seg);
+  int cgt = 0, ceq = 0;
+  for (int base = s0; base < s1; base += kWave) {
+    const int j = base + lane;
+    const bool valid = j < s1;
     const uint32_t kk = valid ? (in_lds ? keys[j] : score_key(row[j])) : 0u;
-    const bool eq = valid && kk == T;
-    const bool gt = valid && kk > T;
+    cgt += __popcll(__ballot(valid && (kk & pmask) > T));
+    ceq += __popcll(__ballot(valid && (kk & pmask) == T));
+  }
+  if (lane == 0) {
+    wave_cnt[0][wave] = cgt;
+    wave_cnt[1][wave] = ceq;
+  }
+  __syncthreads();
+  int eq_run = 0, sel_run = 0;
+  for (int w = 0; w < wave; ++w) {
+    const int e = wave_cnt[1][w];
+    const int taken = max(0, min(e, need_eq - eq_run));
+    sel_run += wave_cnt[0][w] + taken;
+    eq_run += e;
+  }
+  for (int base = s0; base < s1; base += kWave) {
+    const int j = base + lane;
+    const bool valid = j < s1;
+    const uint32_t kk = valid ? (in_lds ? keys[j] : score_key(row[j])) : 0u;
+    const bool eq = valid && (kk & pmask) == T;
     const uint64_t beq = __ballot(eq);
-    if (lane == 0) wave_tot[0][wave] = __popcll(beq);
-    __syncthreads();
-    int eq_before = carry_eq + __popcll(beq & lt_mask);
-    int teq = 0;
-    for (int w = 0; w < kSelWaves; ++w) {
-      const int v = wave_tot[0][w];
-      if (w < wave) eq_before += v;
-      teq += v;
-    }
-    const bool sel = gt || (eq && eq_before < need_eq);
+    const bool sel = (valid && (kk & pmask) > T) || (eq && eq_run + __popcll(beq & lt_mask) < need_eq);
     const uint64_t bsel = __ballot(sel);
-    if (lane == 0) wave_tot[1][wave] = __popcll(bsel);
-    __syncthreads();
-    int pos = carry_sel + __popcll(bsel & lt_mask);
-    int tsel = 0;
-    for (int w = 0; w < kSelWaves; ++w) {
-      const int v = wave_tot[1][w];
-      if (w < wave) pos += v;
-      tsel += v;
-    }
-    if (sel) out[pos] = j;
-    carry_eq += teq;
-    carry_sel += tsel;
-    __syncthreads();
+    const int pos = sel_run + __popcll(bsel & lt_mask);
+    if (sel && pos < ntop) out[pos] = j;
+    eq_run += __popcll(beq);
+    sel_run += __popcll(bsel);
   }
 }
 

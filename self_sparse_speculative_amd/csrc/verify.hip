@@ -30,9 +30,11 @@
 // Other dtypes / head_dim 64 (verify_generic_kernel): a plain per-row kernel
 // that re-reads the (cache-resident) chunk for each row; correctness path.
 //
-// verify_combine_kernel merges the splits per row (log-sum-exp weights, split
-// order) and records each row's log2 normaliser; verify_scores_kernel turns
-// the score partials into normalised probabilities summed over the rows.
+// verify_finalize_kernel merges the splits per row (log-sum-exp weights, split
+// order) and turns the score partials into normalised probabilities summed
+// over the rows. Splits meet at a kernel boundary: a merge inside the main
+// kernel would need an agent-scope release per workgroup, which costs more
+// than the extra launch on this multi-XCD part.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -58,16 +60,23 @@ __device__ __forceinline__ uint32_t u4_word(const uint4& v, int i) {
 template <int NT>
 __global__ __launch_bounds__(kVerThreads, NT <= 2 ? 2 : 1) void verify_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
-    const int* __restrict__ bt, int max_pages, int Hkv, int G, const int* __restrict__ seq_len,
-    int k, float scale_log2, int chunk, int nsplit, int ntile_cap, int with_scores,
-    float* __restrict__ part_o, float* __restrict__ part_ml, _Float16* __restrict__ sc_val,
-    float* __restrict__ sc_max) {
+    const int* __restrict__ bt, int max_pages, int B, int Hkv, int G,
+    const int* __restrict__ seq_len, int k, float scale_log2, int chunk, int nsplit, int ntile_cap,
+    int with_scores, float* __restrict__ part_o, float* __restrict__ part_ml,
+    _Float16* __restrict__ sc_val, float* __restrict__ sc_max) {
   constexpr int D = 128;
   constexpr int RP = 16 * NT;
   __shared__ __attribute__((aligned(16))) uint16_t vt[kVerWaves][D * kVtStride];
   __shared__ float ml_sh[kVerWaves][2][RP];
+  __shared__ int pages_sh[kVerChunkMfma / kPage];
 
-  const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  // Workgroups are dispatched round-robin over the XCDs; consecutive splits of
+  // one (sequence, KV head) pair go to the same XCD.
+  const int npairs = B * Hkv;
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int pair = (local / nsplit) * 8 + xcd, split = local % nsplit;
+  if (pair >= npairs) return;
+  const int b = pair / Hkv, kv = pair % Hkv;
   const int S = seq_len[b];
   const int c0 = split * chunk;
   if (c0 >= S) return;
@@ -107,15 +116,18 @@ __global__ __launch_bounds__(kVerThreads, NT <= 2 ? 2 : 1) void verify_mfma_kern
     for (int dt = 0; dt < 8; ++dt) oacc[nt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
+  // The chunk's physical pages, read once.
   const int* bt_row = bt + (size_t)b * max_pages;
+  const int npg = ceil_div(c1 - c0, kPage);
+  if (tid < npg) pages_sh[tid] = bt_row[(c0 >> 4) + tid];
+  __syncthreads();
   uint16_t* my_vt = vt[wave];
   const int nsub = ceil_div(c1 - c0, kSub);
 
   for (int st = wave; st < nsub; st += kVerWaves) {
     const int pos0 = c0 + st * kSub;
-    const int pg0 = pos0 >> 4;
-    const int page_a = bt_row[pg0];
-    const int page_b = (pos0 + 16 < S) ? bt_row[pg0 + 1] : page_a;
+    const int page_a = pages_sh[2 * st];
+    const int page_b = (pos0 + 16 < S) ? pages_sh[2 * st + 1] : page_a;
 
     // K rows as A fragments: lane (n16 = position in the 16-row tile, g4 = k group)
     bf16x8_t kf[2][4];
@@ -287,6 +299,7 @@ __global__ __launch_bounds__(kVerThreads, NT <= 2 ? 2 : 1) void verify_mfma_kern
     part_ml[(rec + tid) * 2] = base;
     part_ml[(rec + tid) * 2 + 1] = Ls;
   }
+
 }
 
 // Generic path: one row at a time, two passes over the chunk (max, then
@@ -393,67 +406,88 @@ __global__ __launch_bounds__(kVerThreads) void verify_generic_kernel(
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kVerThreads) void verify_combine_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_ml,
-    const int* __restrict__ seq_len, int k, int Hkv, int G, int chunk, int nsplit, int RP,
-    float* __restrict__ out, float* __restrict__ lse, float* __restrict__ lse2) {
-  const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+// Merge the splits of each (sequence, KV head) pair and normalise the score
+// partials. Blocks [0, nblk_o) each write 256 outputs of the merged rows;
+// the remaining blocks each normalise kFinTiles tiles of score partials.
+// Every block first merges the per-split (max, sum) of all rows, in split
+// order, so every value is computed the same way by every block.
+constexpr int kFinTiles = 32;  // score tiles (of 32 positions) per finalize block
+
+template <typename VT, int D>
+__global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, const VT* __restrict__ sc_val,
+    const float* __restrict__ sc_max, const int* __restrict__ seq_len, int k, int Hkv, int G, int chunk,
+    int nsplit, int ntile_cap, int RP, int nblk_o, float* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ scores, int score_stride) {
+  constexpr int kTilesPerPass = kVerThreads / kSub;
+  __shared__ float mrow[64], lrow[64], l2row[64];
+  __shared__ float wt[kTilesPerPass][64];
+  const int kv = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int S = seq_len[b];
+  const int x = blockIdx.x;
+  const int tile_beg = (x - nblk_o) * kFinTiles;
+  if (x >= nblk_o && tile_beg * kSub >= S) return;
   const int used = min(nsplit, ceil_div(S, chunk));
   const int R = (k + 1) * G, Hq = Hkv * G;
   const size_t bkv = (size_t)b * Hkv + kv;
-  constexpr int kRowsPerPass = kVerThreads / D;
-  for (int r0 = 0; r0 < R; r0 += kRowsPerPass) {
-    const int r = r0 + tid / D, d = tid % D;
-    if (r >= R) break;
-    float M = kNegInf;
-    for (int c = 0; c < used; ++c) M = fmaxf(M, part_ml[((bkv * nsplit + c) * RP + r) * 2]);
-    const float base = M == kNegInf ? 0.f : M;
-    float Ls = 0.f, A = 0.f;
-    for (int c = 0; c < used; ++c) {
-      const size_t rec = (bkv * nsplit + c) * RP + r;
-      const float w = exp2f_fast(part_ml[rec * 2] - base);
-      Ls += part_ml[rec * 2 + 1] * w;
-      A += part_o[rec * D + d] * w;
+  // Row statistics: 4 lanes per row, each over every 4th split, then a fixed
+  // butterfly over the 4 lanes (same order in every block).
+  for (int r0 = 0; r0 < R; r0 += kVerThreads / 4) {
+    const int r = r0 + tid / 4, c4 = tid & 3;
+    float m = kNegInf, l = 0.f;
+    if (r < R) {
+      for (int c = c4; c < used; c += 4) m = fmaxf(m, part_ml[((bkv * nsplit + c) * RP + r) * 2]);
     }
-    const int i = r / G, h = kv * G + r % G;
-    out[(((size_t)b * (k + 1) + i) * Hq + h) * D + d] = A / Ls;
-    if (d == 0) {
-      const float l2 = base + __log2f(Ls);
-      if (lse != nullptr) lse[((size_t)b * (k + 1) + i) * Hq + h] = l2 * kLn2;
-      lse2[bkv * RP + r] = l2;
+    m = fmaxf(m, __shfl_xor(m, 1, kWave));
+    m = fmaxf(m, __shfl_xor(m, 2, kWave));
+    const float base = m == kNegInf ? 0.f : m;
+    if (r < R) {
+      for (int c = c4; c < used; c += 4) {
+        const size_t rc = (bkv * nsplit + c) * RP + r;
+        l += part_ml[rc * 2 + 1] * exp2f_fast(part_ml[rc * 2] - base);
+      }
     }
-  }
-}
-
-template <typename VT>
-__global__ __launch_bounds__(kVerThreads) void verify_scores_kernel(
-    const VT* __restrict__ sc_val, const float* __restrict__ sc_max, const float* __restrict__ lse2,
-    const int* __restrict__ seq_len, int k, int Hkv, int G, int ntile_cap, int RP,
-    float* __restrict__ scores, int score_stride) {
-  constexpr int kTiles = kVerThreads / kSub;
-  __shared__ float w[kTiles][64];
-  const int kv = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int S = seq_len[b];
-  const int tile0 = blockIdx.x * kTiles;
-  if (tile0 * kSub >= S) return;
-  const int R = (k + 1) * G;
-  const size_t bkv = (size_t)b * Hkv + kv;
-  for (int t = tid; t < kTiles * R; t += kVerThreads) {
-    const int tl = t / R, r = t % R, tile = tile0 + tl;
-    w[tl][r] = (tile < ntile_cap && tile * kSub < S)
-                   ? exp2f_fast(sc_max[(bkv * ntile_cap + tile) * R + r] - lse2[bkv * RP + r])
-                   : 0.f;
+    l += __shfl_xor(l, 1, kWave);
+    l += __shfl_xor(l, 2, kWave);
+    if (r < R && c4 == 0) {
+      mrow[r] = base;
+      lrow[r] = l;
+      l2row[r] = base + __log2f(l);
+    }
   }
   __syncthreads();
-  const int pos = tile0 * kSub + tid;
-  if (pos < S) {
-    const int tl = tid / kSub, j = tid % kSub;
-    const VT* vals = sc_val + (bkv * ntile_cap + tile0 + tl) * R * kSub + j;
-    float acc = 0.f;
-    for (int r = 0; r < R; ++r) acc = fmaf(w[tl][r], (float)vals[r * kSub], acc);
-    scores[bkv * score_stride + pos] = acc;
+  if (x < nblk_o) {
+    const int t = x * kVerThreads + tid;
+    if (t < R * D) {
+      const int r = t / D, d = t % D;
+      float A = 0.f;
+      for (int c = 0; c < used; ++c) {
+        const size_t rc = (bkv * nsplit + c) * RP + r;
+        A += part_o[rc * D + d] * exp2f_fast(part_ml[rc * 2] - mrow[r]);
+      }
+      const int i = r / G, h = kv * G + r % G;
+      out[(((size_t)b * (k + 1) + i) * Hq + h) * D + d] = A / lrow[r];
+      if (lse != nullptr && d == 0) lse[((size_t)b * (k + 1) + i) * Hq + h] = l2row[r] * kLn2;
+    }
+    return;
+  }
+  const int ntiles = ceil_div(S, kSub);
+  const int tile_end = min(ntiles, tile_beg + kFinTiles);
+  const int tl = tid / kSub, j = tid % kSub;
+  for (int t0 = tile_beg; t0 < tile_end; t0 += kTilesPerPass) {
+    __syncthreads();
+    for (int e = tid; e < kTilesPerPass * R; e += kVerThreads) {
+      const int et = e / R, r = e % R, tile = t0 + et;
+      wt[et][r] = tile < tile_end ? exp2f_fast(sc_max[(bkv * ntile_cap + tile) * R + r] - l2row[r]) : 0.f;
+    }
+    __syncthreads();
+    const int tile = t0 + tl, pos = tile * kSub + j;
+    if (tile < tile_end && pos < S) {
+      const VT* vals = sc_val + (bkv * ntile_cap + tile) * R * kSub + j;
+      float acc = 0.f;
+      for (int r = 0; r < R; ++r) acc = fmaf(wt[tl][r], (float)vals[r * kSub], acc);
+      scores[bkv * score_stride + pos] = acc;
+    }
   }
 }
 
@@ -491,8 +525,10 @@ template <int NT>
 static void launch_mfma(const VerifyPlan& p, const void* q, const void* kp, const void* vp,
                         const int* bt, int max_pages, int Hkv, const int* seq_len, int B, int k,
                         float sl2, int with_scores, char* ws, hipStream_t stream) {
-  hipLaunchKernelGGL((verify_mfma_kernel<NT>), dim3(p.nsplit, Hkv, B), dim3(kVerThreads), 0, stream,
-                     (const bf16_t*)q, (const bf16_t*)kp, (const bf16_t*)vp, bt, max_pages, Hkv,
+  const int npairs = B * Hkv;
+  const int nblocks = ceil_div(npairs, 8) * 8 * p.nsplit;
+  hipLaunchKernelGGL((verify_mfma_kernel<NT>), dim3(nblocks), dim3(kVerThreads), 0, stream,
+                     (const bf16_t*)q, (const bf16_t*)kp, (const bf16_t*)vp, bt, max_pages, B, Hkv,
                      p.G, seq_len, k, sl2, p.chunk, p.nsplit, p.ntile_cap, with_scores,
                      (float*)(ws + p.off_part_o), (float*)(ws + p.off_part_ml),
                      (_Float16*)(ws + p.off_sc_val), (float*)(ws + p.off_sc_max));
@@ -507,13 +543,16 @@ hipError_t launch_verify(int dtype, int D, const void* q, const void* kp, const 
   const float sl2 = scale * kLog2e;
   const int with_scores = scores != nullptr;
   if (p.mfma) {
+#define S3R_MFMA(NTV) \
+  launch_mfma<NTV>(p, q, kp, vp, bt, max_pages, Hkv, seq_len, B, k, sl2, with_scores, ws, stream)
     switch (p.NT) {
-      case 1: launch_mfma<1>(p, q, kp, vp, bt, max_pages, Hkv, seq_len, B, k, sl2, with_scores, ws, stream); break;
-      case 2: launch_mfma<2>(p, q, kp, vp, bt, max_pages, Hkv, seq_len, B, k, sl2, with_scores, ws, stream); break;
-      case 3: launch_mfma<3>(p, q, kp, vp, bt, max_pages, Hkv, seq_len, B, k, sl2, with_scores, ws, stream); break;
-      case 4: launch_mfma<4>(p, q, kp, vp, bt, max_pages, Hkv, seq_len, B, k, sl2, with_scores, ws, stream); break;
+      case 1: S3R_MFMA(1); break;
+      case 2: S3R_MFMA(2); break;
+      case 3: S3R_MFMA(3); break;
+      case 4: S3R_MFMA(4); break;
       default: return hipErrorInvalidValue;
     }
+#undef S3R_MFMA
   } else {
 #define S3R_GEN(TT, DD)                                                                              \
   hipLaunchKernelGGL((verify_generic_kernel<TT, DD>), dim3(p.nsplit, Hkv, B), dim3(kVerThreads), 0, \
@@ -530,26 +569,23 @@ hipError_t launch_verify(int dtype, int D, const void* q, const void* kp, const 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  float* lse2 = (float*)(ws + p.off_lse2);
-  if (D == 128)
-    hipLaunchKernelGGL((verify_combine_kernel<128>), dim3(Hkv, B), dim3(kVerThreads), 0, stream,
-                       (const float*)(ws + p.off_part_o), (const float*)(ws + p.off_part_ml), seq_len,
-                       k, Hkv, p.G, p.chunk, p.nsplit, p.RP, out, lse, lse2);
-  else
-    hipLaunchKernelGGL((verify_combine_kernel<64>), dim3(Hkv, B), dim3(kVerThreads), 0, stream,
-                       (const float*)(ws + p.off_part_o), (const float*)(ws + p.off_part_ml), seq_len,
-                       k, Hkv, p.G, p.chunk, p.nsplit, p.RP, out, lse, lse2);
-  e = hipGetLastError();
-  if (e != hipSuccess || !with_scores) return e;
-  const dim3 sgrid(ceil_div(p.ntile_cap, kVerThreads / kSub), Hkv, B);
-  if (p.mfma)
-    hipLaunchKernelGGL((verify_scores_kernel<_Float16>), sgrid, dim3(kVerThreads), 0, stream,
-                       (const _Float16*)(ws + p.off_sc_val), (const float*)(ws + p.off_sc_max), lse2,
-                       seq_len, k, Hkv, p.G, p.ntile_cap, p.RP, scores, score_stride);
-  else
-    hipLaunchKernelGGL((verify_scores_kernel<float>), sgrid, dim3(kVerThreads), 0, stream,
-                       (const float*)(ws + p.off_sc_val), (const float*)(ws + p.off_sc_max), lse2,
-                       seq_len, k, Hkv, p.G, p.ntile_cap, p.RP, scores, score_stride);
+  const int nblk_o = ceil_div(p.R * D, kVerThreads);
+  const int nblk_s = with_scores ? ceil_div(p.ntile_cap, kFinTiles) : 0;
+  const dim3 fgrid(nblk_o + nblk_s, Hkv, B);
+#define S3R_FIN(VT, DD)                                                                             \
+  hipLaunchKernelGGL((verify_finalize_kernel<VT, DD>), fgrid, dim3(kVerThreads), 0, stream,        \
+                     (const float*)(ws + p.off_part_o), (const float*)(ws + p.off_part_ml),         \
+                     (const VT*)(ws + p.off_sc_val), (const float*)(ws + p.off_sc_max), seq_len, k, \
+                     Hkv, p.G, p.chunk, p.nsplit, p.ntile_cap, p.RP, nblk_o, out, lse, scores,      \
+                     score_stride)
+  if (p.mfma) {
+    S3R_FIN(_Float16, 128);
+  } else if (D == 128) {
+    S3R_FIN(float, 128);
+  } else {
+    S3R_FIN(float, 64);
+  }
+#undef S3R_FIN
   return hipGetLastError();
 }
 
