@@ -154,7 +154,8 @@ s3r_status s3r_select(const float* scores, int32_t score_stride, const int32_t* 
  *   out       device f32 [B][Hq][head_dim]; lse device f32 [B][Hq] or NULL.
  *   ws        workspace of s3r_sparse_decode_workspace_bytes(B, Hq, head_dim,
  *             max_attend) bytes.
- * UNSUPPORTED: Hq / Hkv > 16.
+ * UNSUPPORTED: Hq / Hkv > 16 (bf16, head_dim 128) or Hq / Hkv not in {1, 2, 4, 8}
+ * (other dtype / head_dim combinations).
  */
 size_t s3r_sparse_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head_dim, int32_t max_attend);
 s3r_status s3r_sparse_decode_attn(const void* q, const s3r_paged_kv* kv, const int32_t* idx,

@@ -242,6 +242,206 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
   }
 }
 
+// bf16, head_dim 128: the same step on MFMA. Per 32-position subtile a wave
+// gathers the K rows straight into A fragments of 16x16x32 bf16 MFMA tiles
+// (S^T = K Q^T, the G query heads of the KV head are the N side), keeps the
+// online softmax per head in the lanes that own the head, transposes the
+// gathered V rows through LDS and accumulates O^T += V^T P^T on MFMA. The
+// vector ALU only does the softmax, so the kernel stays a pure gather.
+typedef __bf16 dbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float df32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kDsub = 32;       // positions per subtile
+constexpr int kDvtStride = 40;  // LDS row stride (uint16) of a transposed V subtile
+
+__device__ __forceinline__ uint32_t dperm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+__device__ __forceinline__ uint32_t du4_word(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+__global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
+    const int* __restrict__ bt, int max_pages, int Hkv, int G, const int* __restrict__ idx,
+    int nsel_cap, const int* __restrict__ n_sel, const int* __restrict__ sel_len,
+    const int* __restrict__ cur_len, float scale_log2, int chunk, int nsplit, float* __restrict__ part) {
+  constexpr int D = 128;
+  constexpr int kWaves = kDecThreads / kWave;
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kWaves][D * kDvtStride];
+  __shared__ float ml_sh[kWaves][2][16];
+  __shared__ int rows[kDecChunkMfma];
+
+  const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n16 = lane & 15, g4 = lane >> 4;
+  const int ns = n_sel[b], L = sel_len[b], cur = cur_len[b];
+  const int total = ns + (cur - L);
+  const int p0 = split * chunk;
+  if (p0 >= total) return;
+  const int p1 = min(total, p0 + chunk);
+  const int Hq = Hkv * G;
+
+  // Resolve the split's positions to cache rows (page, KV head, slot) once.
+  const int* idx_row = idx + ((size_t)b * Hkv + kv) * nsel_cap;
+  const int* bt_row = bt + (size_t)b * max_pages;
+  for (int j = p0 + tid; j < p1; j += kDecThreads) {
+    const int pos = j < ns ? idx_row[j] : L + (j - ns);
+    rows[j - p0] = (bt_row[pos >> 4] * Hkv + kv) * kPage + (pos & 15);
+  }
+  __syncthreads();
+  const int cnt = p1 - p0;
+
+  dbf16x8_t qf[4];
+  {
+    const int r = n16;
+    if (r < G) {
+      const bf16_t* qp = q + ((size_t)b * Hq + kv * G + r) * D + g4 * 8;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) qf[kk] = *reinterpret_cast<const dbf16x8_t*>(qp + kk * 32);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) qf[kk] = dbf16x8_t{};
+    }
+  }
+  float m_run = kNegInf, l_run = 0.f;
+  df32x4_t oacc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) oacc[dt] = df32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint16_t* my_vt = vt[wave];
+  const int nsub = ceil_div(cnt, kDsub);
+
+  for (int st = wave; st < nsub; st += kWaves) {
+    const int j0 = st * kDsub;  // subtile start within the split
+    dbf16x8_t kf[2][4];
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      const int jj = j0 + pt * 16 + n16;
+      const size_t row = (size_t)rows[jj < cnt ? jj : j0];
+      const bf16_t* kb = kp + row * D + g4 * 8;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kf[pt][kk] = *reinterpret_cast<const dbf16x8_t*>(kb + kk * 32);
+    }
+    uint4 vraw[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int task = lane + 64 * tt;
+      const int a = task & 7, c = task >> 3;
+      // positions 4a..4a+3 of the subtile (first page half: a < 4)
+      const int pbase = (a < 4 ? 0 : 16) + (a & 3) * 4;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int jj = j0 + pbase + v;
+        const size_t row = (size_t)rows[jj < cnt ? jj : j0];
+        vraw[tt][v] = *reinterpret_cast<const uint4*>(vp + row * D + c * 8);
+      }
+    }
+    df32x4_t s[2];
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      df32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[pt][kk], qf[kk], acc, 0, 0, 0);
+      s[pt] = acc;
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int jj = j0 + pt * 16 + 4 * g4 + v;
+        const float x = jj < cnt ? s[pt][v] * scale_log2 : kNegInf;
+        s[pt][v] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float mn = fmaxf(m_run, mx);
+    const float base = mn == kNegInf ? 0.f : mn;
+    const float alpha = exp2f_fast(m_run - base);
+    float pv[2][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        pv[pt][v] = exp2f_fast(s[pt][v] - base);
+        psum += pv[pt][v];
+      }
+    }
+    l_run = l_run * alpha + psum;
+    m_run = mn;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[dt] *= alpha;
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    u32x4_t pw = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
+                  pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])};
+    const dbf16x8_t pf = __builtin_bit_cast(dbf16x8_t, pw);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int task = lane + 64 * tt;
+      const int a = task & 7, c = task >> 3;
+      const int slot = (a & 3) * 8 + (a >> 2) * 4;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const int wi = e >> 1;
+        const uint32_t lo = dperm(du4_word(vraw[tt][1], wi), du4_word(vraw[tt][0], wi), sel);
+        const uint32_t hi = dperm(du4_word(vraw[tt][3], wi), du4_word(vraw[tt][2], wi), sel);
+        *reinterpret_cast<uint2*>(my_vt + (c * 8 + e) * kDvtStride + slot) = make_uint2(lo, hi);
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const dbf16x8_t vfrag = *reinterpret_cast<const dbf16x8_t*>(my_vt + (dt * 16 + n16) * kDvtStride + g4 * 8);
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfrag, pf, oacc[dt], 0, 0, 0);
+    }
+  }
+
+  // Merge the waves. Row (head) n16; l is a per-lane partial.
+  l_run += __shfl_xor(l_run, 16, kWave);
+  l_run += __shfl_xor(l_run, 32, kWave);
+  __syncthreads();
+  if (g4 == 0) {
+    ml_sh[wave][0][n16] = m_run;
+    ml_sh[wave][1][n16] = l_run;
+  }
+  __syncthreads();
+  float* obuf = reinterpret_cast<float*>(&vt[0][0]);  // 16 x D floats
+  float M = kNegInf;
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml_sh[w][0][n16]);
+  const float baseM = M == kNegInf ? 0.f : M;
+  const float fac = exp2f_fast(m_run - baseM);
+  for (int w = 0; w < kWaves; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int o = n16 * D + dt * 16 + g4 * 4 + v;
+          const float val = oacc[dt][v] * fac;
+          obuf[o] = (w == 0) ? val : obuf[o] + val;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  for (int t = tid; t < G * D; t += kDecThreads) {
+    const int g = t / D, d = t % D;
+    float* rec = part + (((size_t)b * Hq + kv * G + g) * nsplit + split) * (D + 2);
+    rec[2 + d] = obuf[g * D + d];
+    if (d == 0) {
+      float Mg = kNegInf;
+      for (int w = 0; w < kWaves; ++w) Mg = fmaxf(Mg, ml_sh[w][0][g]);
+      const float bg = Mg == kNegInf ? 0.f : Mg;
+      float Ls = 0.f;
+      for (int w = 0; w < kWaves; ++w) Ls += ml_sh[w][1][g] * exp2f_fast(ml_sh[w][0][g] - bg);
+      rec[0] = bg;
+      rec[1] = Ls;
+    }
+  }
+}
+
 // Merge the splits of one (sequence, query head) in split order.
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(
@@ -265,10 +465,15 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(
   if (lse != nullptr && d == 0) lse[(size_t)b * Hq + h] = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : kNegInf;
 }
 
-int decode_nsplit(int max_attend) { return ceil_div(max_attend < 1 ? 1 : max_attend, kDecChunk); }
+static int decode_chunk(int dtype, int D) { return (dtype == 1 && D == 128) ? kDecChunkMfma : kDecChunk; }
 
+int decode_nsplit(int dtype, int D, int max_attend) {
+  return ceil_div(max_attend < 1 ? 1 : max_attend, decode_chunk(dtype, D));
+}
+
+// Sized for the smaller (vector-path) chunk, so one size serves every path.
 size_t decode_workspace_bytes(int B, int Hq, int D, int max_attend) {
-  return (size_t)B * Hq * decode_nsplit(max_attend) * (D + 2) * sizeof(float);
+  return (size_t)B * Hq * decode_nsplit(0, D, max_attend) * (D + 2) * sizeof(float);
 }
 
 template <typename T, int D, int G>
@@ -310,7 +515,7 @@ static hipError_t launch_decode_d(int G, const void* q, const void* kp, const vo
 }
 
 bool decode_supported(int dtype, int D, int G) {
-  (void)dtype;
+  if (dtype == 1 && D == 128) return G >= 1 && G <= 16;
   return (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4 || G == 8);
 }
 
@@ -319,9 +524,19 @@ hipError_t launch_sparse_decode(int dtype, int D, int G, const void* q, const vo
                                 const int* idx, int nsel_cap, const int* n_sel, const int* sel_len,
                                 const int* cur_len, int B, float scale, int max_attend, float* out,
                                 float* lse, void* ws, hipStream_t stream) {
-  const int nsplit = decode_nsplit(max_attend);
+  const int nsplit = decode_nsplit(dtype, D, max_attend);
   const float sl2 = scale * kLog2e;
   float* part = (float*)ws;
+  if (dtype == 1 && D == 128) {
+    hipLaunchKernelGGL(sparse_decode_mfma_kernel, dim3(nsplit, Hkv, B), dim3(kDecThreads), 0, stream,
+                       (const bf16_t*)q, (const bf16_t*)kp, (const bf16_t*)vp, bt, max_pages, Hkv, G, idx,
+                       nsel_cap, n_sel, sel_len, cur_len, sl2, kDecChunkMfma, nsplit, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_combine_kernel<128>), dim3(Hkv * G, B), dim3(128), 0, stream, part, n_sel,
+                       sel_len, cur_len, Hkv * G, kDecChunkMfma, nsplit, out, lse);
+    return hipGetLastError();
+  }
   if (dtype == 1) {
     if (D == 128)
       return launch_decode_d<bf16_t, 128>(G, q, kp, vp, bt, max_pages, Hkv, idx, nsel_cap, n_sel,

@@ -14,10 +14,16 @@ struct BF16Val {
 };
 
 constexpr int kSelLdsKeysMax = 32768;  // keys held in LDS (128 KB); longer contexts re-read global
-constexpr int kDecChunk = 256;         // attended positions per draft split
+constexpr int kDecChunk = 256;         // attended positions per draft split (vector path)
+constexpr int kDecChunkMfma = 512;     // attended positions per draft split (bf16 x 128 MFMA path)
 constexpr int kVerChunkMfma = 1024;    // context positions per verify split (bf16 x 128 path)
 constexpr int kVerChunkGeneric = 256;  // context positions per verify split (generic path)
 constexpr int kSmpChunks = 64;         // vocabulary chunks of the final draw
+#ifndef S3R_VERIFY_BATCH_MB
+#define S3R_VERIFY_BATCH_MB 0
+#endif
+// Byte budget of the verify partials per batch of (sequence, KV head) pairs (0: one batch).
+constexpr size_t kVerBatchBytes = (size_t)S3R_VERIFY_BATCH_MB << 20;
 
 hipError_t launch_select(const float* scores, int stride, const int* ctx_len, int B, int Hkv,
                          int max_ctx_len, int s_num, int s_den, int window, int* idx, int nsel_cap,
@@ -32,7 +38,7 @@ hipError_t launch_sparse_decode(int dtype, int D, int G, const void* q, const vo
                                 float* lse, void* ws, hipStream_t stream);
 
 struct VerifyPlan {
-  int G, R, NT, RP, chunk, nsplit, ntile_cap;
+  int G, R, NT, RP, chunk, nsplit, ntile_cap, pairs_per_batch;
   bool mfma;
   size_t off_part_o, off_part_ml, off_lse2, off_sc_max, off_sc_val, bytes;
 };

@@ -101,7 +101,9 @@ def test_decode_validation(lib):
     assert f(*args(kv, scale=float("nan"))) == INVALID
     assert f(*args(_kv(page=8))) == UNSUPPORTED
     assert f(*args(_kv(D=96))) == UNSUPPORTED
-    assert f(*args(kv, Hq=8 * 3)) == UNSUPPORTED          # G = 3
+    assert f(*args(kv, Hq=8 * 3)) != UNSUPPORTED          # G = 3 runs on the bf16 x 128 path
+    assert f(*args(_kv(dtype=0), Hq=8 * 3)) == UNSUPPORTED  # ... but not on the vector path
+    assert f(*args(kv, Hq=8 * 32)) == UNSUPPORTED         # G = 32
     assert f(*args(_kv(dtype=7))) == INVALID
     assert f(*args(kv, ws=ws_ok - 1)) == WORKSPACE
     assert ws_ok == 4 * 32 * 1 * 130 * 4

@@ -129,6 +129,13 @@ def test_draft_bf16(key, cid, ov):
     _draft_case(cfg, batch, t, [1, cfg.k], range(cfg.B), TOL_BF16, False)
 
 
+@pytest.mark.parametrize("G", [1, 3, 6, 16])
+def test_draft_bf16_group_sizes(G):
+    # head groups the vector path does not cover; long lists span several 512-position splits
+    cfg, batch, t = _batch(f"c2g{G}", 2, B=3, Hq=2 * G, Hkv=2, lengths=("uniform", 3000, 30000), s_num=1, s_den=10)
+    _draft_case(cfg, batch, t, [1, cfg.k], range(cfg.B), TOL_BF16, False)
+
+
 def test_draft_full_budget_is_dense():
     cfg, batch, t = _batch("c2full", 2, B=3, lengths=("uniform", 300, 700), s_num=1, s_den=1)
     idx, n_sel = run_select(cfg, batch, t)
