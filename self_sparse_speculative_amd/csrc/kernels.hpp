@@ -13,10 +13,16 @@ struct BF16Val {
   __device__ __forceinline__ operator float() const { return __uint_as_float((uint32_t)bits << 16); }
 };
 
-constexpr int kSelLdsKeysMax = 32768;  // keys held in LDS (128 KB); longer contexts re-read global
 constexpr int kDecChunk = 256;         // attended positions per draft split (vector path)
 constexpr int kDecChunkMfma = 512;     // attended positions per draft split (bf16 x 128 MFMA path)
-constexpr int kVerChunkMfma = 1024;    // context positions per verify split (bf16 x 128 path)
+#ifndef S3R_VERIFY_CHUNK
+#define S3R_VERIFY_CHUNK 2048
+#endif
+constexpr int kVerChunkMfma = S3R_VERIFY_CHUNK;  // context positions per verify split (bf16 x 128 path)
+#ifndef S3R_VERIFY_PREFETCH
+#define S3R_VERIFY_PREFETCH 0
+#endif
+constexpr bool kVerPrefetch = S3R_VERIFY_PREFETCH != 0;  // software-pipelined K/V loads in verify
 constexpr int kVerChunkGeneric = 256;  // context positions per verify split (generic path)
 constexpr int kSmpChunks = 64;         // vocabulary chunks of the final draw
 #ifndef S3R_VERIFY_BATCH_MB

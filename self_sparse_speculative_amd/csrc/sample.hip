@@ -45,32 +45,31 @@ static size_t align256s(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Float64 exponential, table-driven (Tang, "Table-driven implementation of the
 // exponential function in IEEE floating-point arithmetic", ACM TOMS 1989):
-// x = (32 m + j) ln2/32 + r with |r| <= ln2/64, exp(x) = 2^m 2^(j/32) (1 + p(r)),
-// p the degree-6 Taylor polynomial of expm1 (truncation < 4e-18). The 32 table
-// entries 2^(j/32) are computed once per workgroup with the library exp2.
-// Relative error ~1e-15 for the arguments used here (x <= 0).
+// x = (128 m + j) ln2/128 + r with |r| <= ln2/256, exp(x) = 2^m 2^(j/128) (1 + p(r)),
+// p the degree-4 Taylor polynomial of expm1 (truncation < 2e-15 relative). The
+// 128 table entries 2^(j/128) are computed once per workgroup with the
+// library exp2. Relative error ~2e-15 for the arguments used here (x <= 0).
+constexpr int kExpTab = 128;
 struct Exp64Table {
-  double t[32];
+  double t[kExpTab];
 };
 
 __device__ __forceinline__ void exp64_init(Exp64Table& tab) {
-  if (threadIdx.x < 32) tab.t[threadIdx.x] = exp2((double)threadIdx.x / 32.0);
+  for (int j = threadIdx.x; j < kExpTab; j += blockDim.x) tab.t[j] = exp2((double)j / kExpTab);
   __syncthreads();
 }
 
 __device__ __forceinline__ double exp64(double x, const Exp64Table& tab) {
   x = fmax(x, -1000.0);
-  const double kf = rint(x * (32.0 / 0.6931471805599453));
+  const double kf = rint(x * (kExpTab / 0.6931471805599453));
   const int ki = (int)kf;
-  const double r = fma(-kf, 0.6931471805599453 / 32.0, x);
-  double p = fma(r, 1.0 / 720.0, 1.0 / 120.0);
-  p = fma(r, p, 1.0 / 24.0);
-  p = fma(r, p, 1.0 / 6.0);
+  const double r = fma(-kf, 0.6931471805599453 / kExpTab, x);
+  double p = fma(r, 1.0 / 24.0, 1.0 / 6.0);
   p = fma(r, p, 0.5);
   p = fma(r, p, 1.0);
   p = p * r;
-  const double s = tab.t[ki & 31];
-  return ldexp(fma(s, p, s), ki >> 5);
+  const double s = tab.t[ki & (kExpTab - 1)];
+  return ldexp(fma(s, p, s), ki >> 7);
 }
 
 static SampleWs sample_ws(void* ws, int B, int k, size_t* bytes_out) {
@@ -154,12 +153,40 @@ __global__ __launch_bounds__(kSmpThreads) void row_stats_kernel(
   if ((V & 3) == 0) {
     const float4* z4 = reinterpret_cast<const float4*>(z);
     const int n4 = V >> 2;
-    for (int t = tid; t < n4; t += kSmpThreads) {
-      const float4 v = z4[t];
-      stat_add(st, v.x, 4 * t, invT, gr, tab);
-      stat_add(st, v.y, 4 * t + 1, invT, gr, tab);
-      stat_add(st, v.z, 4 * t + 2, invT, gr, tab);
-      stat_add(st, v.w, 4 * t + 3, invT, gr, tab);
+    constexpr int U = 4;  // float4 loads in flight per thread
+    for (int t0 = tid; t0 < n4; t0 += U * kSmpThreads) {
+      float4 vv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + u * kSmpThreads;
+        vv[u] = t < n4 ? z4[t] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + u * kSmpThreads;
+        const float4 v = vv[u];
+        if (t >= n4) continue;
+        if (gr) {
+          stat_add(st, v.x, 4 * t, invT, gr, tab);
+          stat_add(st, v.y, 4 * t + 1, invT, gr, tab);
+          stat_add(st, v.z, 4 * t + 2, invT, gr, tab);
+          stat_add(st, v.w, 4 * t + 3, invT, gr, tab);
+          continue;
+        }
+        // raise the running maximum once per group of 4, then 4 plain terms
+        const float gm = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+        if (__any(gm > st.m)) {
+          const bool up = gm > st.m;
+          const int gi = v.x == gm ? 0 : (v.y == gm ? 1 : (v.z == gm ? 2 : 3));
+          const double a = st.m == kNegInf ? 0.0 : exp64(((double)st.m - (double)gm) * invT, tab);
+          st.s = up ? st.s * a : st.s;
+          st.i = up ? 4 * t + gi : st.i;
+          st.m = up ? gm : st.m;
+        }
+        const double m = (double)st.m;
+        st.s += exp64(((double)v.x - m) * invT, tab) + exp64(((double)v.y - m) * invT, tab) +
+                exp64(((double)v.z - m) * invT, tab) + exp64(((double)v.w - m) * invT, tab);
+      }
     }
   } else {
     for (int y = tid; y < V; y += kSmpThreads) stat_add(st, z[y], y, invT, gr, tab);
@@ -254,12 +281,24 @@ __global__ __launch_bounds__(kSmpThreads) void chunk_sum_kernel(
   const float md = resid ? smax[so + k + 1 + istar] : 0.f;
   const double sd = resid ? ssum[so + k + 1 + istar] : 1.0;
   double aw = 0.0, ap = 0.0;
-  for (int y = y0 + tid; y < y1; y += kSmpThreads) {
-    const double p = prob(zr[y], mt, st, invT, tab);
-    double w = p;
-    if (resid) w = fmax(0.0, p - prob(dr[y], md, sd, invT, tab));
-    aw += w;
-    ap += p;
+  constexpr int U = 4;  // loads in flight per thread
+  for (int y0u = y0 + tid; y0u < y1; y0u += U * kSmpThreads) {
+    float zt_v[U], zd_v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int y = y0u + u * kSmpThreads;
+      zt_v[u] = y < y1 ? zr[y] : 0.f;
+      zd_v[u] = (resid && y < y1) ? dr[y] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (y0u + u * kSmpThreads >= y1) continue;
+      const double p = prob(zt_v[u], mt, st, invT, tab);
+      double w = p;
+      if (resid) w = fmax(0.0, p - prob(zd_v[u], md, sd, invT, tab));
+      aw += w;
+      ap += p;
+    }
   }
   sh[0][tid] = aw;
   sh[1][tid] = ap;

@@ -5,21 +5,21 @@
 // mean?", mechanism paragraph: the sparse drafter reads the newest positions
 // plus the top-scoring ones from the verifier's last attention pass.
 //
-// One workgroup per (KV head, sequence). The candidate scores are mapped to
-// order-preserving 32-bit keys (-0.0 folded onto +0.0) and held in LDS; a
-// 4-pass 8-bit radix select (wave-aggregated histogram atomics) finds the
-// threshold key T and how many keys equal to T are needed; an ordered pass
-// with wave ballots over per-wave segments then writes every key above T plus
-// the lowest-position keys equal to T, in position order.
-// Everything is integer work on the keys, so the result is exact.
+// One workgroup (512 threads) per (KV head, sequence). Scores are mapped to
+// order-preserving 32-bit keys (-0.0 folded onto +0.0). A 12-bit histogram
+// (wave-aggregated LDS atomics) finds the bucket that holds the threshold
+// rank; the keys of that bucket are compacted into LDS and an exact radix
+// select on their low 20 bits yields the threshold key T and how many keys
+// equal to T are kept; an ordered pass with wave ballots then writes every key
+// above T plus the lowest-position keys equal to T, in position order. The row
+// is re-read from global memory (L2 / Infinity Cache) for each pass, which
+// keeps the LDS footprint small enough for four workgroups per CU. Everything
+// is integer work on the keys, so the result is exact.
 
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace s3r {
-
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / kWave;
 
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -35,8 +35,8 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, bool take, uint32_t dig
   uint64_t pending = __ballot(take);
 #pragma unroll 1
   for (int round = 0; round < 4 && pending != 0ull; ++round) {
-    const int leader = __ffsll((unsigned long long)pending) - 1;
-    const uint32_t d = __shfl(digit, leader, kWave);
+    const int leader = __ffsll((unsigned long long)pending) - 1;  // wave-uniform
+    const uint32_t d = __builtin_amdgcn_readlane(digit, leader);
     const uint64_t same = __ballot(take && digit == d) & pending;
     if (lane == leader) atomicAdd(&hist[d], (uint32_t)__popcll(same));
     pending &= ~same;
@@ -44,15 +44,70 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, bool take, uint32_t dig
   if ((pending >> lane) & 1ull) atomicAdd(&hist[digit], 1u);
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(
+// ---------------------------------------------------------------------------
+// Streaming selector (default). The candidate keys are read from global memory
+// (the row stays in L2 / Infinity Cache between passes) so the workgroup needs
+// little LDS and several workgroups share a CU:
+//   A. 12-bit histogram of the keys (sign, exponent, 3 mantissa bits);
+//   B. the bucket holding the threshold rank is compacted into an LDS list
+//      (key, position) when it has at most kFsCap keys, and an exact radix
+//      select over the remaining 20 bits runs on the list; a larger bucket
+//      (e.g. many equal scores) continues with radix passes over the row;
+//   C. the ordered output pass of the LDS kernel, on masked keys.
+constexpr int kFsThreads = 512;
+constexpr int kFsWaves = kFsThreads / kWave;
+constexpr int kFsBins = 4096;
+constexpr int kFsCap = 2048;
+
+// Find the bucket holding the key of rank `rank` (1-based, counted from the
+// largest key). hist has nbins counts in key order. Every thread returns the
+// bucket, the rank inside it and the bucket's count.
+__device__ __forceinline__ void find_rank_bucket(const uint32_t* hist, int nbins, int rank, int* wsum,
+                                                 int* out3) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int per = (nbins + kFsThreads - 1) / kFsThreads;
+  int own = 0;
+  for (int e = 0; e < per; ++e) {
+    const int i = tid * per + e;  // i-th bucket from the top
+    if (i < nbins) own += (int)hist[nbins - 1 - i];
+  }
+  int incl = own;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int v = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += v;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  const int excl = before + incl - own;
+  if (excl < rank && rank <= excl + own) {
+    int cum = excl;
+    for (int e = 0; e < per; ++e) {
+      const int i = tid * per + e;
+      const int c = (int)hist[nbins - 1 - i];
+      if (cum + c >= rank) {
+        out3[0] = nbins - 1 - i;
+        out3[1] = rank - cum;
+        out3[2] = c;
+        break;
+      }
+      cum += c;
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kFsThreads) void select_stream_kernel(
     const float* __restrict__ scores, int stride, const int* __restrict__ ctx_len, int Hkv,
-    int s_num, int s_den, int window, int* __restrict__ idx, int nsel_cap, int* __restrict__ n_sel,
-    int lds_keys) {
-  extern __shared__ uint32_t keys[];
-  __shared__ uint32_t hist[256];
-  __shared__ int wave_cnt[2][kSelWaves];
-  __shared__ uint32_t bc_digit;
-  __shared__ int bc_remaining, bc_count;
+    int s_num, int s_den, int window, int* __restrict__ idx, int nsel_cap, int* __restrict__ n_sel) {
+  __shared__ uint32_t hist[kFsBins];
+  __shared__ uint32_t lkey[kFsCap];
+  __shared__ int wsum[kFsWaves];
+  __shared__ int wave_cnt[2][kFsWaves];
+  __shared__ int res[3];
+  __shared__ int list_n;
 
   const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -63,102 +118,127 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   if (kv == 0 && tid == 0) n_sel[b] = n;
   const int ncand = L - newest, ntop = n - newest;
   int* out = idx + ((long long)b * Hkv + kv) * nsel_cap;
-  for (int t = tid; t < newest; t += kSelThreads) out[ntop + t] = ncand + t;
+  for (int t = tid; t < newest; t += kFsThreads) out[ntop + t] = ncand + t;
   if (ntop <= 0) return;
   if (ntop >= ncand) {
-    for (int t = tid; t < ncand; t += kSelThreads) out[t] = t;
+    for (int t = tid; t < ncand; t += kFsThreads) out[t] = t;
     return;
   }
   const float* row = scores + ((long long)b * Hkv + kv) * stride;
-  const bool in_lds = ncand <= lds_keys;
-  if (in_lds) {
-    // 8 loads in flight per thread
-    constexpr int U = 8;
-    for (int j0 = tid; j0 < ncand; j0 += U * kSelThreads) {
-      float v[U];
+
+  // A. histogram of the top 12 bits
+  for (int t = tid; t < kFsBins; t += kFsThreads) hist[t] = 0u;
+  if (tid == 0) list_n = 0;
+  __syncthreads();
+  for (int base = wave * kWave * 4; base < ncand; base += kFsThreads * 4) {
+    uint32_t kk[4];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = j0 + u * kSelThreads;
-        v[u] = j < ncand ? row[j] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = j0 + u * kSelThreads;
-        if (j < ncand) keys[j] = score_key(v[u]);
-      }
+    for (int u = 0; u < 4; ++u) {
+      const int j = base + u * kWave + lane;
+      kk[u] = j < ncand ? score_key(row[j]) : 0u;
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) hist_add(hist, base + u * kWave + lane < ncand, kk[u] >> 20, lane);
   }
   __syncthreads();
+  find_rank_bucket(hist, kFsBins, ntop, wsum, res);
+  uint32_t prefix = (uint32_t)res[0] << 20, pmask = 0xfff00000u;
+  int remaining = res[1];
+  const int bucket_n = res[2];
 
-  // Radix select of the ntop-th largest key, 8 bits at a time from the top.
-  uint32_t prefix = 0u, pmask = 0u;
-  int remaining = ntop;  // rank of the wanted key among keys matching prefix
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int t = tid; t < 256; t += kSelThreads) hist[t] = 0u;
-    __syncthreads();
-    for (int base = wave * kWave; base < ncand; base += kSelThreads) {
-      const int j = base + lane;
-      const bool valid = j < ncand;
-      const uint32_t kk = valid ? (in_lds ? keys[j] : score_key(row[j])) : 0u;
-      hist_add(hist, valid && (kk & pmask) == prefix, (kk >> shift) & 255u, lane);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // lane l owns digits 255-4l .. 252-4l (top digits first)
-      uint32_t c[4];
-      uint32_t own = 0;
+  if (bucket_n != remaining) {
+    if (bucket_n <= kFsCap) {
+      // B. compact the threshold bucket, then radix-select its low 20 bits in LDS
+      for (int base = wave * kWave * 4; base < ncand; base += kFsThreads * 4) {
+        uint32_t kv4[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        c[e] = hist[255 - 4 * lane - e];
-        own += c[e];
-      }
-      uint32_t incl = own;  // inclusive prefix over lanes (counts of higher digits)
+        for (int u = 0; u < 4; ++u) {
+          const int j = base + u * kWave + lane;
+          kv4[u] = j < ncand ? score_key(row[j]) : 0u;
+        }
 #pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t v = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += v;
-      }
-      const uint32_t excl = incl - own;
-      if (excl < (uint32_t)remaining && (uint32_t)remaining <= incl) {
-        uint32_t cum = excl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (cum + c[e] >= (uint32_t)remaining) {
-            bc_digit = 255u - 4u * lane - e;
-            bc_remaining = remaining - (int)cum;
-            bc_count = (int)c[e];
-            break;
-          }
-          cum += c[e];
+        for (int u = 0; u < 4; ++u) {
+          const int j = base + u * kWave + lane;
+          const bool in = j < ncand && (kv4[u] & pmask) == prefix;
+          const uint64_t m = __ballot(in);
+          int off = 0;
+          if (lane == 0 && m) off = atomicAdd(&list_n, __popcll(m));
+          off = __builtin_amdgcn_readfirstlane(off);
+          if (in) lkey[off + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (kWave - lane))))] = kv4[u];
         }
       }
+      __syncthreads();
+      const int cnt = list_n;
+      const int shifts[2] = {8, 0};
+      const uint32_t widths[2] = {0xfffu, 0xffu};
+      for (int ps = 0; ps < 2; ++ps) {
+        const int sh = shifts[ps];
+        const int nb = (int)widths[ps] + 1;
+        for (int t = tid; t < nb; t += kFsThreads) hist[t] = 0u;
+        __syncthreads();
+        for (int i = tid; i < cnt; i += kFsThreads) {
+          const uint32_t kk = lkey[i];
+          if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> sh) & widths[ps]], 1u);
+        }
+        __syncthreads();
+        find_rank_bucket(hist, nb, remaining, wsum, res);
+        prefix |= (uint32_t)res[0] << sh;
+        pmask |= widths[ps] << sh;
+        remaining = res[1];
+        if (res[2] == remaining) break;  // the whole bucket is kept
+      }
+    } else {
+      // Large tie-heavy bucket: radix passes over the row for the low 20 bits.
+      const int shifts[3] = {12, 4, 0};
+      const uint32_t widths[3] = {0xffu, 0xffu, 0xfu};
+      for (int ps = 0; ps < 3; ++ps) {
+        const int sh = shifts[ps];
+        const int nb = (int)widths[ps] + 1;
+        for (int t = tid; t < nb; t += kFsThreads) hist[t] = 0u;
+        __syncthreads();
+        for (int base = wave * kWave * 4; base < ncand; base += kFsThreads * 4) {
+          uint32_t kv4[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int j = base + u * kWave + lane;
+            kv4[u] = j < ncand ? score_key(row[j]) : 0u;
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int j = base + u * kWave + lane;
+            hist_add(hist, j < ncand && (kv4[u] & pmask) == prefix, (kv4[u] >> sh) & widths[ps], lane);
+          }
+        }
+        __syncthreads();
+        find_rank_bucket(hist, nb, remaining, wsum, res);
+        prefix |= (uint32_t)res[0] << sh;
+        pmask |= widths[ps] << sh;
+        remaining = res[1];
+        if (res[2] == remaining) break;
+      }
     }
-    __syncthreads();
-    prefix |= bc_digit << shift;
-    pmask |= 255u << shift;
-    remaining = bc_remaining;
-    const bool whole_bucket = bc_count == remaining;
-    __syncthreads();
-    if (whole_bucket) break;  // every key of the bucket is kept: lower digits decide nothing
   }
-  // Keys are compared on the resolved prefix bits: above the prefix is kept,
-  // equal to it is kept in position order while fewer than need_eq precede.
   const uint32_t T = prefix;
   const int need_eq = remaining;
 
-  // Ordered compaction. Each wave owns one contiguous segment of positions:
-  // pass A counts keys above T and equal to T per segment, one barrier
-  // publishes the counts, pass B writes the kept positions in order.
+  // C. ordered output on masked keys, one contiguous segment per wave
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  const int seg = ceil_div(ceil_div(ncand, kSelWaves), kWave) * kWave;
+  const int seg = ceil_div(ceil_div(ncand, kFsWaves), kWave) * kWave;
   const int s0 = wave * seg, s1 = min(ncand, s0 + seg);
   int cgt = 0, ceq = 0;
-  for (int base = s0; base < s1; base += kWave) {
-    const int j = base + lane;
-    const bool valid = j < s1;
-    const uint32_t kk = valid ? (in_lds ? keys[j] : score_key(row[j])) : 0u;
-    cgt += __popcll(__ballot(valid && (kk & pmask) > T));
-    ceq += __popcll(__ballot(valid && (kk & pmask) == T));
+  for (int base = s0; base < s1; base += 4 * kWave) {
+    uint32_t kv4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = base + u * kWave + lane;
+      kv4[u] = j < s1 ? (score_key(row[j]) & pmask) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool valid = base + u * kWave + lane < s1;
+      cgt += __popcll(__ballot(valid && kv4[u] > T));
+      ceq += __popcll(__ballot(valid && kv4[u] == T));
+    }
   }
   if (lane == 0) {
     wave_cnt[0][wave] = cgt;
@@ -172,34 +252,35 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     sel_run += wave_cnt[0][w] + taken;
     eq_run += e;
   }
-  for (int base = s0; base < s1; base += kWave) {
-    const int j = base + lane;
-    const bool valid = j < s1;
-    const uint32_t kk = valid ? (in_lds ? keys[j] : score_key(row[j])) : 0u;
-    const bool eq = valid && (kk & pmask) == T;
-    const uint64_t beq = __ballot(eq);
-    const bool sel = (valid && (kk & pmask) > T) || (eq && eq_run + __popcll(beq & lt_mask) < need_eq);
-    const uint64_t bsel = __ballot(sel);
-    const int pos = sel_run + __popcll(bsel & lt_mask);
-    if (sel && pos < ntop) out[pos] = j;
-    eq_run += __popcll(beq);
-    sel_run += __popcll(bsel);
+  for (int base = s0; base < s1; base += 4 * kWave) {
+    uint32_t kv4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = base + u * kWave + lane;
+      kv4[u] = j < s1 ? (score_key(row[j]) & pmask) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = base + u * kWave + lane;
+      const bool valid = j < s1;
+      const bool eq = valid && kv4[u] == T;
+      const uint64_t beq = __ballot(eq);
+      const bool sel = (valid && kv4[u] > T) || (eq && eq_run + __popcll(beq & lt_mask) < need_eq);
+      const uint64_t bsel = __ballot(sel);
+      const int pos = sel_run + __popcll(bsel & lt_mask);
+      if (sel && pos < ntop) out[pos] = j;
+      eq_run += __popcll(beq);
+      sel_run += __popcll(bsel);
+    }
   }
 }
-
-int select_lds_keys(int max_ncand) { return max_ncand < kSelLdsKeysMax ? max_ncand : kSelLdsKeysMax; }
 
 hipError_t launch_select(const float* scores, int stride, const int* ctx_len, int B, int Hkv,
                          int max_ctx_len, int s_num, int s_den, int window, int* idx, int nsel_cap,
                          int* n_sel, hipStream_t stream) {
-  const int lds_keys = select_lds_keys(max_ctx_len);
-  const size_t lds = (size_t)lds_keys * sizeof(uint32_t);
-  hipError_t e = hipFuncSetAttribute((const void*)select_kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     kSelLdsKeysMax * (int)sizeof(uint32_t));
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(select_kernel, dim3(Hkv, B), dim3(kSelThreads), lds, stream, scores, stride,
-                     ctx_len, Hkv, s_num, s_den, window, idx, nsel_cap, n_sel, lds_keys);
+  (void)max_ctx_len;
+  hipLaunchKernelGGL(select_stream_kernel, dim3(Hkv, B), dim3(kFsThreads), 0, stream, scores, stride,
+                     ctx_len, Hkv, s_num, s_den, window, idx, nsel_cap, n_sel);
   return hipGetLastError();
 }
 

@@ -57,8 +57,8 @@ __device__ __forceinline__ uint32_t u4_word(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-template <int NT>
-__global__ __launch_bounds__(kVerThreads, NT <= 2 ? 2 : 1) void verify_mfma_kernel(
+template <int NT, bool PF>
+__global__ __launch_bounds__(kVerThreads, (NT <= 2 && !PF) ? 2 : 1) void verify_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
     const int* __restrict__ bt, int max_pages, int pair0, int npairs_b, int Hkv, int G,
     const int* __restrict__ seq_len, int k, float scale_log2, int chunk, int nsplit, int ntile_cap,
@@ -124,21 +124,20 @@ __global__ __launch_bounds__(kVerThreads, NT <= 2 ? 2 : 1) void verify_mfma_kern
   uint16_t* my_vt = vt[wave];
   const int nsub = ceil_div(c1 - c0, kSub);
 
-  for (int st = wave; st < nsub; st += kVerWaves) {
+  struct Sub {
+    bf16x8_t kf[2][4];  // K rows as A fragments: lane (n16 = position in the 16-row tile, g4 = k group)
+    uint4 vraw[2][4];   // V rows for the LDS transpose: task = (4 positions a, 8-wide d chunk c)
+  };
+  auto load_sub = [&](int st, Sub& d) {
     const int pos0 = c0 + st * kSub;
     const int page_a = pages_sh[2 * st];
     const int page_b = (pos0 + 16 < S) ? pages_sh[2 * st + 1] : page_a;
-
-    // K rows as A fragments: lane (n16 = position in the 16-row tile, g4 = k group)
-    bf16x8_t kf[2][4];
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
       const bf16_t* kb = kp + (((size_t)(pt ? page_b : page_a) * Hkv + kv) * kPage + n16) * D + g4 * 8;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) kf[pt][kk] = *reinterpret_cast<const bf16x8_t*>(kb + kk * 32);
+      for (int kk = 0; kk < 4; ++kk) d.kf[pt][kk] = *reinterpret_cast<const bf16x8_t*>(kb + kk * 32);
     }
-    // V rows for the LDS transpose: task = (group of 4 positions a, 8-wide d chunk c)
-    uint4 vraw[2][4];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int task = lane + 64 * tt;
@@ -146,8 +145,20 @@ __global__ __launch_bounds__(kVerThreads, NT <= 2 ? 2 : 1) void verify_mfma_kern
       const int page = a < 4 ? page_a : page_b;
       const bf16_t* vb = vp + (((size_t)page * Hkv + kv) * kPage + (a & 3) * 4) * D + c * 8;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) vraw[tt][v] = *reinterpret_cast<const uint4*>(vb + v * D);
+      for (int v = 0; v < 4; ++v) d.vraw[tt][v] = *reinterpret_cast<const uint4*>(vb + v * D);
     }
+  };
+
+  Sub cur, nxt;
+  if (wave < nsub) load_sub(wave, cur);
+  for (int st = wave; st < nsub; st += kVerWaves) {
+    const int pos0 = c0 + st * kSub;
+    if (PF) {
+      // the next subtile's loads are in flight while this one is computed
+      if (st + kVerWaves < nsub) load_sub(st + kVerWaves, nxt);
+    }
+    const auto& kf = cur.kf;
+    const auto& vraw = cur.vraw;
 
     // S^T = K Q^T: s[pt][nt][v] is position pos0 + pt*16 + 4*g4 + v, row nt*16 + n16
     f32x4_t s[2][NT];
@@ -241,6 +252,11 @@ __global__ __launch_bounds__(kVerThreads, NT <= 2 ? 2 : 1) void verify_mfma_kern
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfrag, pf[nt], oacc[nt][dt], 0, 0, 0);
+    }
+    if (PF) {
+      cur = nxt;
+    } else if (st + kVerWaves < nsub) {
+      load_sub(st + kVerWaves, cur);
     }
   }
 
@@ -412,7 +428,7 @@ __global__ __launch_bounds__(kVerThreads) void verify_generic_kernel(
 // the remaining blocks each normalise kFinTiles tiles of score partials.
 // Every block first merges the per-split (max, sum) of all rows, in split
 // order, so every value is computed the same way by every block.
-constexpr int kFinTiles = 32;  // score tiles (of 32 positions) per finalize block
+constexpr int kFinTiles = kVerThreads / (kSub / 4);  // score tiles per finalize block (4 positions per thread)
 
 template <typename VT, int D>
 __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
@@ -420,9 +436,8 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
     const float* __restrict__ sc_max, const int* __restrict__ seq_len, int k, int Hkv, int G, int chunk,
     int nsplit, int ntile_cap, int RP, int nblk_o, int pair0, float* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ scores, int score_stride) {
-  constexpr int kTilesPerPass = kVerThreads / kSub;
   __shared__ float mrow[64], lrow[64], l2row[64];
-  __shared__ float wt[kTilesPerPass][64];
+  __shared__ float wt[kFinTiles][64];
   const int lp = blockIdx.y, pair = pair0 + lp, tid = threadIdx.x;
   const int b = pair / Hkv, kv = pair % Hkv;
   const int S = seq_len[b];
@@ -476,21 +491,30 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
   }
   const int ntiles = ceil_div(S, kSub);
   const int tile_end = min(ntiles, tile_beg + kFinTiles);
-  const int tl = tid / kSub, j = tid % kSub;
-  for (int t0 = tile_beg; t0 < tile_end; t0 += kTilesPerPass) {
-    __syncthreads();
-    for (int e = tid; e < kTilesPerPass * R; e += kVerThreads) {
-      const int et = e / R, r = e % R, tile = t0 + et;
-      wt[et][r] = tile < tile_end ? exp2f_fast(sc_max[(bkv * ntile_cap + tile) * R + r] - l2row[r]) : 0.f;
+  // weights of every (tile, row) of this block, then 4 positions per thread
+  for (int e = tid; e < kFinTiles * R; e += kVerThreads) {
+    const int et = e / R, r = e % R, tile = tile_beg + et;
+    wt[et][r] = tile < tile_end ? exp2f_fast(sc_max[(bkv * ntile_cap + tile) * R + r] - l2row[r]) : 0.f;
+  }
+  __syncthreads();
+  const int tl = tid / (kSub / 4), j4 = (tid % (kSub / 4)) * 4;
+  const int tile = tile_beg + tl, pos = tile * kSub + j4;
+  if (tile < tile_end && pos < S) {
+    const VT* vals = sc_val + (bkv * ntile_cap + tile) * R * kSub + j4;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int r = 0; r < R; ++r) {
+      const float w = wt[tl][r];
+      const VT* v = vals + r * kSub;
+      a0 = fmaf(w, (float)v[0], a0);
+      a1 = fmaf(w, (float)v[1], a1);
+      a2 = fmaf(w, (float)v[2], a2);
+      a3 = fmaf(w, (float)v[3], a3);
     }
-    __syncthreads();
-    const int tile = t0 + tl, pos = tile * kSub + j;
-    if (tile < tile_end && pos < S) {
-      const VT* vals = sc_val + (bkv * ntile_cap + tile) * R * kSub + j;
-      float acc = 0.f;
-      for (int r = 0; r < R; ++r) acc = fmaf(wt[tl][r], (float)vals[r * kSub], acc);
-      scores[gkv * score_stride + pos] = acc;
-    }
+    float* dst = scores + gkv * score_stride + pos;
+    dst[0] = a0;
+    if (pos + 1 < S) dst[1] = a1;
+    if (pos + 2 < S) dst[2] = a2;
+    if (pos + 3 < S) dst[3] = a3;
   }
 }
 
@@ -542,7 +566,7 @@ static void launch_mfma(const VerifyPlan& p, const void* q, const void* kp, cons
                         const int* bt, int max_pages, int Hkv, const int* seq_len, int pair0,
                         int npairs_b, int k, float sl2, int with_scores, char* ws, hipStream_t stream) {
   const int nblocks = ceil_div(npairs_b, 8) * 8 * p.nsplit;
-  hipLaunchKernelGGL((verify_mfma_kernel<NT>), dim3(nblocks), dim3(kVerThreads), 0, stream,
+  hipLaunchKernelGGL((verify_mfma_kernel<NT, kVerPrefetch>), dim3(nblocks), dim3(kVerThreads), 0, stream,
                      (const bf16_t*)q, (const bf16_t*)kp, (const bf16_t*)vp, bt, max_pages, pair0,
                      npairs_b, Hkv, p.G, seq_len, k, sl2, p.chunk, p.nsplit, p.ntile_cap, with_scores,
                      (float*)(ws + p.off_part_o), (float*)(ws + p.off_part_ml),

@@ -64,10 +64,12 @@ def test_select_matches_oracle(key, cid, ov):
     _check_select(cfg, batch, batch.scores, idx, n_sel, units)
 
 
-def test_select_edge_cases():
+@pytest.mark.parametrize("long_row", [40000, 24000])
+def test_select_edge_cases(long_row):
+    # a 40000-position row takes the streaming kernel, 24000 the register-resident one
     cfg = get_config(2, B=7, Hkv=2)
     rng = np.random.default_rng(7)
-    L = np.array([1, 5, 64, 65, 200, 40000, 1000], dtype=np.int32)  # window 64; 40000 > LDS key capacity
+    L = np.array([1, 5, 64, 65, 200, long_row, 1000], dtype=np.int32)  # window 64
     stride = int(L.max())
     sc = np.zeros((7, 2, stride), np.float32)
     sc[0] = 0.0
@@ -77,9 +79,10 @@ def test_select_edge_cases():
     sc[3, 1, :65] = -np.inf
     sc[4, :, :200] = rng.integers(0, 4, (2, 200)).astype(np.float32)  # heavy ties
     sc[4, 1, 7] = -0.0
-    sc[5, :, :40000] = rng.random((2, 40000)).astype(np.float32)
+    sc[5, :, :long_row] = rng.random((2, long_row)).astype(np.float32)
     sc[5, 0, 100:200] = 0.5  # ties in the long row
     sc[6, :, :1000] = (rng.integers(0, 2, (2, 1000)) * 2 - 1) * np.float32(1e-38)  # denormal-range signs
+    sc[5, 1, :3000] = 0.25  # a tie bucket larger than the compaction capacity
     dev = torch.device("cuda")
     for s_num, s_den in [(1, 20), (1, 2), (1, 1), (0, 1), (7, 9)]:
         nc = s3r.budget(stride, s_num, s_den, cfg.window)
