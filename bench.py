@@ -275,7 +275,7 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "s3r_verify_attn (verify_mfma_kernel + verify_combine_kernel + verify_scores_kernel)",
+            "kernel": "s3r_verify_attn: verify_mfma_kernel (split pass) + verify_finalize_kernel (split merge, scores)",
             "bound": "hbm",
             "achieved": round(ver_gbs, 1),
             "peak": HBM_PEAK_GBS,

@@ -190,6 +190,9 @@ def test_verify_c1_f32():
     ("c5k2", 5, {"B": 2, "k": 2, "lengths": ("uniform", 900, 3000)}),   # 12 rows
     ("c5k8", 5, {"B": 2, "k": 8, "lengths": ("uniform", 900, 3000)}),   # 36 rows (three row tiles)
     ("c3k15", 3, {"B": 2, "k": 15, "lengths": ("uniform", 100, 2100)}),  # 64 rows (four row tiles)
+    # longer contexts: 31-33 splits of 2048 positions per (sequence, KV head)
+    ("c3long", 3, {"B": 2, "lengths": ("uniform", 62000, 66000)}),
+    ("c3k15long", 3, {"B": 1, "k": 15, "lengths": ("uniform", 40000, 41000)}),
 ])
 def test_verify_bf16(key, cid, ov):
     cfg, batch, t = _batch(key, cid, parts=("kv", "q"), **ov)
@@ -300,6 +303,17 @@ def test_determinism_and_poisoned_workspace():
         assert np.array_equal(results[0][2][b, :, :S], results[1][2][b, :, :S])
         assert np.isfinite(results[0][2][b, :, :S]).all()
     assert np.isfinite(results[0][0]).all()
+
+
+@pytest.mark.parametrize("key,ov", [("c2v", {"B": 4}), ("c3long", {"B": 2, "lengths": ("uniform", 62000, 66000)})])
+def test_verify_without_scores_matches(key, ov):
+    # the output rows and lse do not depend on whether scores are requested
+    cfg, batch, t = _batch(key, 2 if key == "c2v" else 3, parts=("kv", "q"), **ov)
+    o1, l1, _ = run_verify(cfg, batch, t)
+    o2, l2, s2 = run_verify(cfg, batch, t, want_scores=False)
+    torch.cuda.synchronize()
+    assert s2 is None
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 def test_invalid_arguments_raise():
