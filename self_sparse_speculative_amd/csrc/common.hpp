@@ -40,6 +40,17 @@ __device__ __forceinline__ float fmax_nan_free(float a, float b) { return a > b 
 // Exponent base 2 that returns 0 for -inf inputs (v_exp_f32 already does).
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lanes of one wave that hand data to each other through LDS (a transpose)
+// need this between the writes and the reads: without it the compiler may,
+// reasoning one lane at a time, reuse an earlier read of the same address in
+// lanes that did not write in between. Wave-scope fences emit no wait of
+// their own; LDS operations of one wave complete in order.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Ordered split of [0, n) into `parts` contiguous chunks of `chunk` elements.
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 

@@ -377,6 +377,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
     u32x4_t pw = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
                   pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])};
     const dbf16x8_t pf = __builtin_bit_cast(dbf16x8_t, pw);
+    wave_lds_sync();  // the previous subtile's reads of the buffer precede these writes
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int task = lane + 64 * tt;
@@ -391,6 +392,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
         *reinterpret_cast<uint2*>(my_vt + (c * 8 + e) * kDvtStride + slot) = make_uint2(lo, hi);
       }
     }
+    wave_lds_sync();  // each lane reads rows written by other lanes
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const dbf16x8_t vfrag = *reinterpret_cast<const dbf16x8_t*>(my_vt + (dt * 16 + n16) * kDvtStride + g4 * 8);

@@ -231,6 +231,7 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 && !PF) ? 2 : 1) void verify_
     }
 
     // V^T into LDS: row d holds 32 slots; slot g*8 + pt*4 + v <- position pt*16 + 4g + v
+    wave_lds_sync();  // the previous subtile's reads of the buffer precede these writes
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int task = lane + 64 * tt;
@@ -245,6 +246,7 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 && !PF) ? 2 : 1) void verify_
         *reinterpret_cast<uint2*>(my_vt + (c * 8 + e) * kVtStride + slot) = make_uint2(lo, hi);
       }
     }
+    wave_lds_sync();  // each lane reads rows written by other lanes
     // O^T += V^T P^T
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
