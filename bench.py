@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--sigma", type=float, default=None)
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-seqs", type=int, default=24, help="sequences in the oracle's timed CPU sample")
+    ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences in the oracle's timed CPU sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline (profiling runs)")
     ap.add_argument("--copy-gib", type=float, default=2.0,
                     help="size of the device-to-device copy timed as the HBM reference (0 to skip)")
