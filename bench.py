@@ -1,7 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of one S3R round on one MI355X: select, k sparse draft steps,
 dense block verification (with next-round scores) and exact speculative
-sampling, all through the C ABI of libs3r.so on one stream.
+sampling, all through the C ABI of libs3r.so. The next round's scores are
+formed on a second stream while sampling runs (--serial-scores: one
+s3r_verify_attn call on the launch stream instead).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 
@@ -42,6 +44,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences in the oracle's timed CPU sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline (profiling runs)")
+    ap.add_argument("--serial-scores", action="store_true",
+                    help="one s3r_verify_attn call (scores on the launch stream) instead of the deferred pair")
     ap.add_argument("--copy-gib", type=float, default=2.0,
                     help="size of the device-to-device copy timed as the HBM reference (0 to skip)")
     return ap.parse_args()
@@ -72,15 +76,18 @@ def source_sha(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def load_traffic(kernel_src):
-    """Measured HBM bytes per verify launch from the committed counter summary, if it is current."""
+def load_traffic(kernel_src, key):
+    """Counter-measured HBM bytes per launch from the committed summary, if it is current.
+
+    key: "rows" (split pass + output merge, the deferred call) or "one_call" (s3r_verify_attn)."""
     path = os.path.join(ROOT, "profiles", "verify_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     if rec.get("source_sha") != source_sha(kernel_src):
         return None
-    return rec.get("bytes_per_launch")
+    per = rec.get("bytes_per_launch")
+    return per.get(key) if isinstance(per, dict) else None
 
 
 def cpu_baseline(cfg, nseq, seed):
@@ -165,7 +172,14 @@ def main():
     n_out = torch.empty((B,), dtype=torch.int32, device="cuda")
     accepted = torch.empty((B, k), dtype=torch.int8, device="cuda")
 
-    def step(ev=None):
+    # The next round's scores are only read by the next select, so they are
+    # formed on a side stream (default priority) while sampling runs; the
+    # round ends when both streams are done.
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    rows_done = torch.cuda.Event()
+
+    def step(ev=None, sev=None):
         if ev is not None:
             ev[0].record()
         s3r.select(scores, t["ctx_len"], max_ctx, cfg.s_num, cfg.s_den, cfg.window, idx=idx, n_sel=n_sel)
@@ -176,13 +190,28 @@ def main():
                                    out=dout, lse=dlse, ws=ws)
         if ev is not None:
             ev[2].record()
-        s3r.verify_attn(t["q_verify"], t["kv"], t["seq_len"], k, scale, max_seq, out=vout, lse=vlse, scores=scores,
-                        ws=ws)
-        if ev is not None:
-            ev[3].record()
+        if args.serial_scores:
+            s3r.verify_attn(t["q_verify"], t["kv"], t["seq_len"], k, scale, max_seq, out=vout, lse=vlse,
+                            scores=scores, ws=ws)
+            if ev is not None:
+                ev[3].record()
+        else:
+            s3r.verify_attn_deferred(t["q_verify"], t["kv"], t["seq_len"], k, scale, max_seq, out=vout, lse=vlse,
+                                     ws=ws)
+            if ev is not None:
+                ev[3].record()
+            rows_done.record(main)
+            side.wait_event(rows_done)
+            if sev is not None:
+                sev[0].record(side)
+            s3r.verify_scores(t["kv"], t["seq_len"], B, k, Hq, D, max_seq, scores=scores, ws=ws, stream=side)
+            if sev is not None:
+                sev[1].record(side)
         s3r.spec_sample(t["zt"], t["zd"], t["d"], t["u"], T, tokens=tokens, n_out=n_out, accepted=accepted, ws=ws)
         if ev is not None:
             ev[4].record()
+        if not args.serial_scores:
+            main.wait_stream(side)  # the next select reads the scores
 
     for _ in range(args.warmup):
         step()
@@ -195,23 +224,28 @@ def main():
     nsel_np = n_sel.cpu().numpy()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        step(evs[i])
+        step(evs[i], sevs[i])
     stop.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(stop) / args.steps
     phase = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])  # ms
     t_sel, t_draft, t_ver, t_smp = phase.mean(axis=0)
+    t_scores = None if args.serial_scores else float(np.mean([e[0].elapsed_time(e[1]) for e in sevs]))
 
     # algorithmic bytes per launch (see the design doc for the per-unit figures)
     e = 2 if cfg.dtype == "bf16" else 4
     L = batch.ctx_len.astype(np.int64)
     S = batch.seq_len.astype(np.int64)
     kv_row = 2 * D * e  # one K row + one V row
-    ver_bytes = int(Hkv * S.sum() * (kv_row + 4) + B * (k + 1) * Hq * (D * e + D * 4 + 4))
+    # the verify call on the launch stream: K and V rows, q, output rows and lse; in
+    # the one-call form also the scores it writes
+    ver_bytes = int(Hkv * S.sum() * (kv_row + (4 if args.serial_scores else 0)) + B * (k + 1) * Hq * (D * e + D * 4 + 4))
+    score_bytes = int(Hkv * S.sum() * 4)
     draft_bytes = int(sum(Hkv * (nsel_np.astype(np.int64) + j).sum() * (kv_row + 4) for j in range(1, k + 1))
                       + k * B * Hq * (D * e + D * 4 + 4))
     sel_bytes = int(Hkv * L.sum() * 4 + Hkv * nsel_np.astype(np.int64).sum() * 4)
@@ -221,7 +255,8 @@ def main():
     ver_gbs = ver_bytes / (t_ver * 1e-3) / 1e9
     from self_sparse_speculative_amd import s3r as s3r_mod  # noqa: F401
 
-    traffic = load_traffic(os.path.join(ROOT, "self_sparse_speculative_amd", "csrc", "verify.hip"))
+    traffic = load_traffic(os.path.join(ROOT, "self_sparse_speculative_amd", "csrc", "verify.hip"),
+                           "one_call" if args.serial_scores else "rows")
     value = verified / (ms_step * 1e-3)
     copy_gbs = read_gbs = None
     if args.copy_gib > 0:
@@ -275,7 +310,9 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "s3r_verify_attn: verify_mfma_kernel (split pass) + verify_finalize_kernel (split merge, scores)",
+            "kernel": ("s3r_verify_attn: verify_mfma_kernel (split pass) + verify_finalize_kernel (merge, scores)"
+                       if args.serial_scores else
+                       "s3r_verify_attn_deferred: verify_mfma_kernel (split pass) + verify_finalize_kernel (output merge)"),
             "bound": "hbm",
             "achieved": round(ver_gbs, 1),
             "peak": HBM_PEAK_GBS,
@@ -290,17 +327,20 @@ def main():
             "verified_tokens_per_round": verified,
             "tokens_per_sequence": round(verified / B, 4),
             "ms": {"select": round(float(t_sel), 4), "draft_k_steps": round(float(t_draft), 4),
-                   "verify": round(float(t_ver), 4), "spec_sample": round(float(t_smp), 4)},
+                   "verify": round(float(t_ver), 4), "spec_sample": round(float(t_smp), 4),
+                   "verify_scores_side_stream": None if t_scores is None else round(t_scores, 4)},
             "GBs": {"select": round(sel_bytes / (t_sel * 1e-3) / 1e9, 1),
                     "draft": round(draft_bytes / (t_draft * 1e-3) / 1e9, 1),
                     "verify": round(ver_gbs, 1),
-                    "spec_sample": round(smp_bytes / (t_smp * 1e-3) / 1e9, 1)},
+                    "spec_sample": round(smp_bytes / (t_smp * 1e-3) / 1e9, 1),
+                    "verify_scores_side_stream": None if t_scores is None else round(score_bytes / (t_scores * 1e-3) / 1e9, 1)},
             "draft_plus_verify_kv_GBs": round(kv_bytes / (kv_ms * 1e-3) / 1e9, 1),
             "draft_plus_verify_frac_of_hbm_peak": round(kv_bytes / (kv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "device_copy_GBs": None if copy_gbs is None else round(copy_gbs, 1),
             "device_read_GBs": None if read_gbs is None else round(read_gbs, 1),
-            "round_algorithmic_bytes": kv_bytes + sel_bytes + smp_bytes,
-            "round_frac_of_hbm_peak": round((kv_bytes + sel_bytes + smp_bytes) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "round_algorithmic_bytes": kv_bytes + sel_bytes + smp_bytes + (0 if args.serial_scores else score_bytes),
+            "round_frac_of_hbm_peak": round((kv_bytes + sel_bytes + smp_bytes + (0 if args.serial_scores else score_bytes))
+                                            / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         },
     }
     print(json.dumps(res))

@@ -11,7 +11,9 @@
  *                           (called k times per round);
  *   s3r_verify_attn         dense attention of the k + 1 block queries over
  *                           the complete paged cache, causal inside the block;
- *                           also emits the next round's selector scores;
+ *                           also emits the next round's selector scores
+ *                           (or s3r_verify_attn_deferred now and
+ *                           s3r_verify_scores on another stream);
  *   s3r_spec_sample         exact speculative sampling: accept each draft with
  *                           probability min(1, p/q), else draw the correction
  *                           from the normalised residual max(0, p - q); a fully
@@ -197,6 +199,30 @@ s3r_status s3r_verify_attn(const void* q, const s3r_paged_kv* kv, const int32_t*
                            int32_t B, int32_t k, int32_t Hq, float scale, int32_t max_seq_len,
                            float* out, float* lse, float* scores, int32_t score_stride, void* ws,
                            size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The same verification in two calls, so that the scores, which only the
+ * next round's selection reads, can be formed on another stream while the
+ * output rows go on to sampling. [explainer], mechanism paragraph: the
+ * selector's scores come from the verifier's last attention pass, refreshed
+ * after every round.
+ *
+ * s3r_verify_attn_deferred writes out and lse exactly as s3r_verify_attn and
+ * leaves the score partials in ws. s3r_verify_scores then writes scores
+ * exactly as s3r_verify_attn would (bit for bit) from those partials; call it
+ * with the same kv description, seq_len, B, k, Hq, max_seq_len and ws, on
+ * any stream ordered after the deferred call (e.g. through an event), and
+ * before ws is used again. Arguments as for s3r_verify_attn; scores is
+ * required by s3r_verify_scores, which reads only the metadata of kv
+ * (num_kv_heads, head_dim, dtype, page_size, max_pages_per_seq).
+ */
+s3r_status s3r_verify_attn_deferred(const void* q, const s3r_paged_kv* kv, const int32_t* seq_len,
+                                    int32_t B, int32_t k, int32_t Hq, float scale, int32_t max_seq_len,
+                                    float* out, float* lse, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
+s3r_status s3r_verify_scores(const s3r_paged_kv* kv, const int32_t* seq_len, int32_t B, int32_t k,
+                             int32_t Hq, int32_t max_seq_len, float* scores, int32_t score_stride,
+                             const void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * s3r_spec_sample - exact speculative sampling with caller-supplied uniforms.

@@ -21,5 +21,7 @@ from .s3r import (  # noqa: F401
     spec_sample_workspace_bytes,
     status_string,
     verify_attn,
+    verify_attn_deferred,
+    verify_scores,
     verify_workspace_bytes,
 )

@@ -104,13 +104,12 @@ size_t s3r_verify_workspace_bytes(int32_t B, int32_t k, int32_t Hq, int32_t Hkv,
   return s3r::verify_plan(B, k, Hq, Hkv, head_dim, dtype, max_seq_len).bytes;
 }
 
-s3r_status s3r_verify_attn(const void* q, const s3r_paged_kv* kv, const int32_t* seq_len,
-                           int32_t B, int32_t k, int32_t Hq, float scale, int32_t max_seq_len,
-                           float* out, float* lse, float* scores, int32_t score_stride, void* ws,
-                           size_t ws_bytes, hipStream_t stream) {
-  if (!q || !kv_ok(kv) || !seq_len || !out) return S3R_ERR_INVALID_ARG;
+// Shared argument checks of the verification entry points.
+static s3r_status verify_check(const s3r_paged_kv* kv, const int32_t* seq_len, int32_t B, int32_t k,
+                               int32_t Hq, int32_t max_seq_len, float* scores, int32_t score_stride,
+                               void* ws, size_t ws_bytes) {
+  if (!kv_ok(kv) || !seq_len) return S3R_ERR_INVALID_ARG;
   if (B < 1 || B > 65535 || Hq < 1 || k < 0 || k > kMaxK || max_seq_len < k + 1) return S3R_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return S3R_ERR_INVALID_ARG;
   const int Hkv = kv->num_kv_heads;
   if (Hq % Hkv != 0 || Hkv > 65535) return S3R_ERR_INVALID_ARG;
   if ((long long)kv->max_pages_per_seq * kv->page_size < max_seq_len) return S3R_ERR_INVALID_ARG;
@@ -120,10 +119,43 @@ s3r_status s3r_verify_attn(const void* q, const s3r_paged_kv* kv, const int32_t*
   if ((k + 1) * (Hq / Hkv) > kMaxRows) return S3R_ERR_UNSUPPORTED;
   const size_t need = s3r::verify_plan(B, k, Hq, Hkv, kv->head_dim, kv->dtype, max_seq_len).bytes;
   if (ws_bytes < need || ws == nullptr) return S3R_ERR_WORKSPACE;
+  return S3R_OK;
+}
+
+s3r_status s3r_verify_attn(const void* q, const s3r_paged_kv* kv, const int32_t* seq_len,
+                           int32_t B, int32_t k, int32_t Hq, float scale, int32_t max_seq_len,
+                           float* out, float* lse, float* scores, int32_t score_stride, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  if (!q || !out || !isfinite(scale)) return S3R_ERR_INVALID_ARG;
+  const s3r_status st = verify_check(kv, seq_len, B, k, Hq, max_seq_len, scores, score_stride, ws, ws_bytes);
+  if (st != S3R_OK) return st;
   return from_hip(s3r::launch_verify(kv->dtype, kv->head_dim, q, kv->k_pages, kv->v_pages,
-                                     kv->block_table, kv->max_pages_per_seq, Hkv, seq_len, B, k,
-                                     Hq, scale, max_seq_len, out, lse, scores, score_stride, ws,
+                                     kv->block_table, kv->max_pages_per_seq, kv->num_kv_heads, seq_len,
+                                     B, k, Hq, scale, max_seq_len, out, lse, scores, score_stride, false,
+                                     ws, stream));
+}
+
+s3r_status s3r_verify_attn_deferred(const void* q, const s3r_paged_kv* kv, const int32_t* seq_len,
+                                    int32_t B, int32_t k, int32_t Hq, float scale, int32_t max_seq_len,
+                                    float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !out || !isfinite(scale)) return S3R_ERR_INVALID_ARG;
+  const s3r_status st = verify_check(kv, seq_len, B, k, Hq, max_seq_len, nullptr, 0, ws, ws_bytes);
+  if (st != S3R_OK) return st;
+  return from_hip(s3r::launch_verify(kv->dtype, kv->head_dim, q, kv->k_pages, kv->v_pages,
+                                     kv->block_table, kv->max_pages_per_seq, kv->num_kv_heads, seq_len,
+                                     B, k, Hq, scale, max_seq_len, out, lse, nullptr, 0, true, ws,
                                      stream));
+}
+
+s3r_status s3r_verify_scores(const s3r_paged_kv* kv, const int32_t* seq_len, int32_t B, int32_t k,
+                             int32_t Hq, int32_t max_seq_len, float* scores, int32_t score_stride,
+                             const void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!scores) return S3R_ERR_INVALID_ARG;
+  const s3r_status st = verify_check(kv, seq_len, B, k, Hq, max_seq_len, scores, score_stride,
+                                     const_cast<void*>(ws), ws_bytes);
+  if (st != S3R_OK) return st;
+  return from_hip(s3r::launch_verify_scores(kv->dtype, kv->head_dim, seq_len, B, k, Hq, kv->num_kv_heads,
+                                            max_seq_len, scores, score_stride, ws, stream));
 }
 
 size_t s3r_spec_sample_workspace_bytes(int32_t B, int32_t k, int32_t V) {

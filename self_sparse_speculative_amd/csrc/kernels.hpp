@@ -25,11 +25,6 @@ constexpr int kVerChunkMfma = S3R_VERIFY_CHUNK;  // context positions per verify
 constexpr bool kVerPrefetch = S3R_VERIFY_PREFETCH != 0;  // software-pipelined K/V loads in verify
 constexpr int kVerChunkGeneric = 256;  // context positions per verify split (generic path)
 constexpr int kSmpChunks = 64;         // vocabulary chunks of the final draw
-#ifndef S3R_VERIFY_BATCH_MB
-#define S3R_VERIFY_BATCH_MB 0
-#endif
-// Byte budget of the verify partials per batch of (sequence, KV head) pairs (0: one batch).
-constexpr size_t kVerBatchBytes = (size_t)S3R_VERIFY_BATCH_MB << 20;
 
 hipError_t launch_select(const float* scores, int stride, const int* ctx_len, int B, int Hkv,
                          int max_ctx_len, int s_num, int s_den, int window, int* idx, int nsel_cap,
@@ -44,15 +39,22 @@ hipError_t launch_sparse_decode(int dtype, int D, int G, const void* q, const vo
                                 float* lse, void* ws, hipStream_t stream);
 
 struct VerifyPlan {
-  int G, R, NT, RP, chunk, nsplit, ntile_cap, pairs_per_batch;
+  int G, R, NT, RP, chunk, nsplit, ntile_cap;
   bool mfma;
-  size_t off_part_o, off_part_ml, off_lse2, off_sc_max, off_sc_val, bytes;
+  size_t off_part_o, off_part_ml, off_sc_max, off_sc_val, bytes;
 };
 VerifyPlan verify_plan(int B, int k, int Hq, int Hkv, int D, int dtype, int max_seq_len);
+// Split pass + merge of the output rows. With scores != nullptr the scores
+// are written too; with defer_scores the score partials stay in ws for a
+// later launch_verify_scores (scores must then be nullptr).
 hipError_t launch_verify(int dtype, int D, const void* q, const void* kp, const void* vp,
                          const int* bt, int max_pages, int Hkv, const int* seq_len, int B, int k,
                          int Hq, float scale, int max_seq_len, float* out, float* lse,
-                         float* scores, int score_stride, void* ws, hipStream_t stream);
+                         float* scores, int score_stride, bool defer_scores, void* ws,
+                         hipStream_t stream);
+hipError_t launch_verify_scores(int dtype, int D, const int* seq_len, int B, int k, int Hq, int Hkv,
+                                int max_seq_len, float* scores, int score_stride, const void* ws,
+                                hipStream_t stream);
 
 size_t sample_workspace_bytes(int B, int k, int V);
 hipError_t launch_spec_sample(const float* zt, const float* zd, const int* dtok, const float* u,

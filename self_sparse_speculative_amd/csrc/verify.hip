@@ -60,7 +60,7 @@ __device__ __forceinline__ uint32_t u4_word(const uint4& v, int i) {
 template <int NT, bool PF>
 __global__ __launch_bounds__(kVerThreads, (NT <= 2 && !PF) ? 2 : 1) void verify_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
-    const int* __restrict__ bt, int max_pages, int pair0, int npairs_b, int Hkv, int G,
+    const int* __restrict__ bt, int max_pages, int npairs, int Hkv, int G,
     const int* __restrict__ seq_len, int k, float scale_log2, int chunk, int nsplit, int ntile_cap,
     int with_scores, float* __restrict__ part_o, float* __restrict__ part_ml,
     _Float16* __restrict__ sc_val, float* __restrict__ sc_max) {
@@ -73,9 +73,8 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 && !PF) ? 2 : 1) void verify_
   // Workgroups are dispatched round-robin over the XCDs; consecutive splits of
   // one (sequence, KV head) pair go to the same XCD.
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-  const int lp = (local / nsplit) * 8 + xcd, split = local % nsplit;  // pair within the batch
-  if (lp >= npairs_b) return;
-  const int pair = pair0 + lp;
+  const int pair = (local / nsplit) * 8 + xcd, split = local % nsplit;
+  if (pair >= npairs) return;
   const int b = pair / Hkv, kv = pair % Hkv;
   const int S = seq_len[b];
   const int c0 = split * chunk;
@@ -86,7 +85,7 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 && !PF) ? 2 : 1) void verify_
   const int Hq = Hkv * G;
   const int R = (k + 1) * G;
   const int P0 = S - (k + 1);
-  const size_t bkv = (size_t)lp;  // partial records are per pair of the batch
+  const size_t bkv = (size_t)pair;
 
   bf16x8_t qf[NT][4];
   int row_last[NT];
@@ -326,7 +325,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kVerThreads) void verify_generic_kernel(
     const T* __restrict__ q, const T* __restrict__ kp, const T* __restrict__ vp,
     const int* __restrict__ bt, int max_pages, int Hkv, int G, const int* __restrict__ seq_len,
-    int k, float scale_log2, int chunk, int nsplit, int ntile_cap, int RP, int with_scores, int pair0,
+    int k, float scale_log2, int chunk, int nsplit, int ntile_cap, int RP, int with_scores,
     float* __restrict__ part_o, float* __restrict__ part_ml, float* __restrict__ sc_val,
     float* __restrict__ sc_max) {
   constexpr int EPL = D / 16;
@@ -334,7 +333,7 @@ __global__ __launch_bounds__(kVerThreads) void verify_generic_kernel(
   __shared__ float red[kVerWaves][D + 2];
   __shared__ float bc;
 
-  const int split = blockIdx.x, lp = blockIdx.y, pair = pair0 + lp;
+  const int split = blockIdx.x, pair = blockIdx.y;
   const int b = pair / Hkv, kv = pair % Hkv;
   const int S = seq_len[b];
   const int c0 = split * chunk;
@@ -343,7 +342,7 @@ __global__ __launch_bounds__(kVerThreads) void verify_generic_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, sub = lane & 15;
   const int stream = wave * 4 + (lane >> 4);
   const int Hq = Hkv * G, R = (k + 1) * G, P0 = S - (k + 1);
-  const size_t bkv = (size_t)lp;  // partial records are per pair of the batch
+  const size_t bkv = (size_t)pair;
   const int* bt_row = bt + (size_t)b * max_pages;
   const size_t head_stride = (size_t)kPage * D;
 
@@ -436,20 +435,19 @@ template <typename VT, int D>
 __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, const VT* __restrict__ sc_val,
     const float* __restrict__ sc_max, const int* __restrict__ seq_len, int k, int Hkv, int G, int chunk,
-    int nsplit, int ntile_cap, int RP, int nblk_o, int pair0, float* __restrict__ out,
+    int nsplit, int ntile_cap, int RP, int nblk_o, int x0, float* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ scores, int score_stride) {
   __shared__ float mrow[64], lrow[64], l2row[64];
   __shared__ float wt[kFinTiles][64];
-  const int lp = blockIdx.y, pair = pair0 + lp, tid = threadIdx.x;
+  const int pair = blockIdx.y, tid = threadIdx.x;
   const int b = pair / Hkv, kv = pair % Hkv;
   const int S = seq_len[b];
-  const int x = blockIdx.x;
+  const int x = x0 + (int)blockIdx.x;
   const int tile_beg = (x - nblk_o) * kFinTiles;
   if (x >= nblk_o && tile_beg * kSub >= S) return;
   const int used = min(nsplit, ceil_div(S, chunk));
   const int R = (k + 1) * G, Hq = Hkv * G;
-  const size_t bkv = (size_t)lp;      // partial records of the batch
-  const size_t gkv = (size_t)pair;   // output rows
+  const size_t bkv = (size_t)pair;
   // Row statistics: 4 lanes per row, each over every 4th split, then a fixed
   // butterfly over the 4 lanes (same order in every block).
   for (int r0 = 0; r0 < R; r0 += kVerThreads / 4) {
@@ -512,7 +510,7 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
       a2 = fmaf(w, (float)v[2], a2);
       a3 = fmaf(w, (float)v[3], a3);
     }
-    float* dst = scores + gkv * score_stride + pos;
+    float* dst = scores + bkv * score_stride + pos;
     dst[0] = a0;
     if (pos + 1 < S) dst[1] = a1;
     if (pos + 2 < S) dst[2] = a2;
@@ -534,27 +532,13 @@ VerifyPlan verify_plan(int B, int k, int Hq, int Hkv, int D, int dtype, int max_
   p.chunk = p.mfma ? kVerChunkMfma : kVerChunkGeneric;
   p.nsplit = ceil_div(max_seq_len, p.chunk);
   p.ntile_cap = ceil_div(max_seq_len, kSub);
-  // Partial records per (sequence, KV head) pair; pairs are processed in
-  // batches whose partials fit a byte budget (the partial buffer is reused
-  // by every batch).
-  const size_t per_pair = (size_t)p.nsplit * p.RP * D * sizeof(float) +
-                          (size_t)p.nsplit * p.RP * 2 * sizeof(float) +
-                          (size_t)p.ntile_cap * p.R * sizeof(float) +
-                          (size_t)p.ntile_cap * p.R * kSub * (p.mfma ? sizeof(_Float16) : sizeof(float));
-  const int npairs = B * Hkv;
-  int ppb = npairs;
-  if (kVerBatchBytes > 0) {
-    ppb = (int)(kVerBatchBytes / per_pair) / 8 * 8;
-    ppb = ppb < 8 ? 8 : (ppb > npairs ? npairs : ppb);
-  }
-  p.pairs_per_batch = ppb;
-  const size_t nbkv = (size_t)ppb;
+  // Partial records per (sequence, KV head) pair.
+  const size_t nbkv = (size_t)B * Hkv;
   size_t off = 0;
   p.off_part_o = off;
   off = align256(off + nbkv * p.nsplit * p.RP * D * sizeof(float));
   p.off_part_ml = off;
   off = align256(off + nbkv * p.nsplit * p.RP * 2 * sizeof(float));
-  p.off_lse2 = off;
   p.off_sc_max = off;
   off = align256(off + nbkv * p.ntile_cap * p.R * sizeof(float));
   p.off_sc_val = off;
@@ -565,75 +549,90 @@ VerifyPlan verify_plan(int B, int k, int Hq, int Hkv, int D, int dtype, int max_
 
 template <int NT>
 static void launch_mfma(const VerifyPlan& p, const void* q, const void* kp, const void* vp,
-                        const int* bt, int max_pages, int Hkv, const int* seq_len, int pair0,
-                        int npairs_b, int k, float sl2, int with_scores, char* ws, hipStream_t stream) {
-  const int nblocks = ceil_div(npairs_b, 8) * 8 * p.nsplit;
+                        const int* bt, int max_pages, int Hkv, const int* seq_len, int npairs, int k,
+                        float sl2, int with_scores, char* ws, hipStream_t stream) {
+  const int nblocks = ceil_div(npairs, 8) * 8 * p.nsplit;
   hipLaunchKernelGGL((verify_mfma_kernel<NT, kVerPrefetch>), dim3(nblocks), dim3(kVerThreads), 0, stream,
-                     (const bf16_t*)q, (const bf16_t*)kp, (const bf16_t*)vp, bt, max_pages, pair0,
-                     npairs_b, Hkv, p.G, seq_len, k, sl2, p.chunk, p.nsplit, p.ntile_cap, with_scores,
+                     (const bf16_t*)q, (const bf16_t*)kp, (const bf16_t*)vp, bt, max_pages, npairs, Hkv,
+                     p.G, seq_len, k, sl2, p.chunk, p.nsplit, p.ntile_cap, with_scores,
                      (float*)(ws + p.off_part_o), (float*)(ws + p.off_part_ml),
                      (_Float16*)(ws + p.off_sc_val), (float*)(ws + p.off_sc_max));
+}
+
+// Finalize blocks [x0, x0 + nx) of the (output rows | score tiles) range.
+static hipError_t launch_finalize(const VerifyPlan& p, int D, const int* seq_len, int npairs, int k,
+                                  int Hkv, int x0, int nx, float* out, float* lse, float* scores,
+                                  int score_stride, const char* ws, hipStream_t stream) {
+  if (nx <= 0) return hipSuccess;
+  const int nblk_o = ceil_div(p.R * D, kVerThreads);
+  const dim3 grid(nx, npairs);
+#define S3R_FIN(VT, DD)                                                                              \
+  hipLaunchKernelGGL((verify_finalize_kernel<VT, DD>), grid, dim3(kVerThreads), 0, stream,          \
+                     (const float*)(ws + p.off_part_o), (const float*)(ws + p.off_part_ml),          \
+                     (const VT*)(ws + p.off_sc_val), (const float*)(ws + p.off_sc_max), seq_len, k,  \
+                     Hkv, p.G, p.chunk, p.nsplit, p.ntile_cap, p.RP, nblk_o, x0, out, lse, scores,   \
+                     score_stride)
+  if (p.mfma) {
+    S3R_FIN(_Float16, 128);
+  } else if (D == 128) {
+    S3R_FIN(float, 128);
+  } else {
+    S3R_FIN(float, 64);
+  }
+#undef S3R_FIN
+  return hipGetLastError();
 }
 
 hipError_t launch_verify(int dtype, int D, const void* q, const void* kp, const void* vp,
                          const int* bt, int max_pages, int Hkv, const int* seq_len, int B, int k,
                          int Hq, float scale, int max_seq_len, float* out, float* lse,
-                         float* scores, int score_stride, void* ws_v, hipStream_t stream) {
+                         float* scores, int score_stride, bool defer_scores, void* ws_v,
+                         hipStream_t stream) {
   const VerifyPlan p = verify_plan(B, k, Hq, Hkv, D, dtype, max_seq_len);
   char* ws = (char*)ws_v;
   const float sl2 = scale * kLog2e;
-  const int with_scores = scores != nullptr;
+  const int with_scores = (scores != nullptr || defer_scores) ? 1 : 0;
   const int npairs = B * Hkv;
-  const int nblk_o = ceil_div(p.R * D, kVerThreads);
-  const int nblk_s = with_scores ? ceil_div(p.ntile_cap, kFinTiles) : 0;
-  for (int pair0 = 0; pair0 < npairs; pair0 += p.pairs_per_batch) {
-    const int nb = npairs - pair0 < p.pairs_per_batch ? npairs - pair0 : p.pairs_per_batch;
-    if (p.mfma) {
+  if (p.mfma) {
 #define S3R_MFMA(NTV) \
-  launch_mfma<NTV>(p, q, kp, vp, bt, max_pages, Hkv, seq_len, pair0, nb, k, sl2, with_scores, ws, stream)
-      switch (p.NT) {
-        case 1: S3R_MFMA(1); break;
-        case 2: S3R_MFMA(2); break;
-        case 3: S3R_MFMA(3); break;
-        case 4: S3R_MFMA(4); break;
-        default: return hipErrorInvalidValue;
-      }
+  launch_mfma<NTV>(p, q, kp, vp, bt, max_pages, Hkv, seq_len, npairs, k, sl2, with_scores, ws, stream)
+    switch (p.NT) {
+      case 1: S3R_MFMA(1); break;
+      case 2: S3R_MFMA(2); break;
+      case 3: S3R_MFMA(3); break;
+      case 4: S3R_MFMA(4); break;
+      default: return hipErrorInvalidValue;
+    }
 #undef S3R_MFMA
-    } else {
-#define S3R_GEN(TT, DD)                                                                             \
-  hipLaunchKernelGGL((verify_generic_kernel<TT, DD>), dim3(p.nsplit, nb), dim3(kVerThreads), 0,    \
-                     stream, (const TT*)q, (const TT*)kp, (const TT*)vp, bt, max_pages, Hkv, p.G,  \
-                     seq_len, k, sl2, p.chunk, p.nsplit, p.ntile_cap, p.RP, with_scores, pair0,     \
-                     (float*)(ws + p.off_part_o), (float*)(ws + p.off_part_ml),                     \
+  } else {
+#define S3R_GEN(TT, DD)                                                                               \
+  hipLaunchKernelGGL((verify_generic_kernel<TT, DD>), dim3(p.nsplit, npairs), dim3(kVerThreads), 0,  \
+                     stream, (const TT*)q, (const TT*)kp, (const TT*)vp, bt, max_pages, Hkv, p.G,    \
+                     seq_len, k, sl2, p.chunk, p.nsplit, p.ntile_cap, p.RP, with_scores,              \
+                     (float*)(ws + p.off_part_o), (float*)(ws + p.off_part_ml),                       \
                      (float*)(ws + p.off_sc_val), (float*)(ws + p.off_sc_max))
-      if (dtype == 1) {
-        if (D == 128) S3R_GEN(BF16Val, 128); else S3R_GEN(BF16Val, 64);
-      } else {
-        if (D == 128) S3R_GEN(float, 128); else S3R_GEN(float, 64);
-      }
-#undef S3R_GEN
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const dim3 fgrid(nblk_o + nblk_s, nb);
-#define S3R_FIN(VT, DD)                                                                             \
-  hipLaunchKernelGGL((verify_finalize_kernel<VT, DD>), fgrid, dim3(kVerThreads), 0, stream,        \
-                     (const float*)(ws + p.off_part_o), (const float*)(ws + p.off_part_ml),         \
-                     (const VT*)(ws + p.off_sc_val), (const float*)(ws + p.off_sc_max), seq_len, k, \
-                     Hkv, p.G, p.chunk, p.nsplit, p.ntile_cap, p.RP, nblk_o, pair0, out, lse,       \
-                     scores, score_stride)
-    if (p.mfma) {
-      S3R_FIN(_Float16, 128);
-    } else if (D == 128) {
-      S3R_FIN(float, 128);
+    if (dtype == 1) {
+      if (D == 128) S3R_GEN(BF16Val, 128); else S3R_GEN(BF16Val, 64);
     } else {
-      S3R_FIN(float, 64);
+      if (D == 128) S3R_GEN(float, 128); else S3R_GEN(float, 64);
     }
-#undef S3R_FIN
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+#undef S3R_GEN
   }
-  return hipSuccess;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nblk_o = ceil_div(p.R * D, kVerThreads);
+  const int nblk_s = (scores != nullptr && !defer_scores) ? ceil_div(p.ntile_cap, kFinTiles) : 0;
+  return launch_finalize(p, D, seq_len, npairs, k, Hkv, 0, nblk_o + nblk_s, out, lse,
+                         defer_scores ? nullptr : scores, score_stride, ws, stream);
+}
+
+hipError_t launch_verify_scores(int dtype, int D, const int* seq_len, int B, int k, int Hq, int Hkv,
+                                int max_seq_len, float* scores, int score_stride, const void* ws,
+                                hipStream_t stream) {
+  const VerifyPlan p = verify_plan(B, k, Hq, Hkv, D, dtype, max_seq_len);
+  const int nblk_o = ceil_div(p.R * D, kVerThreads);
+  return launch_finalize(p, D, seq_len, B * Hkv, k, Hkv, nblk_o, ceil_div(p.ntile_cap, kFinTiles), nullptr,
+                         nullptr, scores, score_stride, (const char*)ws, stream);
 }
 
 }  // namespace s3r

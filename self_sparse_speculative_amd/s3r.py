@@ -27,7 +27,7 @@ S3R_F32, S3R_BF16 = 0, 1
 EXPORTED = (
     "s3r_status_string", "s3r_version", "s3r_budget", "s3r_select",
     "s3r_sparse_decode_workspace_bytes", "s3r_sparse_decode_attn",
-    "s3r_verify_workspace_bytes", "s3r_verify_attn",
+    "s3r_verify_workspace_bytes", "s3r_verify_attn", "s3r_verify_attn_deferred", "s3r_verify_scores",
     "s3r_spec_sample_workspace_bytes", "s3r_spec_sample",
 )
 
@@ -86,6 +86,12 @@ def load():
         L.s3r_verify_attn.restype = ctypes.c_int
         L.s3r_verify_attn.argtypes = [vp, ctypes.POINTER(PagedKVStruct), vp, i32, i32, i32, f32, i32, vp,
                                       vp, vp, i32, vp, sz, vp]
+        L.s3r_verify_attn_deferred.restype = ctypes.c_int
+        L.s3r_verify_attn_deferred.argtypes = [vp, ctypes.POINTER(PagedKVStruct), vp, i32, i32, i32, f32, i32,
+                                               vp, vp, vp, sz, vp]
+        L.s3r_verify_scores.restype = ctypes.c_int
+        L.s3r_verify_scores.argtypes = [ctypes.POINTER(PagedKVStruct), vp, i32, i32, i32, i32, vp, i32, vp, sz,
+                                        vp]
         L.s3r_spec_sample_workspace_bytes.restype = sz
         L.s3r_spec_sample_workspace_bytes.argtypes = [i32, i32, i32]
         L.s3r_spec_sample.restype = ctypes.c_int
@@ -240,6 +246,41 @@ def verify_attn(q, kv: PagedKV, seq_len, k, scale, max_seq_len, out=None, lse=No
                              int(max_seq_len), _ptr(out), _ptr(lse), _ptr(scores), stride, _ptr(buf),
                              buf.numel(), _stream(stream)), "s3r_verify_attn")
     return out, lse, scores
+
+
+def verify_attn_deferred(q, kv: PagedKV, seq_len, k, scale, max_seq_len, out=None, lse=None, want_lse=True,
+                         ws=None, stream=None):
+    """s3r_verify_attn_deferred: output rows and lse now, score partials kept in the workspace for
+    verify_scores. Returns (out, lse)."""
+    L = load()
+    B, kp1, Hq, D = q.shape
+    assert kp1 == k + 1
+    if out is None:
+        out = torch.empty((B, k + 1, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, k + 1, Hq), dtype=torch.float32, device=q.device)
+    nb = verify_workspace_bytes(B, k, Hq, kv.num_kv_heads, D, kv.dtype_code, int(max_seq_len))
+    buf = _ws(ws, q.device).get("verify", nb)
+    _check(L.s3r_verify_attn_deferred(_ptr(q), ctypes.byref(kv.struct), _ptr(seq_len), B, int(k), Hq,
+                                      float(scale), int(max_seq_len), _ptr(out), _ptr(lse), _ptr(buf),
+                                      buf.numel(), _stream(stream)), "s3r_verify_attn_deferred")
+    return out, lse
+
+
+def verify_scores(kv: PagedKV, seq_len, B, k, Hq, head_dim, max_seq_len, scores=None, score_stride=None, ws=None,
+                  stream=None):
+    """s3r_verify_scores: the scores of the preceding verify_attn_deferred on the same workspace."""
+    L = load()
+    Hkv = kv.num_kv_heads
+    if scores is None:
+        stride = int(max_seq_len) if score_stride is None else int(score_stride)
+        scores = torch.empty((B, Hkv, stride), dtype=torch.float32, device=seq_len.device)
+    nb = verify_workspace_bytes(B, k, Hq, Hkv, head_dim, kv.dtype_code, int(max_seq_len))
+    buf = _ws(ws, seq_len.device).get("verify", nb)
+    _check(L.s3r_verify_scores(ctypes.byref(kv.struct), _ptr(seq_len), int(B), int(k), int(Hq), int(max_seq_len),
+                               _ptr(scores), scores.shape[2], _ptr(buf), buf.numel(), _stream(stream)),
+           "s3r_verify_scores")
+    return scores
 
 
 def spec_sample_workspace_bytes(B, k, V) -> int:

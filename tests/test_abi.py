@@ -128,6 +128,24 @@ def test_verify_validation(lib):
     assert f(*args(_kv(), stride=0, sc=None, ws_b=ws - 1)) == WORKSPACE
 
 
+def test_verify_deferred_validation(lib):
+    fd, fs = lib.s3r_verify_attn_deferred, lib.s3r_verify_scores
+    ws = lib.s3r_verify_workspace_bytes(4, 6, 32, 8, 128, 1, 160)
+    dargs = lambda kvs, k=6, Hq=32, msl=160, ws_b=ws, out=FAKE: (
+        FAKE, ctypes.byref(kvs), FAKE, 4, k, Hq, 0.088, msl, out, None, FAKE, ws_b, None)
+    assert fd(*dargs(_kv(), out=None)) == INVALID
+    assert fd(*dargs(_kv(), k=16)) == INVALID
+    assert fd(*dargs(_kv(), msl=161)) == INVALID
+    assert fd(*dargs(_kv(hkv=4), k=15, Hq=32)) == UNSUPPORTED
+    assert fd(*dargs(_kv(), ws_b=ws - 1)) == WORKSPACE
+    sargs = lambda kvs, sc=FAKE, stride=160, ws_b=ws, msl=160: (
+        ctypes.byref(kvs), FAKE, 4, 6, 32, msl, sc, stride, FAKE, ws_b, None)
+    assert fs(*sargs(_kv(), sc=None)) == INVALID           # scores are required here
+    assert fs(*sargs(_kv(), stride=159)) == INVALID
+    assert fs(*sargs(_kv(page=32))) == UNSUPPORTED
+    assert fs(*sargs(_kv(), ws_b=ws - 1)) == WORKSPACE
+
+
 def test_sample_validation(lib):
     f = lib.s3r_spec_sample
     ws = lib.s3r_spec_sample_workspace_bytes(4, 6, 1000)

@@ -317,6 +317,31 @@ def test_verify_without_scores_matches(key, ov):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("key,cid,ov", [("c2v", 2, {"B": 4}), ("c5k8", 5, {"B": 2, "k": 8, "lengths": ("uniform", 900, 3000)}),
+                                        ("g64", 1, {"D": 64, "dtype": "bf16", "B": 2, "Hq": 8, "Hkv": 2,
+                                                    "lengths": ("uniform", 300, 600)})])
+def test_verify_deferred_scores_on_a_second_stream(key, cid, ov):
+    # output rows now, scores later on another stream: bit-identical to the one-call form
+    cfg, batch, t = _batch(key, cid, parts=("kv", "q", "scores") if key == "g64" else ("kv", "q"), **ov)
+    ms = int(batch.seq_len.max())
+    o1, l1, s1 = run_verify(cfg, batch, t)
+    ws = s3r.Workspace()
+    o2, l2 = s3r.verify_attn_deferred(t["q_verify"], t["kv"], t["seq_len"], cfg.k, float(batch.scale), ms, ws=ws)
+    done = torch.cuda.Event()
+    done.record()
+    side = torch.cuda.Stream()
+    side.wait_event(done)
+    with torch.cuda.stream(side):
+        s2 = s3r.verify_scores(t["kv"], t["seq_len"], cfg.B, cfg.k, cfg.Hq, cfg.D, ms, ws=ws,
+                               stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for b in range(cfg.B):
+        S = int(batch.seq_len[b])
+        assert torch.equal(s1[b, :, :S], s2[b, :, :S]), b
+
+
 def test_invalid_arguments_raise():
     cfg, batch, t = _batch("c1", 1)
     with pytest.raises(s3r.S3RError):
