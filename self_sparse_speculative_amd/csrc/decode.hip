@@ -264,7 +264,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
     const int* __restrict__ bt, int max_pages, int Hkv, int G, const int* __restrict__ idx,
     int nsel_cap, const int* __restrict__ n_sel, const int* __restrict__ sel_len,
-    const int* __restrict__ cur_len, float scale_log2, int chunk, int nsplit, float* __restrict__ part) {
+    const int* __restrict__ cur_len, float scale_log2, int chunk, int nsplit, float* __restrict__ part,
+    float* __restrict__ out, float* __restrict__ lse) {
   constexpr int D = 128;
   constexpr int kWaves = kDecThreads / kWave;
   __shared__ __attribute__((aligned(16))) uint16_t vt[kWaves][D * kDvtStride];
@@ -277,9 +278,17 @@ __global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
   const int ns = n_sel[b], L = sel_len[b], cur = cur_len[b];
   const int total = ns + (cur - L);
   const int p0 = split * chunk;
-  if (p0 >= total) return;
-  const int p1 = min(total, p0 + chunk);
   const int Hq = Hkv * G;
+  if (p0 >= total) {
+    if (nsplit == 1) {  // nothing attended: zero output, lse = -inf
+      for (int t = tid; t < G * D; t += kDecThreads) {
+        out[((size_t)b * Hq + kv * G + t / D) * D + t % D] = 0.f;
+        if (lse != nullptr && t % D == 0) lse[(size_t)b * Hq + kv * G + t / D] = kNegInf;
+      }
+    }
+    return;
+  }
+  const int p1 = min(total, p0 + chunk);
 
   // Resolve the split's positions to cache rows (page, KV head, slot) once.
   const int* idx_row = idx + ((size_t)b * Hkv + kv) * nsel_cap;
@@ -428,6 +437,22 @@ __global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
     }
     __syncthreads();
   }
+  if (nsplit == 1) {
+    // The only split: normalise here (same arithmetic as the split merge with
+    // one split, whose weight is exp2(0) = 1).
+    for (int t = tid; t < G * D; t += kDecThreads) {
+      const int g = t / D, d = t % D;
+      float Mg = kNegInf;
+      for (int w = 0; w < kWaves; ++w) Mg = fmaxf(Mg, ml_sh[w][0][g]);
+      const float bg = Mg == kNegInf ? 0.f : Mg;
+      float Ls = 0.f;
+      for (int w = 0; w < kWaves; ++w) Ls += ml_sh[w][1][g] * exp2f_fast(ml_sh[w][0][g] - bg);
+      const size_t h = (size_t)b * Hq + kv * G + g;
+      out[h * D + d] = Ls > 0.f ? obuf[g * D + d] / Ls : 0.f;
+      if (lse != nullptr && d == 0) lse[h] = Ls > 0.f ? (bg + __log2f(Ls)) * kLn2 : kNegInf;
+    }
+    return;
+  }
   for (int t = tid; t < G * D; t += kDecThreads) {
     const int g = t / D, d = t % D;
     float* rec = part + (((size_t)b * Hq + kv * G + g) * nsplit + split) * (D + 2);
@@ -530,13 +555,19 @@ hipError_t launch_sparse_decode(int dtype, int D, int G, const void* q, const vo
   const float sl2 = scale * kLog2e;
   float* part = (float*)ws;
   if (dtype == 1 && D == 128) {
-    hipLaunchKernelGGL(sparse_decode_mfma_kernel, dim3(nsplit, Hkv, B), dim3(kDecThreads), 0, stream,
+    // At most kDecChunkMfma positions per split, spread evenly over the splits
+    // the host bound needs (a multiple of the subtile): 4922 positions become
+    // 3 x 1664 rather than 2048 + 2048 + 826.
+    const int att = max_attend < 1 ? 1 : max_attend;
+    const int ns = ceil_div(att, kDecChunkMfma);
+    const int chunk = kDecBalance ? ceil_div(ceil_div(att, ns), kDsub) * kDsub : kDecChunkMfma;
+    hipLaunchKernelGGL(sparse_decode_mfma_kernel, dim3(ns, Hkv, B), dim3(kDecThreads), 0, stream,
                        (const bf16_t*)q, (const bf16_t*)kp, (const bf16_t*)vp, bt, max_pages, Hkv, G, idx,
-                       nsel_cap, n_sel, sel_len, cur_len, sl2, kDecChunkMfma, nsplit, part);
+                       nsel_cap, n_sel, sel_len, cur_len, sl2, chunk, ns, part, out, lse);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || ns == 1) return e;  // one split writes the output itself
     hipLaunchKernelGGL((decode_combine_kernel<128>), dim3(Hkv * G, B), dim3(128), 0, stream, part, n_sel,
-                       sel_len, cur_len, Hkv * G, kDecChunkMfma, nsplit, out, lse);
+                       sel_len, cur_len, Hkv * G, chunk, ns, out, lse);
     return hipGetLastError();
   }
   if (dtype == 1) {

@@ -14,15 +14,26 @@ struct BF16Val {
 };
 
 constexpr int kDecChunk = 256;         // attended positions per draft split (vector path)
-constexpr int kDecChunkMfma = 512;     // attended positions per draft split (bf16 x 128 MFMA path)
+#ifndef S3R_DRAFT_CHUNK
+#define S3R_DRAFT_CHUNK 2048
+#endif
+constexpr int kDecChunkMfma = S3R_DRAFT_CHUNK;  // most attended positions per draft split (bf16 x 128 MFMA path)
+#ifndef S3R_DRAFT_BALANCE
+#define S3R_DRAFT_BALANCE 1
+#endif
+constexpr bool kDecBalance = S3R_DRAFT_BALANCE != 0;  // equal-size draft splits
 #ifndef S3R_VERIFY_CHUNK
 #define S3R_VERIFY_CHUNK 2048
 #endif
 constexpr int kVerChunkMfma = S3R_VERIFY_CHUNK;  // context positions per verify split (bf16 x 128 path)
-#ifndef S3R_VERIFY_PREFETCH
-#define S3R_VERIFY_PREFETCH 0
+#ifndef S3R_VERIFY_Q_LDS
+#define S3R_VERIFY_Q_LDS 1
 #endif
-constexpr bool kVerPrefetch = S3R_VERIFY_PREFETCH != 0;  // software-pipelined K/V loads in verify
+// Verify query fragments read from LDS each subtile instead of held in
+// registers, for three row tiles (33-48 rows): the freed VGPRs let two
+// workgroups share a CU instead of one (36 rows at 24K: 3.90 -> 3.64 ms).
+// At two row tiles the same change spills and is slower (3.39 -> 3.48 ms).
+constexpr bool kVerQLds = S3R_VERIFY_Q_LDS != 0;
 constexpr int kVerChunkGeneric = 256;  // context positions per verify split (generic path)
 constexpr int kSmpChunks = 64;         // vocabulary chunks of the final draw
 

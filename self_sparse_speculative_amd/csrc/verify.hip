@@ -57,8 +57,8 @@ __device__ __forceinline__ uint32_t u4_word(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-template <int NT, bool PF>
-__global__ __launch_bounds__(kVerThreads, (NT <= 2 && !PF) ? 2 : 1) void verify_mfma_kernel(
+template <int NT, bool QL>
+__global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
     const int* __restrict__ bt, int max_pages, int npairs, int Hkv, int G,
     const int* __restrict__ seq_len, int k, float scale_log2, int chunk, int nsplit, int ntile_cap,
@@ -69,6 +69,9 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 && !PF) ? 2 : 1) void verify_
   __shared__ __attribute__((aligned(16))) uint16_t vt[kVerWaves][D * kVtStride];
   __shared__ float ml_sh[kVerWaves][2][RP];
   __shared__ int pages_sh[kVerChunkMfma / kPage];
+  // QL: Q rows as B fragments, slot (nt, kk, lane) = row nt*16 + lane%16,
+  // elements kk*32 + 8*(lane/16) .. +8 (zero rows past R)
+  __shared__ uint4 q_sh[QL ? NT * 4 * 64 : 1];
 
   // Workgroups are dispatched round-robin over the XCDs; consecutive splits of
   // one (sequence, KV head) pair go to the same XCD.
@@ -87,21 +90,34 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 && !PF) ? 2 : 1) void verify_
   const int P0 = S - (k + 1);
   const size_t bkv = (size_t)pair;
 
-  bf16x8_t qf[NT][4];
+  bf16x8_t qf[QL ? 1 : NT][4];
   int row_last[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = nt * 16 + n16;
-    if (r < R) {
-      const int i = r / G, h = kv * G + r % G;
-      const bf16_t* qp = q + (((size_t)b * (k + 1) + i) * Hq + h) * D + g4 * 8;
+    row_last[nt] = r < R ? P0 + r / G : -1;
+    if constexpr (!QL) {
+      if (r < R) {
+        const int i = r / G, h = kv * G + r % G;
+        const bf16_t* qp = q + (((size_t)b * (k + 1) + i) * Hq + h) * D + g4 * 8;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qf[nt][kk] = *reinterpret_cast<const bf16x8_t*>(qp + kk * 32);
-      row_last[nt] = P0 + i;
-    } else {
+        for (int kk = 0; kk < 4; ++kk) qf[nt][kk] = *reinterpret_cast<const bf16x8_t*>(qp + kk * 32);
+      } else {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qf[nt][kk] = bf16x8_t{};
-      row_last[nt] = -1;
+        for (int kk = 0; kk < 4; ++kk) qf[nt][kk] = bf16x8_t{};
+      }
+    }
+  }
+  if constexpr (QL) {
+    for (int t = tid; t < NT * 4 * 64; t += kVerThreads) {
+      const int nt = t >> 8, kk = (t >> 6) & 3, l = t & 63;
+      const int r = nt * 16 + (l & 15);
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (r < R) {
+        const int i = r / G, h = kv * G + r % G;
+        v = *reinterpret_cast<const uint4*>(q + (((size_t)b * (k + 1) + i) * Hq + h) * D + kk * 32 + (l >> 4) * 8);
+      }
+      q_sh[t] = v;
     }
   }
 
@@ -148,14 +164,10 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 && !PF) ? 2 : 1) void verify_
     }
   };
 
-  Sub cur, nxt;
+  Sub cur;
   if (wave < nsub) load_sub(wave, cur);
   for (int st = wave; st < nsub; st += kVerWaves) {
     const int pos0 = c0 + st * kSub;
-    if (PF) {
-      // the next subtile's loads are in flight while this one is computed
-      if (st + kVerWaves < nsub) load_sub(st + kVerWaves, nxt);
-    }
     const auto& kf = cur.kf;
     const auto& vraw = cur.vraw;
 
@@ -168,7 +180,9 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 && !PF) ? 2 : 1) void verify_
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[pt][kk], qf[nt][kk], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              kf[pt][kk], QL ? __builtin_bit_cast(bf16x8_t, q_sh[(nt * 4 + kk) * 64 + lane]) : qf[QL ? 0 : nt][kk],
+              acc, 0, 0, 0);
         s[pt][nt] = acc;
       }
     }
@@ -254,11 +268,7 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 && !PF) ? 2 : 1) void verify_
       for (int nt = 0; nt < NT; ++nt)
         oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfrag, pf[nt], oacc[nt][dt], 0, 0, 0);
     }
-    if (PF) {
-      cur = nxt;
-    } else if (st + kVerWaves < nsub) {
-      load_sub(st + kVerWaves, cur);
-    }
+    if (st + kVerWaves < nsub) load_sub(st + kVerWaves, cur);
   }
 
   // Merge the waves: rows are lane % 16 (+16 nt); l is a per-lane partial.
@@ -552,7 +562,7 @@ static void launch_mfma(const VerifyPlan& p, const void* q, const void* kp, cons
                         const int* bt, int max_pages, int Hkv, const int* seq_len, int npairs, int k,
                         float sl2, int with_scores, char* ws, hipStream_t stream) {
   const int nblocks = ceil_div(npairs, 8) * 8 * p.nsplit;
-  hipLaunchKernelGGL((verify_mfma_kernel<NT, kVerPrefetch>), dim3(nblocks), dim3(kVerThreads), 0, stream,
+  hipLaunchKernelGGL((verify_mfma_kernel<NT, kVerQLds && NT == 3>), dim3(nblocks), dim3(kVerThreads), 0, stream,
                      (const bf16_t*)q, (const bf16_t*)kp, (const bf16_t*)vp, bt, max_pages, npairs, Hkv,
                      p.G, seq_len, k, sl2, p.chunk, p.nsplit, p.ntile_cap, with_scores,
                      (float*)(ws + p.off_part_o), (float*)(ws + p.off_part_ml),

@@ -134,9 +134,27 @@ def test_draft_bf16(key, cid, ov):
 
 @pytest.mark.parametrize("G", [1, 3, 6, 16])
 def test_draft_bf16_group_sizes(G):
-    # head groups the vector path does not cover; long lists span several 512-position splits
+    # head groups the vector path does not cover; lists of up to 3000 positions span two splits
     cfg, batch, t = _batch(f"c2g{G}", 2, B=3, Hq=2 * G, Hkv=2, lengths=("uniform", 3000, 30000), s_num=1, s_den=10)
     _draft_case(cfg, batch, t, [1, cfg.k], range(cfg.B), TOL_BF16, False)
+
+
+@pytest.mark.parametrize("key,cid,ov", [("c1", 1, {}), ("c2d", 2, {"B": 6})])
+def test_draft_nothing_attended(key, cid, ov):
+    # no kept position and no position of this round: output 0, lse = -inf (both kernel paths)
+    cfg, batch, t = _batch(key, cid, **ov)
+    idx = torch.zeros((cfg.B, cfg.Hkv, 4), dtype=torch.int32, device="cuda")
+    n_sel = torch.zeros((cfg.B,), dtype=torch.int32, device="cuda")
+    out = torch.full((cfg.B, cfg.Hq, cfg.D), 7.0, dtype=torch.float32, device="cuda")
+    lse = torch.full((cfg.B, cfg.Hq), 7.0, dtype=torch.float32, device="cuda")
+    s3r.sparse_decode_attn(t["q_draft"][0], t["kv"], idx, n_sel, t["ctx_len"], t["ctx_len"], float(batch.scale), 4,
+                           out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert (out == 0).all() and torch.isneginf(lse).all()
+    ro, rl = oracle.sparse_decode(batch.q_draft[0, 0], batch.k_pages, batch.v_pages, batch.block_table[0],
+                                  np.zeros((cfg.Hkv, 4), np.int32), 0, int(batch.ctx_len[0]), int(batch.ctx_len[0]),
+                                  float(batch.scale))
+    assert (ro == 0).all() and np.isneginf(rl).all()
 
 
 def test_draft_full_budget_is_dense():
@@ -282,6 +300,31 @@ def test_spec_sample_chi_square_on_gpu():
         counts = np.bincount(toks[sel, i], minlength=V)
         pv = stats.chisquare(counts, P[i] * sel.sum()).pvalue
         assert pv > 1e-3, (i, pv)
+
+
+# ----------------------------------------------------------------- rollout config
+
+@pytest.mark.parametrize("layer", [0, 27])
+def test_rollout_config_round(layer):
+    """Config 4 (Qwen3-1.7B shapes, 1024-token prompt prefix page-aliased across the 8 responses
+    of a prompt, lognormal response lengths): two prompts x 8 responses, first and last of the 28
+    layers, every step of the round against the oracle."""
+    cfg = get_config(4, B=16)
+    batch = make_batch(cfg, layer=layer)
+    shared = 1024 // cfg.page
+    for g in range(2):
+        rows = batch.block_table[8 * g:8 * g + 8, :shared]
+        assert (rows == rows[0]).all()  # the prefix pages really are shared
+    assert not np.array_equal(batch.block_table[0, :shared], batch.block_table[8, :shared])
+    t = to_dev(batch)
+    idx, n_sel = run_select(cfg, batch, t)
+    torch.cuda.synchronize()
+    _check_select(cfg, batch, batch.scores, idx, n_sel, [(b, kv) for b in range(cfg.B) for kv in range(cfg.Hkv)])
+    _draft_case(cfg, batch, t, [1, cfg.k], range(cfg.B), TOL_BF16, False)
+    _verify_case(cfg, batch, t, range(cfg.B), False)
+    toks, nout, acc = run_sample(cfg, batch, t)
+    torch.cuda.synchronize()
+    _check_sample(cfg, batch, toks, nout, acc, batch.temperature, range(cfg.B))
 
 
 # ----------------------------------------------------------------- robustness
