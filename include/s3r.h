@@ -40,7 +40,9 @@
  *     Device values beyond the host bounds are undefined behaviour.
  *   - The workspace of a call is caller memory of at least the size the
  *     matching *_workspace_bytes() returns; its content on entry does not
- *     matter and on exit is unspecified. Concurrent calls must not share one.
+ *     matter and on exit is unspecified, except that s3r_verify_attn_deferred
+ *     leaves in it what the following s3r_verify_scores reads. Concurrent
+ *     calls must not share one.
  *   - Identical inputs give bit-identical outputs (no float atomics; fixed
  *     reduction orders).
  *   - Status codes: S3R_ERR_INVALID_ARG for null required pointers,

@@ -8,10 +8,14 @@
 //
 // The step is a gather: every attended position costs one K row and one V row
 // (2 * head_dim * element bytes) and the work per byte is G multiply-adds per
-// element, so it is bound by HBM gather bandwidth, not by arithmetic. Layout
-// of the work:
-//   * grid (split, KV head, sequence); a split is a fixed chunk of the
-//     attended list (selected positions first, then this round's positions);
+// element, so it is bound by HBM gather bandwidth, not by arithmetic. Grid
+// (split, KV head, sequence); a split is a chunk of the attended list
+// (selected positions first, then this round's positions).
+//
+// bf16, head_dim 128: sparse_decode_mfma_kernel (below), splits of at most
+// 2048 positions made equal; a lone split writes the output itself.
+//
+// Other dtypes / head_dim 64 (sparse_decode_kernel), splits of 256:
 //   * 16 lanes share one position row (each lane loads head_dim/16 contiguous
 //     elements, 16 B for bf16 x 128), so one wave gathers 4 rows per load and
 //     one workgroup (4 waves) keeps 16 position streams in flight;

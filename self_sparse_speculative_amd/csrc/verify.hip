@@ -8,14 +8,17 @@
 // rollouts for RL - What does it mean?", mechanism paragraph: the selector's
 // scores come from the verifier's last attention pass.
 //
-// Work split: grid (split, KV head, sequence); a split is a fixed chunk of the
-// context. The (k+1) * G query rows of one KV head share every K/V byte read,
-// so each chunk is streamed once for all rows.
+// Work split: one workgroup per (split, KV head, sequence); a split is a fixed
+// chunk of the context (2048 positions on the MFMA path). The (k+1) * G query
+// rows of one KV head share every K/V byte read, so each chunk is streamed
+// once for all rows.
 //
 // bf16, head_dim 128 (verify_mfma_kernel): the rows are the N side of
-// 16x16x32 bf16 MFMA tiles. Per 32-position subtile a wave
+// 16x16x32 bf16 MFMA tiles; a 1-D grid puts consecutive splits of one
+// (sequence, KV head) pair on one XCD. Per 32-position subtile a wave
 //   - loads K straight from the page into A fragments (16 B per lane) and
-//     computes S^T = K Q^T (positions x rows) with Q^T resident in registers;
+//     computes S^T = K Q^T (positions x rows) with Q^T resident in registers
+//     (read from LDS for three row tiles, see kVerQLds);
 //   - keeps the online-softmax state per row in the lanes that hold that row
 //     (lane % 16), so row rescales are lane-local;
 //   - writes the probabilities (relative to the running row maximum, fp16)
@@ -32,9 +35,11 @@
 //
 // verify_finalize_kernel merges the splits per row (log-sum-exp weights, split
 // order) and turns the score partials into normalised probabilities summed
-// over the rows. Splits meet at a kernel boundary: a merge inside the main
-// kernel would need an agent-scope release per workgroup, which costs more
-// than the extra launch on this multi-XCD part.
+// over the rows; its output-row blocks and score blocks can run as one launch
+// or, for s3r_verify_attn_deferred + s3r_verify_scores, as two. Splits meet
+// at a kernel boundary: merging inside the main kernel (by the last split to
+// arrive, or by splits that exchange row statistics and keep their
+// probabilities on chip) measured slower on this part.
 
 #include "common.hpp"
 #include "kernels.hpp"
