@@ -76,7 +76,13 @@ def to_dev(batch, s3r, torch):
 
 
 def source_sha(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of the code in a source file, ignoring // comments and blank lines."""
+    lines = []
+    for ln in open(path).read().splitlines():
+        code = ln.split("//", 1)[0].rstrip()
+        if code:
+            lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
 def load_traffic(kernel_src, key):
