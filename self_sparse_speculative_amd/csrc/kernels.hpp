@@ -23,9 +23,13 @@ constexpr int kDecChunkMfma = S3R_DRAFT_CHUNK;  // most attended positions per d
 #endif
 constexpr bool kDecBalance = S3R_DRAFT_BALANCE != 0;  // equal-size draft splits
 #ifndef S3R_VERIFY_CHUNK
-#define S3R_VERIFY_CHUNK 2048
+#define S3R_VERIFY_CHUNK 4096
 #endif
-constexpr int kVerChunkMfma = S3R_VERIFY_CHUNK;  // context positions per verify split (bf16 x 128 path)
+constexpr int kVerChunkMfma = S3R_VERIFY_CHUNK;  // most context positions per verify split (bf16 x 128 path)
+#ifndef S3R_VERIFY_BALANCE
+#define S3R_VERIFY_BALANCE 1
+#endif
+constexpr bool kVerBalance = S3R_VERIFY_BALANCE != 0;  // equal-size verify splits
 #ifndef S3R_VERIFY_Q_LDS
 #define S3R_VERIFY_Q_LDS 1
 #endif

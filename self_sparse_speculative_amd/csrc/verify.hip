@@ -9,7 +9,7 @@
 // scores come from the verifier's last attention pass.
 //
 // Work split: one workgroup per (split, KV head, sequence); a split is a fixed
-// chunk of the context (2048 positions on the MFMA path). The (k+1) * G query
+// chunk of the context (at most 4096 positions on the MFMA path, sized evenly). The (k+1) * G query
 // rows of one KV head share every K/V byte read, so each chunk is streamed
 // once for all rows.
 //
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
   // The chunk's physical pages, read once.
   const int* bt_row = bt + (size_t)b * max_pages;
   const int npg = ceil_div(c1 - c0, kPage);
-  if (tid < npg) pages_sh[tid] = bt_row[(c0 >> 4) + tid];
+  for (int t = tid; t < npg; t += kVerThreads) pages_sh[t] = bt_row[(c0 >> 4) + t];
   __syncthreads();
   uint16_t* my_vt = vt[wave];
   const int nsub = ceil_div(c1 - c0, kSub);
@@ -546,6 +546,11 @@ VerifyPlan verify_plan(int B, int k, int Hq, int Hkv, int D, int dtype, int max_
   p.RP = 16 * p.NT;
   p.chunk = p.mfma ? kVerChunkMfma : kVerChunkGeneric;
   p.nsplit = ceil_div(max_seq_len, p.chunk);
+  if (p.mfma && kVerBalance) {
+    // the splits the longest sequence needs, made equal (a multiple of the
+    // subtile): 24583 positions become 7 x 3520 rather than 6 x 4096 + 7
+    p.chunk = ceil_div(ceil_div(max_seq_len, p.nsplit), kSub) * kSub;
+  }
   p.ntile_cap = ceil_div(max_seq_len, kSub);
   // Partial records per (sequence, KV head) pair.
   const size_t nbkv = (size_t)B * Hkv;

@@ -208,7 +208,7 @@ def test_verify_c1_f32():
     ("c5k2", 5, {"B": 2, "k": 2, "lengths": ("uniform", 900, 3000)}),   # 12 rows
     ("c5k8", 5, {"B": 2, "k": 8, "lengths": ("uniform", 900, 3000)}),   # 36 rows (three row tiles)
     ("c3k15", 3, {"B": 2, "k": 15, "lengths": ("uniform", 100, 2100)}),  # 64 rows (four row tiles)
-    # long contexts: 31-38 splits of 2048 positions per (sequence, KV head)
+    # long contexts: 16-19 splits per (sequence, KV head)
     ("c3long", 3, {"B": 2, "lengths": ("uniform", 62000, 66000)}),
     ("c3xlong", 3, {"B": 1, "lengths": ("uniform", 75000, 76000)}),
     ("c3k15long", 3, {"B": 1, "k": 15, "lengths": ("uniform", 40000, 41000)}),
