@@ -29,7 +29,7 @@ constexpr int kVerChunkMfma = S3R_VERIFY_CHUNK;  // most context positions per v
 #ifndef S3R_VERIFY_BALANCE
 #define S3R_VERIFY_BALANCE 1
 #endif
-constexpr bool kVerBalance = S3R_VERIFY_BALANCE != 0;  // equal-size verify splits
+constexpr bool kVerBalance = S3R_VERIFY_BALANCE != 0;  // equal-size verify splits per sequence
 #ifndef S3R_VERIFY_Q_LDS
 #define S3R_VERIFY_Q_LDS 1
 #endif

@@ -85,9 +85,12 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
   if (pair >= npairs) return;
   const int b = pair / Hkv, kv = pair % Hkv;
   const int S = seq_len[b];
-  const int c0 = split * chunk;
+  // `chunk` is the most positions a split holds; each sequence spreads its
+  // ceil(S / chunk) splits evenly (a multiple of the subtile)
+  const int ch = kVerBalance ? ceil_div(ceil_div(S, ceil_div(S, chunk)), kSub) * kSub : chunk;
+  const int c0 = split * ch;
   if (c0 >= S) return;
-  const int c1 = min(S, c0 + chunk);
+  const int c1 = min(S, c0 + ch);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, g4 = lane >> 4;
   const int Hq = Hkv * G;
@@ -544,13 +547,12 @@ VerifyPlan verify_plan(int B, int k, int Hq, int Hkv, int D, int dtype, int max_
   p.mfma = (dtype == 1 && D == 128);
   p.NT = ceil_div(p.R, 16);
   p.RP = 16 * p.NT;
+  // MFMA path: at most kVerChunkMfma positions per split; the kernel spreads
+  // each sequence's splits evenly (24583 positions: 7 x 3520 rather than
+  // 6 x 4096 + 7). The split count of a sequence, ceil(S / chunk), is the
+  // same either way.
   p.chunk = p.mfma ? kVerChunkMfma : kVerChunkGeneric;
   p.nsplit = ceil_div(max_seq_len, p.chunk);
-  if (p.mfma && kVerBalance) {
-    // the splits the longest sequence needs, made equal (a multiple of the
-    // subtile): 24583 positions become 7 x 3520 rather than 6 x 4096 + 7
-    p.chunk = ceil_div(ceil_div(max_seq_len, p.nsplit), kSub) * kSub;
-  }
   p.ntile_cap = ceil_div(max_seq_len, kSub);
   // Partial records per (sequence, KV head) pair.
   const size_t nbkv = (size_t)B * Hkv;
