@@ -42,7 +42,10 @@ def parse():
     ap.add_argument("--sigma", type=float, default=None)
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences in the oracle's timed CPU sample")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="stacked layers (the rollout workload has 28; 1 times one layer of it)")
+    ap.add_argument("--cpu-seqs", type=int, default=None,
+                    help="sequences in the oracle's timed CPU sample (default 64 for one layer, 8 for 28 layers)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline (profiling runs)")
     ap.add_argument("--sweep", action="store_true",
                     help="run all 48 points of the 24K sweep (s x k x draft noise), one JSON line per point")
@@ -100,7 +103,10 @@ def load_traffic(kernel_src, key):
 
 
 def cpu_baseline(cfg, nseq, seed):
-    """The fp64 oracle, timed on a bounded sample of the same workload on the host cores."""
+    """The fp64 oracle, timed on a bounded sample of the same workload on the host cores.
+
+    With stacked layers every layer's select, draft steps and verify run on the first
+    layer's inputs (the oracle's cost does not depend on the values), then one sampling."""
     import oracle
     from s3r_inputs import make_batch
 
@@ -114,19 +120,22 @@ def cpu_baseline(cfg, nseq, seed):
     tokens = 0
     for b in range(nseq):
         L = int(batch.ctx_len[b])
-        idx = [oracle.select(batch.scores[b, kv], L, cfg.s_num, cfg.s_den, cfg.window) for kv in range(cfg.Hkv)]
-        n = len(idx[0])
-        for j in range(1, cfg.k + 1):
-            oracle.sparse_decode(batch.q_draft[j - 1, b], batch.k_pages, batch.v_pages, batch.block_table[b], idx, n,
-                                 L, L + j, float(batch.scale))
-        oracle.verify(batch.q_verify[b], batch.k_pages, batch.v_pages, batch.block_table[b], int(batch.seq_len[b]),
-                      cfg.k, float(batch.scale))
+        for _layer in range(cfg.layers):
+            idx = [oracle.select(batch.scores[b, kv], L, cfg.s_num, cfg.s_den, cfg.window) for kv in range(cfg.Hkv)]
+            n = len(idx[0])
+            for j in range(1, cfg.k + 1):
+                oracle.sparse_decode(batch.q_draft[j - 1, b], batch.k_pages, batch.v_pages, batch.block_table[b], idx,
+                                     n, L, L + j, float(batch.scale))
+            oracle.verify(batch.q_verify[b], batch.k_pages, batch.v_pages, batch.block_table[b],
+                          int(batch.seq_len[b]), cfg.k, float(batch.scale))
         _, n_out, _ = oracle.spec_sample(batch.zt[b], batch.zd[b], batch.d[b], batch.u[b], batch.temperature)
         tokens += int(n_out)
     dt = time.perf_counter() - t0
     return {"value": tokens / dt, "unit": "verified tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"full round (select, {cfg.k} draft steps, verify with scores, sampling) for the first {nseq} "
-                      f"of {cfg.B} sequences of the same workload, fp64 numpy, {dt:.1f} s, {tokens} tokens",
+            "sample": f"full round (select, {cfg.k} draft steps, verify with scores"
+                      + (f", for each of {cfg.layers} layers on the first layer's inputs" if cfg.layers > 1 else "")
+                      + f", sampling) for the first {nseq} of {cfg.B} sequences of the same workload, fp64 numpy, "
+                      f"{dt:.1f} s, {tokens} tokens",
             "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -317,11 +326,217 @@ def run_sweep(args, torch, s3r):
         torch.cuda.empty_cache()
 
 
+def rollout_unique_positions(seq_len, idx, n_sel, prefix, group, k):
+    """Unique (sequence-group, KV head, position) rows one layer's launches read, with the
+    shared prompt prefix counted once per group: verify, and each of the k draft steps."""
+    B, Hkv = idx.shape[0], idx.shape[1]
+    S = seq_len.astype(np.int64)
+    members = np.bincount(np.arange(B) // group)
+    ver = Hkv * (int(S.sum()) - int(((members - 1) * prefix).sum()))
+    dup = 0  # selected prefix rows read by more than one member of a group
+    for g in range(len(members)):
+        rows = range(g * group, g * group + int(members[g]))
+        for h in range(Hkv):
+            sel = [idx[b, h, :n_sel[b]] for b in rows]
+            sel = [s[s < prefix] for s in sel]
+            dup += sum(len(s) for s in sel) - len(np.unique(np.concatenate(sel)))
+    nsel = n_sel.astype(np.int64)
+    draft = [Hkv * int((nsel + j).sum()) - dup for j in range(1, k + 1)]
+    return ver, draft
+
+
+def run_rollout(args, cfg, torch, s3r):
+    """The stacked-layer rollout round: selection for every layer, then each of the k draft
+    steps through every layer, verification of every layer, and one sampling step.
+
+    Lengths, block tables (prompt-prefix pages aliased within each group of responses),
+    queries, first-round scores and logits come from the seeded generator; the K/V pages of
+    the layers (about 7.7 GB each) are drawn N(0, 1) on the device from a generator seeded
+    per layer, since host generation of all layers would take far longer than the run."""
+    from s3r_inputs import make_batch
+
+    L_layers, B, k, Hq, Hkv, D, P = cfg.layers, cfg.B, cfg.k, cfg.Hq, cfg.Hkv, cfg.D, cfg.page
+    prefix, group = cfg.lengths[1], cfg.lengths[5]
+    t0 = time.time()
+    lb = make_batch(cfg, seed=args.seed, parts=("logits",))
+    ctx_np, seq_np = lb.ctx_len, lb.seq_len
+    ctx_len = torch.from_numpy(ctx_np).cuda()
+    seq_len = torch.from_numpy(seq_np).cuda()
+    zt, zd = torch.from_numpy(lb.zt).cuda(), torch.from_numpy(lb.zd).cuda()
+    u, dtok = torch.from_numpy(lb.u).cuda(), torch.from_numpy(lb.d).cuda()
+    T = float(lb.temperature)
+    scale = float(lb.scale)
+    del lb
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    layers = []
+    gen = torch.Generator(device="cuda")
+    for l in range(L_layers):
+        b = make_batch(cfg, layer=l, seed=args.seed, parts=("q", "scores"))
+        assert np.array_equal(b.seq_len, seq_np)
+        gen.manual_seed(((args.seed * 1000003 + cfg.cid) * 1000003 + l) & ((1 << 63) - 1))
+        shape = (b.num_pages, Hkv, P, D)
+        kp = torch.empty(shape, dtype=torch.bfloat16, device="cuda").normal_(generator=gen)
+        vp = torch.empty(shape, dtype=torch.bfloat16, device="cuda").normal_(generator=gen)
+        layers.append({"kv": s3r.PagedKV(kp, vp, torch.from_numpy(b.block_table).cuda()),
+                       "q_draft": bf16(b.q_draft), "q_verify": bf16(b.q_verify),
+                       "scores": torch.from_numpy(b.scores).cuda(), "num_pages": b.num_pages})
+        del b
+        print(f"[bench] layer {l + 1}/{L_layers} resident ({time.time() - t0:.0f} s, "
+              f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB)", file=sys.stderr, flush=True)
+
+    max_ctx, max_seq = int(ctx_np.max()), int(seq_np.max())
+    cap = s3r.budget(max_ctx, cfg.s_num, cfg.s_den, cfg.window)
+    max_attend = cap + k
+    ws = s3r.Workspace()
+    idx = [torch.empty((B, Hkv, cap), dtype=torch.int32, device="cuda") for _ in range(L_layers)]
+    n_sel = [torch.empty((B,), dtype=torch.int32, device="cuda") for _ in range(L_layers)]
+    cur = [ctx_len + j for j in range(1, k + 1)]
+    dout = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    dlse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    vout = torch.empty((B, k + 1, Hq, D), dtype=torch.float32, device="cuda")
+    vlse = torch.empty((B, k + 1, Hq), dtype=torch.float32, device="cuda")
+    tokens = torch.empty((B, k + 1), dtype=torch.int32, device="cuda")
+    n_out = torch.empty((B,), dtype=torch.int32, device="cuda")
+    accepted = torch.empty((B, k), dtype=torch.int8, device="cuda")
+
+    def step(ev=None):
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        for l, ly in enumerate(layers):
+            s3r.select(ly["scores"], ctx_len, max_ctx, cfg.s_num, cfg.s_den, cfg.window, idx=idx[l], n_sel=n_sel[l])
+        rec(1)
+        for j in range(k):
+            for l, ly in enumerate(layers):
+                s3r.sparse_decode_attn(ly["q_draft"][j], ly["kv"], idx[l], n_sel[l], ctx_len, cur[j], scale,
+                                       max_attend, out=dout, lse=dlse, ws=ws)
+        rec(2)
+        for ly in layers:
+            s3r.verify_attn(ly["q_verify"], ly["kv"], seq_len, k, scale, max_seq, out=vout, lse=vlse,
+                            scores=ly["scores"], ws=ws)
+        rec(3)
+        s3r.spec_sample(zt, zd, dtok, u, T, tokens=tokens, n_out=n_out, accepted=accepted, ws=ws)
+        rec(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    tok_a = n_out.clone()
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(tok_a, n_out), "rounds over the same inputs must give the same token counts"
+    verified = int(n_out.sum().item())
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    phase = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])
+    t_sel, t_draft, t_ver, t_smp = phase.mean(axis=0)
+    round_median = float(np.median([e[0].elapsed_time(e[4]) for e in evs]))
+
+    # algorithmic bytes: logical rows (each sequence's own view of the cache) and unique
+    # rows (the shared prefix once per group, the HBM lower bound), per layer
+    e = 2
+    kv_row = 2 * D * e
+    S = seq_np.astype(np.int64)
+    L = ctx_np.astype(np.int64)
+    ver_io = B * (k + 1) * Hq * (D * e + D * 4 + 4)
+    draft_io = k * B * Hq * (D * e + D * 4 + 4)
+    ver_log = ver_uni = draft_log = draft_uni = sel_bytes = 0
+    for l in range(L_layers):
+        ix, ns = idx[l].cpu().numpy(), n_sel[l].cpu().numpy()
+        vu, du = rollout_unique_positions(seq_np, ix, ns, prefix, group, k)
+        ver_log += Hkv * int(S.sum()) * (kv_row + 4) + ver_io
+        ver_uni += vu * kv_row + Hkv * int(S.sum()) * 4 + ver_io
+        nsel = ns.astype(np.int64)
+        draft_log += sum(Hkv * int((nsel + j).sum()) * (kv_row + 4) for j in range(1, k + 1)) + draft_io
+        draft_uni += sum(d * kv_row + Hkv * int((nsel + j).sum()) * 4 for j, d in zip(range(1, k + 1), du)) + draft_io
+        sel_bytes += Hkv * int(L.sum()) * 4 + Hkv * int(nsel.sum()) * 4
+    smp_bytes = B * (2 * k + 1) * cfg.V * 4
+    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+    t_ver_launch = float(t_ver) / L_layers
+    ver_uni_launch, ver_log_launch = ver_uni / L_layers, ver_log / L_layers
+    round_uni = ver_uni + draft_uni + sel_bytes + smp_bytes
+    breakdown = {
+        "verified_tokens_per_round": verified,
+        "tokens_per_sequence": round(verified / B, 4),
+        "layers": L_layers,
+        "ms": {"select_all_layers": round(float(t_sel), 4), "draft_k_steps_all_layers": round(float(t_draft), 4),
+               "verify_all_layers": round(float(t_ver), 4), "spec_sample": round(float(t_smp), 4),
+               "round_median": round(round_median, 4)},
+        "GBs_unique": {"select": round(gbs(sel_bytes, t_sel), 1), "draft": round(gbs(draft_uni, t_draft), 1),
+                       "verify": round(gbs(ver_uni, t_ver), 1), "spec_sample": round(gbs(smp_bytes, t_smp), 1)},
+        "GBs_logical": {"draft": round(gbs(draft_log, t_draft), 1), "verify": round(gbs(ver_log, t_ver), 1)},
+        "draft_plus_verify_kv_GBs_unique": round(gbs(ver_uni + draft_uni, t_ver + t_draft), 1),
+        "draft_plus_verify_frac_of_hbm_peak": round(gbs(ver_uni + draft_uni, t_ver + t_draft) / HBM_PEAK_GBS, 4),
+        "round_algorithmic_bytes_unique": int(round_uni),
+        "round_algorithmic_bytes_logical": int(ver_log + draft_log + sel_bytes + smp_bytes),
+        "round_frac_of_hbm_peak": round(gbs(round_uni, ms_step) / HBM_PEAK_GBS, 4),
+        "kv_cache_GiB_resident": round(sum(ly["num_pages"] for ly in layers) * Hkv * P * kv_row / 2**30, 1),
+    }
+    copy_gbs, read_gbs = reference_rates(args, torch) if args.copy_gib > 0 else (None, None)
+    breakdown["device_copy_GBs"] = None if copy_gbs is None else round(copy_gbs, 1)
+    breakdown["device_read_GBs"] = None if read_gbs is None else round(read_gbs, 1)
+    del layers
+    torch.cuda.empty_cache()
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, min(args.cpu_seqs or 8, B), args.seed)
+    return {
+        "metric": "verified tokens/s per draft+verify round; KV-read GB/s as % of HBM peak",
+        "value": round(verified / (ms_step * 1e-3), 1),
+        "unit": "verified tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (K/V pages drawn on the device)",
+        "config": {
+            "workload": f"{cfg.name}: {L_layers} stacked attention layers, B={B} ({B // group} prompts x {group} "
+                        f"responses sharing a {prefix}-token prefix, page-aliased), Hq={Hq}, Hkv={Hkv}, head_dim={D}, "
+                        f"{cfg.dtype} paged KV (page {P}), responses lognormal(median {cfg.lengths[2]}, "
+                        f"sigma {cfg.lengths[3]}) clipped to {cfg.lengths[4]}, s={cfg.s_num}/{cfg.s_den}, window "
+                        f"{cfg.window}, k={k}, V={cfg.V}, one sampling step per round",
+            "global_batch": B,
+            "seq_len": max_seq,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "s3r_verify_attn: verify_mfma_kernel (split pass) + verify_finalize_kernel (merge, scores), "
+                      "per layer; unique bytes (shared prefix once per group)",
+            "bound": "hbm",
+            "achieved": round(gbs(ver_uni_launch, t_ver_launch), 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs(ver_uni_launch, t_ver_launch) / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": int(ver_uni_launch),
+            "logical_bytes_per_launch": int(ver_log_launch),
+            "ms_per_launch": round(t_ver_launch, 4),
+        },
+        "cpu_baseline": cpu,
+        "breakdown": breakdown,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the hot path is single-GPU; "
-              "sharding is described in DESIGN.md)", file=sys.stderr)
+              "sharding the batch by sequence or by KV head needs no exchange in the attention steps)", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -342,9 +557,13 @@ def main():
         ov["noise_std"] = args.sigma
     if args.batch is not None:
         ov["B"] = args.batch
+    if args.layers is not None:
+        ov["layers"] = args.layers
     cfg = get_config(args.config, **ov)
-    if cfg.layers != 1:
-        cfg = get_config(args.config, layers=1, **ov)
+    if cfg.layers > 1:
+        print(f"[bench] {cfg.name}: {cfg.layers} layers, B={cfg.B}, k={cfg.k}", file=sys.stderr, flush=True)
+        print(json.dumps(run_rollout(args, cfg, torch, s3r)))
+        return
     print(f"[bench] generating {cfg.name} B={cfg.B} k={cfg.k} s={cfg.s_num}/{cfg.s_den}", file=sys.stderr, flush=True)
     t0 = time.time()
     batch = make_batch(cfg, seed=args.seed)
@@ -358,7 +577,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg, min(args.cpu_seqs, cfg.B), args.seed)
+        cpu = cpu_baseline(cfg, min(args.cpu_seqs or 64, cfg.B), args.seed)
     B, k, Hq, Hkv, D = cfg.B, cfg.k, cfg.Hq, cfg.Hkv, cfg.D
     breakdown = dict(r["breakdown"])
     breakdown["device_copy_GBs"] = None if copy_gbs is None else round(copy_gbs, 1)
