@@ -34,4 +34,5 @@ from .budget import budget  # noqa: F401
 from .select import select  # noqa: F401
 from .attention import attend, gather, sparse_decode, verify, dense_decode  # noqa: F401
 from .sampling import softmax_t, invcdf, spec_decide, spec_sample  # noqa: F401
-from .round import next_lengths, verified_tokens  # noqa: F401
+from .round import commit, next_lengths, verified_tokens  # noqa: F401
+from .cache import kv_append  # noqa: F401

@@ -18,5 +18,6 @@ from .gen import (  # noqa: F401
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     make_batch,
+    make_round_inputs,
     unit_rng,
 )

@@ -17,7 +17,11 @@ Recipe (one independent PCG64 stream per (seed, config, layer, seq, tag)):
 * draft tokens d_b,i are drawn from softmax(zd_b,i / T) by the Gumbel-max
   construction (argmax of zd/T plus Gumbel noise, float64), or argmax(zd) at
   T = 0. They are inputs here because the drafting forward pass that would
-  sample them is outside this step.
+  sample them is outside this step;
+* multi-round runs (make_round_inputs): round r draws its own queries, the
+  K/V rows each draft step appends, the K/V rows of the verified block,
+  logits, uniforms and draft tokens, with the same distributions, from
+  streams of their own.
 """
 
 import math
@@ -32,6 +36,10 @@ from .configs import Config
 
 TAG_LEN, TAG_PAGES, TAG_QD, TAG_QV, TAG_K, TAG_V, TAG_SCORES = 1, 2, 3, 4, 5, 6, 7
 TAG_ZT, TAG_ZD, TAG_U, TAG_DTOK, TAG_KP, TAG_VP = 8, 9, 10, 11, 12, 13
+TAG_KD, TAG_VD, TAG_KB, TAG_VB = 14, 15, 16, 17
+# The streams of round r of a multi-round run use layer ROUND_LAYER + r, far
+# from the layer numbers of a model.
+ROUND_LAYER = 1 << 20
 
 _POOL_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
@@ -233,28 +241,75 @@ def make_batch(cfg: Config, layer: int = 0, seed: int = 0, B: Optional[int] = No
             sc[b, :, :L[b]] = exact_uniform_f32(unit_rng(seed, cfg.cid, layer, b, TAG_SCORES), (Hkv, int(L[b])))
         batch.scores = sc
     if "logits" in parts:
-        zt = np.empty((B, k + 1, V), dtype=np.float32)
-        zd = np.empty((B, k, V), dtype=np.float32)
-        u = np.empty((B, k + 1), dtype=np.float32)
-        d = np.empty((B, k), dtype=np.int32)
-        T = float(np.float32(cfg.temperature))
-
-        def do_logits(b):
-            # logits do not depend on the layer: one sampling step per round
-            zt[b] = np.float32(cfg.target_std) * unit_rng(seed, cfg.cid, 0, b, TAG_ZT).standard_normal((k + 1, V), dtype=np.float32)
-            noise = unit_rng(seed, cfg.cid, 0, b, TAG_ZD).standard_normal((k, V), dtype=np.float32)
-            zd[b] = zt[b, :k] + np.float32(cfg.noise_std) * noise
-            u[b] = exact_uniform_f32(unit_rng(seed, cfg.cid, 0, b, TAG_U), (k + 1,))
-            rg = unit_rng(seed, cfg.cid, 0, b, TAG_DTOK)
-            for i in range(k):
-                if T > 0.0:
-                    e = (rg.integers(0, 1 << 53, size=V, dtype=np.int64).astype(np.float64) + 0.5) * 2.0 ** -53
-                    g = -np.log(-np.log(e))
-                    d[b, i] = int(np.argmax(zd[b, i].astype(np.float64) / T + g))
-                else:
-                    d[b, i] = int(np.argmax(zd[b, i]))
-
-        with ThreadPoolExecutor(threads) as ex:
-            list(ex.map(do_logits, range(B)))
-        batch.zt, batch.zd, batch.u, batch.d = zt, zd, u, d
+        # logits do not depend on the layer: one sampling step per round
+        batch.zt, batch.zd, batch.u, batch.d = _logits(cfg, seed, 0, B, threads)
     return batch
+
+
+def _logits(cfg: Config, seed: int, layer: int, B: int, threads: int):
+    """Target and draft logits, uniforms and draft tokens of one round."""
+    k, V = cfg.k, cfg.V
+    zt = np.empty((B, k + 1, V), dtype=np.float32)
+    zd = np.empty((B, k, V), dtype=np.float32)
+    u = np.empty((B, k + 1), dtype=np.float32)
+    d = np.empty((B, k), dtype=np.int32)
+    T = float(np.float32(cfg.temperature))
+
+    def do_logits(b):
+        zt[b] = np.float32(cfg.target_std) * unit_rng(seed, cfg.cid, layer, b, TAG_ZT).standard_normal((k + 1, V), dtype=np.float32)
+        noise = unit_rng(seed, cfg.cid, layer, b, TAG_ZD).standard_normal((k, V), dtype=np.float32)
+        zd[b] = zt[b, :k] + np.float32(cfg.noise_std) * noise
+        u[b] = exact_uniform_f32(unit_rng(seed, cfg.cid, layer, b, TAG_U), (k + 1,))
+        rg = unit_rng(seed, cfg.cid, layer, b, TAG_DTOK)
+        for i in range(k):
+            if T > 0.0:
+                e = (rg.integers(0, 1 << 53, size=V, dtype=np.int64).astype(np.float64) + 0.5) * 2.0 ** -53
+                g = -np.log(-np.log(e))
+                d[b, i] = int(np.argmax(zd[b, i].astype(np.float64) / T + g))
+            else:
+                d[b, i] = int(np.argmax(zd[b, i]))
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(do_logits, range(B)))
+    return zt, zd, u, d
+
+
+@dataclass
+class RoundInputs:
+    """What the model would hand the step in round r of a multi-round run (one layer)."""
+    q_draft: np.ndarray  # [k][B][Hq][D]: query of draft step j (1..k) at position L + j - 1
+    k_draft: np.ndarray  # [k][B][Hkv][D]: K row draft step j appends at position L + j - 1
+    v_draft: np.ndarray
+    q_verify: np.ndarray  # [B][k+1][Hq][D]
+    k_block: np.ndarray  # [B][k+1][Hkv][D]: K rows of the block positions L .. L + k
+    v_block: np.ndarray
+    zt: np.ndarray  # float32 [B][k+1][V]
+    zd: np.ndarray  # float32 [B][k][V]
+    u: np.ndarray  # float32 [B][k+1]
+    d: np.ndarray  # int32 [B][k]
+
+
+def make_round_inputs(cfg: Config, rnd: int, seed: int = 0, B: Optional[int] = None,
+                      threads: Optional[int] = None) -> RoundInputs:
+    """Queries, new K/V rows, logits, uniforms and draft tokens of round ``rnd``."""
+    threads = _POOL_THREADS if threads is None else threads
+    B = cfg.B if B is None else B
+    lay = ROUND_LAYER + rnd
+    k, Hq, Hkv, D = cfg.k, cfg.Hq, cfg.Hkv, cfg.D
+    sd = _store_dtype(cfg)
+    qd = np.empty((k, B, Hq, D), dtype=sd)
+    kd = np.empty((k, B, Hkv, D), dtype=sd)
+    vd = np.empty((k, B, Hkv, D), dtype=sd)
+    qv = np.empty((B, k + 1, Hq, D), dtype=sd)
+    kb = np.empty((B, k + 1, Hkv, D), dtype=sd)
+    vb = np.empty((B, k + 1, Hkv, D), dtype=sd)
+    for b in range(B):
+        qd[:, b] = _normal(unit_rng(seed, cfg.cid, lay, b, TAG_QD), (k, Hq, D), cfg.dtype)
+        kd[:, b] = _normal(unit_rng(seed, cfg.cid, lay, b, TAG_KD), (k, Hkv, D), cfg.dtype)
+        vd[:, b] = _normal(unit_rng(seed, cfg.cid, lay, b, TAG_VD), (k, Hkv, D), cfg.dtype)
+        qv[b] = _normal(unit_rng(seed, cfg.cid, lay, b, TAG_QV), (k + 1, Hq, D), cfg.dtype)
+        kb[b] = _normal(unit_rng(seed, cfg.cid, lay, b, TAG_KB), (k + 1, Hkv, D), cfg.dtype)
+        vb[b] = _normal(unit_rng(seed, cfg.cid, lay, b, TAG_VB), (k + 1, Hkv, D), cfg.dtype)
+    zt, zd, u, d = _logits(cfg, seed, lay, B, threads)
+    return RoundInputs(qd, kd, vd, qv, kb, vb, zt, zd, u, d)
+

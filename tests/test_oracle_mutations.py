@@ -86,6 +86,14 @@ def _pin_sampling(orc):
     return min(_chi2_run(mod.spec_decide, n=100_000)) > 1e-3
 
 
+def _pin_append(orc):
+    from tests.test_oracle_driver import pin_append_against_generator
+    try:
+        return pin_append_against_generator(orc)
+    except IndexError:  # a slip that writes outside the cache fails the pin too
+        return False
+
+
 MUTANTS = [
     ("budget.py", "frac = -((-s_num * L) // s_den)", "frac = (s_num * L) // s_den", _pin_budget),
     ("budget.py", "return min(L, max(newest, frac))", "return min(L, newest + frac)", _pin_budget),
@@ -99,12 +107,17 @@ MUTANTS = [
     ("attention.py", "np.arange(L, cur, dtype=np.int64)])", "np.arange(L, cur - 1, dtype=np.int64)])", _pin_decode),
     ("sampling.py", "if p >= q or float(u[i]) * q < p:", "if p >= q or float(u[i]) * p < q:", _pin_sampling),
     ("sampling.py", "tokens[k] = invcdf(p_rows[k], u[k])", "tokens[k] = invcdf(p_rows[k - 1], u[k])", _pin_sampling),
+    ("cache.py", "j = int(pos) + t", "j = int(pos) + t + 1", _pin_append),
+    ("cache.py", "k_pages[page, :, j % P, :] = k_rows[t]", "k_pages[page, :, j % P, :] = k_rows[n - 1 - t]", _pin_append),
+    ("cache.py", "v_pages[page, :, j % P, :] = v_rows[t]", "v_pages[page, :, j % P, :] = k_rows[t]", _pin_append),
+    ("cache.py", "page = int(bt_row[j // P])", "page = int(bt_row[j % P])", _pin_append),
 ]
 
 
 def test_unmutated_oracle_passes_pins():
     import oracle
     assert _pin_budget(oracle) and _pin_select(oracle) and _pin_verify(oracle) and _pin_decode(oracle)
+    assert _pin_append(oracle)
 
 
 @pytest.mark.parametrize("case", range(len(MUTANTS)))
