@@ -18,6 +18,8 @@
  *                           probability min(1, p/q), else draw the correction
  *                           from the normalised residual max(0, p - q); a fully
  *                           accepted round adds a bonus token drawn from p.
+ * Rounds are joined on the device by s3r_kv_append (new K/V rows into the
+ * cache) and s3r_commit (lengths and pending token for the next round).
  *
  * Sources (web pages about the method, cited by title and section):
  *   [news]      "Long-context RL training stops waiting on autoregressive
@@ -260,6 +262,62 @@ s3r_status s3r_spec_sample(const float* target_logits, const float* draft_logits
                            int32_t k, int32_t V, float temperature, int32_t* tokens,
                            int32_t* n_out, int8_t* accepted, void* ws, size_t ws_bytes,
                            hipStream_t stream);
+
+/*
+ * Multi-round driving: the two calls that join rounds on the device, so that
+ * rounds follow each other without a host synchronisation (and can be
+ * captured in a HIP graph together with the four calls above).
+ *
+ * s3r_kv_append - write new K/V rows into the paged cache. [explainer],
+ * mechanism paragraph: each draft step reads this round's own positions, so
+ * a draft token's K/V row is cached before the step that reads it; [news],
+ * Interpretation: verification recomputes the block against the complete
+ * cache, so the block's K/V rows replace the draft rows at those positions.
+ *
+ *   k_rows, v_rows device [B][n][num_kv_heads][head_dim] in kv->dtype: row t
+ *             of sequence b is written at position pos[b] + t (all KV heads),
+ *             byte for byte.
+ *   kv        the cache: its k_pages and v_pages are WRITTEN (the descriptor's
+ *             const qualifiers describe the reading calls); block_table must
+ *             map every written position of a sequence to a page no other
+ *             sequence writes in the same call (pages shared by several
+ *             sequences, such as a common prompt prefix, must not be written).
+ *   pos       device i32 [B]: first position of each sequence's rows.
+ *   n         rows per sequence (host, >= 1).
+ *   max_pos   host bound: pos[b] + n <= max_pos <= max_pages_per_seq * 16.
+ *             Rows whose position falls outside [0, max_pages_per_seq * 16)
+ *             are skipped; other device values beyond the bounds are
+ *             undefined behaviour.
+ * No workspace. UNSUPPORTED: page_size != 16, head_dim not 64 or 128.
+ */
+s3r_status s3r_kv_append(const void* k_rows, const void* v_rows, const s3r_paged_kv* kv,
+                         const int32_t* pos, int32_t B, int32_t n, int32_t max_pos, hipStream_t stream);
+
+/*
+ * s3r_commit - close a round on the device. [explainer], Jargon "Block
+ * efficiency (tau)" and the draft/verify illustration: a round outputs the
+ * accepted drafts plus one corrected (or bonus) token, the pending token and
+ * the accepted drafts join the cache, and the last output token is the next
+ * round's pending token. Rows of rejected drafts at and beyond the new length
+ * stay in the cache until the next round overwrites them; nothing reads them
+ * before (the rollback is implicit).
+ *
+ * For each sequence b with 1 <= n_out[b] <= k + 1 (others are left as they
+ * are):
+ *   ctx_len[b] (in/out)  L_b -> L'_b = L_b + n_out[b];
+ *   pending[b]           tokens[b][n_out[b] - 1]                 (or NULL);
+ *   cur_len[(j-1)*B + b] L'_b + j, j = 1..k: the next round's draft steps
+ *                        (one [B] array per step, as s3r_sparse_decode_attn
+ *                        takes them)                             (or NULL);
+ *   seq_len[b]           L'_b + k + 1, the next verification     (or NULL);
+ *   verified[0] (in/out) += sum of n_out over the updated sequences (or NULL).
+ *
+ *   n_out, tokens: as written by s3r_spec_sample (device i32 [B], [B][k+1]).
+ * No workspace; one workgroup.
+ */
+s3r_status s3r_commit(const int32_t* n_out, const int32_t* tokens, int32_t B, int32_t k, int32_t* ctx_len,
+                      int32_t* pending, int32_t* cur_len, int32_t* seq_len, int64_t* verified,
+                      hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -12,6 +12,8 @@ from .s3r import (  # noqa: F401
     S3RError,
     Workspace,
     budget,
+    commit,
+    kv_append,
     lib_path,
     load,
     select,

@@ -178,4 +178,28 @@ s3r_status s3r_spec_sample(const float* target_logits, const float* draft_logits
                                           V, temperature, tokens, n_out, accepted, ws, stream));
 }
 
+s3r_status s3r_kv_append(const void* k_rows, const void* v_rows, const s3r_paged_kv* kv,
+                         const int32_t* pos, int32_t B, int32_t n, int32_t max_pos, hipStream_t stream) {
+  if (!k_rows || !v_rows || !pos || !kv_ok(kv)) return S3R_ERR_INVALID_ARG;
+  if (B < 1 || n < 1 || max_pos < n) return S3R_ERR_INVALID_ARG;
+  if ((long long)kv->max_pages_per_seq * kv->page_size < max_pos) return S3R_ERR_INVALID_ARG;
+  const s3r_status st = kv_supported(kv);
+  if (st != S3R_OK) return st;
+  const int row_bytes = kv->head_dim * (kv->dtype == S3R_BF16 ? 2 : 4);
+  // The descriptor's pointers are const for the reading calls; this one writes the pages.
+  return from_hip(s3r::launch_kv_append(k_rows, v_rows, const_cast<void*>(kv->k_pages),
+                                        const_cast<void*>(kv->v_pages), kv->block_table,
+                                        kv->max_pages_per_seq, pos, B, n, kv->num_kv_heads, row_bytes,
+                                        stream));
+}
+
+s3r_status s3r_commit(const int32_t* n_out, const int32_t* tokens, int32_t B, int32_t k, int32_t* ctx_len,
+                      int32_t* pending, int32_t* cur_len, int32_t* seq_len, int64_t* verified,
+                      hipStream_t stream) {
+  if (!n_out || !tokens || !ctx_len) return S3R_ERR_INVALID_ARG;
+  if (B < 1 || k < 0 || k > kMaxK) return S3R_ERR_INVALID_ARG;
+  return from_hip(s3r::launch_commit(n_out, tokens, B, k, ctx_len, pending, k > 0 ? cur_len : nullptr,
+                                     seq_len, reinterpret_cast<long long*>(verified), stream));
+}
+
 }  // extern "C"

@@ -76,4 +76,10 @@ hipError_t launch_spec_sample(const float* zt, const float* zd, const int* dtok,
                               int B, int k, int V, float temperature, int* tokens, int* n_out,
                               int8_t* accepted, void* ws, hipStream_t stream);
 
+hipError_t launch_kv_append(const void* k_rows, const void* v_rows, void* k_pages, void* v_pages,
+                            const int* bt, int max_pages, const int* pos, int B, int n, int Hkv,
+                            int row_bytes, hipStream_t stream);
+hipError_t launch_commit(const int* n_out, const int* tokens, int B, int k, int* ctx_len, int* pending,
+                         int* cur_len, int* seq_len, long long* verified, hipStream_t stream);
+
 }  // namespace s3r

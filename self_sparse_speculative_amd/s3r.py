@@ -7,8 +7,9 @@ computes any step of the method itself and has no CPU fallback: if the
 library is missing, loading it raises.
 
 The functions mirror the C entry points of include/s3r.h:
-``select``, ``sparse_decode_attn``, ``verify_attn``, ``spec_sample`` plus the
-``budget`` host helper and the ``*_workspace_bytes`` queries.
+``select``, ``sparse_decode_attn``, ``verify_attn``, ``spec_sample``, the
+multi-round ``kv_append`` and ``commit``, plus the ``budget`` host helper and
+the ``*_workspace_bytes`` queries.
 """
 
 import ctypes
@@ -28,7 +29,7 @@ EXPORTED = (
     "s3r_status_string", "s3r_version", "s3r_budget", "s3r_select",
     "s3r_sparse_decode_workspace_bytes", "s3r_sparse_decode_attn",
     "s3r_verify_workspace_bytes", "s3r_verify_attn", "s3r_verify_attn_deferred", "s3r_verify_scores",
-    "s3r_spec_sample_workspace_bytes", "s3r_spec_sample",
+    "s3r_spec_sample_workspace_bytes", "s3r_spec_sample", "s3r_kv_append", "s3r_commit",
 )
 
 
@@ -96,6 +97,10 @@ def load():
         L.s3r_spec_sample_workspace_bytes.argtypes = [i32, i32, i32]
         L.s3r_spec_sample.restype = ctypes.c_int
         L.s3r_spec_sample.argtypes = [vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
+        L.s3r_kv_append.restype = ctypes.c_int
+        L.s3r_kv_append.argtypes = [vp, vp, ctypes.POINTER(PagedKVStruct), vp, i32, i32, i32, vp]
+        L.s3r_commit.restype = ctypes.c_int
+        L.s3r_commit.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, vp, vp]
         _lib = L
         return L
 
@@ -307,3 +312,28 @@ def spec_sample(target_logits, draft_logits, draft_tokens, uniforms, temperature
                              float(temperature), _ptr(tokens), _ptr(n_out), _ptr(accepted), _ptr(buf),
                              buf.numel(), _stream(stream)), "s3r_spec_sample")
     return tokens, n_out, accepted
+
+
+def kv_append(k_rows, v_rows, kv: PagedKV, pos, max_pos, stream=None):
+    """s3r_kv_append. k_rows, v_rows [B][n][Hkv][D] in the cache dtype; pos i32 [B] (device)."""
+    L = load()
+    B, n, hkv, d = k_rows.shape
+    if v_rows.shape != k_rows.shape or k_rows.dtype != kv.k_pages.dtype or v_rows.dtype != kv.k_pages.dtype:
+        raise ValueError("k_rows and v_rows must be [B][n][Hkv][D] in the cache dtype")
+    if hkv != kv.num_kv_heads or d != kv.head_dim:
+        raise ValueError("rows must have the cache's KV heads and head_dim")
+    _check(L.s3r_kv_append(_ptr(k_rows), _ptr(v_rows), ctypes.byref(kv.struct), _ptr(pos), B, n, int(max_pos),
+                           _stream(stream)), "s3r_kv_append")
+
+
+def commit(n_out, tokens, ctx_len, pending=None, cur_len=None, seq_len=None, verified=None, stream=None):
+    """s3r_commit: ctx_len += n_out in place; optional pending [B], cur_len [k][B], seq_len [B],
+    verified int64 [1] (accumulated)."""
+    L = load()
+    B, kp1 = tokens.shape
+    if cur_len is not None and tuple(cur_len.shape) != (kp1 - 1, B):
+        raise ValueError("cur_len must be int32 [k][B]")
+    if verified is not None and verified.dtype != torch.int64:
+        raise ValueError("verified must be int64")
+    _check(L.s3r_commit(_ptr(n_out), _ptr(tokens), B, kp1 - 1, _ptr(ctx_len), _ptr(pending), _ptr(cur_len),
+                        _ptr(seq_len), _ptr(verified), _stream(stream)), "s3r_commit")

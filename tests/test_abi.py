@@ -160,6 +160,29 @@ def test_sample_validation(lib):
     assert f(*args(k=0, zd=None, ws_b=0)) == WORKSPACE
 
 
+def test_kv_append_validation(lib):
+    f = lib.s3r_kv_append
+    args = lambda kvs, n=7, B=4, mp=160, pos=FAKE, kr=FAKE: (kr, FAKE, ctypes.byref(kvs), pos, B, n, mp, None)
+    assert f(*args(_kv(), kr=None)) == INVALID
+    assert f(*args(_kv(), pos=None)) == INVALID
+    assert f(*args(_kv(null=True))) == INVALID
+    assert f(*args(_kv(), n=0)) == INVALID
+    assert f(*args(_kv(), B=0)) == INVALID
+    assert f(*args(_kv(), mp=6)) == INVALID                # max_pos < n
+    assert f(*args(_kv(), mp=161)) == INVALID              # beyond 10 pages x 16
+    assert f(*args(_kv(page=32))) == UNSUPPORTED
+    assert f(*args(_kv(D=96))) == UNSUPPORTED
+
+
+def test_commit_validation(lib):
+    f = lib.s3r_commit
+    assert f(None, FAKE, 4, 6, FAKE, None, None, None, None, None) == INVALID
+    assert f(FAKE, None, 4, 6, FAKE, None, None, None, None, None) == INVALID
+    assert f(FAKE, FAKE, 4, 6, None, None, None, None, None, None) == INVALID
+    assert f(FAKE, FAKE, 0, 6, FAKE, None, None, None, None, None) == INVALID
+    assert f(FAKE, FAKE, 4, 16, FAKE, None, None, None, None, None) == INVALID
+
+
 def test_workspace_queries_reject_bad_shapes(lib):
     assert lib.s3r_verify_workspace_bytes(0, 6, 32, 8, 128, 1, 100) == 0
     assert lib.s3r_verify_workspace_bytes(4, 6, 30, 8, 128, 1, 100) == 0
