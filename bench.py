@@ -52,6 +52,12 @@ def parse():
     ap.add_argument("--overlap-scores", action="store_true",
                     help="verify as s3r_verify_attn_deferred + s3r_verify_scores on a side stream, concurrent "
                          "with sampling (default: one s3r_verify_attn call on the launch stream)")
+    ap.add_argument("--rounds", action="store_true",
+                    help="consecutive rounds through the multi-round driver (K/V append, device-side commit, "
+                         "growing lengths), eager and replayed from one captured HIP graph")
+    ap.add_argument("--cost-model", action="store_true",
+                    help="round cost against dense decoding: dense single-token attention step, draft step and "
+                         "verification timed on the workload, break-even tokens and acceptance, attention speedup")
     ap.add_argument("--copy-gib", type=float, default=2.0,
                     help="size of the device-to-device copy timed as the HBM reference (0 to skip)")
     return ap.parse_args()
@@ -532,6 +538,138 @@ def run_rollout(args, cfg, torch, s3r):
     }
 
 
+def run_rounds(args, cfg, torch, s3r):
+    """warmup + steps consecutive rounds with lengths growing as tokens are committed, all state on the
+    device: eagerly, then (from the same starting state) as replays of one captured round."""
+    from s3r_inputs import make_batch, make_round_inputs
+    from s3r_inputs.gen import make_lengths
+    from self_sparse_speculative_amd.driver import RoundDriver
+
+    k, B = cfg.k, cfg.B
+    total_rounds = args.warmup + args.steps
+    t0 = time.time()
+    L0 = make_lengths(cfg, args.seed).astype(np.int64)
+    # room for every round: the cache holds L0 + total_rounds * (k + 1) positions
+    b = make_batch(cfg, seed=args.seed, lengths=L0 + (total_rounds - 1) * (k + 1), parts=("kv", "scores"))
+    ri = make_round_inputs(cfg, 0, seed=args.seed)
+    max_len = int(L0.max()) + total_rounds * (k + 1)
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def st(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    def fresh():
+        kv = s3r.PagedKV(st(b.k_pages), st(b.v_pages), torch.from_numpy(b.block_table).cuda())
+        drv = RoundDriver(kv, torch.from_numpy(L0.astype(np.int32)).cuda(), torch.from_numpy(b.scores).cuda(), k=k,
+                          Hq=cfg.Hq, V=cfg.V, s_num=cfg.s_num, s_den=cfg.s_den, window=cfg.window,
+                          scale=float(b.scale), temperature=float(b.temperature), max_len=max_len)
+        drv.set_inputs(st(ri.q_draft), st(ri.k_draft), st(ri.v_draft), st(ri.q_verify), st(ri.k_block),
+                       st(ri.v_block), st(ri.zt), st(ri.zd), st(ri.d), st(ri.u))
+        drv.prepare()
+        return drv
+
+    res = {}
+    for mode in ("eager", "graph"):
+        drv = fresh()
+        run = drv.step
+        if mode == "graph":
+            drv.capture()
+            run = drv.replay
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        v0 = int(drv.verified.item())
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        tok = int(drv.verified.item()) - v0
+        res[mode] = {"ms_per_round": round(ms, 4), "verified_tokens": tok,
+                     "verified_tokens_per_s": round(tok / (ms * args.steps * 1e-3), 1),
+                     "final_ctx_len_max": int(drv.ctx_len.max().item())}
+        del drv
+        torch.cuda.empty_cache()
+    assert res["eager"]["verified_tokens"] == res["graph"]["verified_tokens"], res
+    g = res["graph"]
+    return {
+        "metric": "verified tokens/s per draft+verify round; KV-read GB/s as % of HBM peak",
+        "value": g["verified_tokens_per_s"],
+        "unit": "verified tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": g["ms_per_round"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {total_rounds} consecutive rounds from context {cfg.lengths} (lengths grow by "
+                        f"each round's output), B={B}, Hq={cfg.Hq}, Hkv={cfg.Hkv}, head_dim={cfg.D}, {cfg.dtype} paged "
+                        f"KV, s={cfg.s_num}/{cfg.s_den}, window {cfg.window}, k={k}, V={cfg.V}; each round appends the "
+                        f"draft and block K/V rows and commits on the device; the same round inputs every round",
+            "global_batch": B,
+            "seq_len": max_len,
+            "parallelism": "single GPU",
+        },
+        "rounds": res,
+        "graph_speedup": round(res["eager"]["ms_per_round"] / g["ms_per_round"], 4),
+    }
+
+
+def run_cost_model(args, cfg, batch, t, torch, s3r):
+    """The round's attention cost in dense decoding steps on this GPU (break-even and speedup)."""
+    from self_sparse_speculative_amd import cost_model as cm
+
+    r = measure_round(args, cfg, batch, t, s3r, torch)
+    k, B = cfg.k, cfg.B
+    ms = r["breakdown"]["ms"]
+    t_draft = ms["draft_k_steps"] / k
+    t_verify = ms["verify"]
+    # one dense decoding step of attention: the pending token's query over the whole cache
+    # (a block of one row, no scores)
+    q1 = t["q_verify"][:, :1].contiguous()
+    seq1 = (t["ctx_len"] + 1).to(torch.int32)
+    max1 = int(batch.ctx_len.max()) + 1
+    ws = s3r.Workspace()
+    out = torch.empty((B, 1, cfg.Hq, cfg.D), dtype=torch.float32, device="cuda")
+    dense = lambda: s3r.verify_attn(q1, t["kv"], seq1, 0, float(batch.scale), max1, out=out, want_scores=False,
+                                    want_lse=False, ws=ws)
+    for _ in range(3):
+        dense()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        dense()
+    e1.record()
+    torch.cuda.synchronize()
+    t_dense = e0.elapsed_time(e1) / args.steps
+    tau = r["verified"] / B
+    e = 2 if cfg.dtype == "bf16" else 4
+    dense_bytes = int(cfg.Hkv * (batch.ctx_len.astype(np.int64) + 1).sum() * 2 * cfg.D * e)
+    return {
+        "cost_model": cfg.name,
+        "k": k, "s": f"{cfg.s_num}/{cfg.s_den}", "sigma": cfg.noise_std, "B": B,
+        "t_dense_step_ms": round(t_dense, 4),
+        "dense_step_GBs": round(dense_bytes / (t_dense * 1e-3) / 1e9, 1),
+        "t_draft_step_ms": round(t_draft, 4),
+        "t_verify_ms": round(t_verify, 4),
+        "round_attention_ms": round(cm.round_cost(k, t_draft, t_verify), 4),
+        "tokens_per_round": round(tau, 4),
+        "break_even_tokens": round(cm.break_even_tokens(t_dense, k, t_draft, t_verify), 4),
+        "alpha_be": round(cm.break_even_acceptance(t_dense, k, t_draft, t_verify), 4),
+        "attention_speedup": round(cm.speedup(tau, t_dense, k, t_draft, t_verify), 4),
+        "attention_speedup_full_acceptance": round(cm.speedup(k + 1, t_dense, k, t_draft, t_verify), 4),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -560,6 +698,10 @@ def main():
     if args.layers is not None:
         ov["layers"] = args.layers
     cfg = get_config(args.config, **ov)
+    if args.rounds:
+        cfg = get_config(args.config, **{**ov, "layers": 1})
+        print(json.dumps(run_rounds(args, cfg, torch, s3r)))
+        return
     if cfg.layers > 1:
         print(f"[bench] {cfg.name}: {cfg.layers} layers, B={cfg.B}, k={cfg.k}", file=sys.stderr, flush=True)
         print(json.dumps(run_rollout(args, cfg, torch, s3r)))
@@ -570,6 +712,9 @@ def main():
     t = to_dev(batch, s3r, torch)
     print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
+    if args.cost_model:
+        print(json.dumps(run_cost_model(args, cfg, batch, t, torch, s3r)))
+        return
     r = measure_round(args, cfg, batch, t, s3r, torch)
     traffic = load_traffic(os.path.join(ROOT, "self_sparse_speculative_amd", "csrc", "verify.hip"),
                            "rows" if args.overlap_scores else "one_call")

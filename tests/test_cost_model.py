@@ -1,0 +1,61 @@
+"""Pins of the round cost model against the numbers the pages print (CPU only)."""
+
+import json
+import os
+
+import numpy as np
+
+from self_sparse_speculative_amd import cost_model as cm
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_table7_totals_and_break_even():
+    g = json.load(open(os.path.join(GOLDEN, "table7_round_costs_k6.json")))
+    k = g["k"]
+    for row in g["rows"]:
+        t_dense, t_draft, t_verify = cm.from_table_row(row["ar"], row["draft"], row["verify"], k)
+        # the printed total is the round: 6 draft steps plus the verification
+        assert abs(cm.round_cost(k, t_draft, t_verify) - row["total"]) < 0.006, row
+        a = cm.break_even_acceptance(t_dense, k, t_draft, t_verify)
+        if row["alpha_be"] == ">100%":
+            assert a > 1.0, row
+        else:
+            assert round(100 * a, 1) == row["alpha_be"], (row, 100 * a)
+        # at break-even a round is exactly as fast as dense decoding
+        assert abs(cm.speedup(cm.break_even_tokens(t_dense, k, t_draft, t_verify), t_dense, k, t_draft, t_verify)
+                   - 1.0) < 1e-12
+
+
+def test_explainer_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "explainer_round_cost.json")))
+    k = g["k"]
+    assert abs(cm.round_cost(k, g["sparse"], g["verify"]) - g["round_units"]) < 1e-12
+    assert abs(cm.break_even_tokens(g["dense"], k, g["sparse"], g["verify"]) - g["round_units"]) < 1e-12
+    for s in g["speedups"]:
+        got = cm.speedup(s["tokens"], g["dense"], k, g["sparse"], g["verify"])
+        assert round(got, s["decimals"]) == s["speedup"], (s, got)
+    # the measured break-even near 3.8 tokens per round is the B=32, 16K row of Table 7
+    t7 = json.load(open(os.path.join(GOLDEN, "table7_round_costs_k6.json")))
+    row = [r for r in t7["rows"] if r["B"] == g["measured_row"]["B"] and r["S"] == g["measured_row"]["S"]][0]
+    t = cm.from_table_row(row["ar"], row["draft"], row["verify"], k)
+    assert round(cm.break_even_tokens(*t[:1], k, *t[1:]), 1) == g["measured_break_even_tokens"]
+
+
+def test_expected_tokens_closed_form_and_limits():
+    k = 6
+    for a in (0.0, 0.3, 0.8, 0.88, 0.999):
+        assert abs(cm.expected_tokens(a, k) - (1 - a ** (k + 1)) / (1 - a)) < 1e-12
+    assert cm.expected_tokens(1.0, k) == k + 1  # full acceptance: the bonus token too
+    assert cm.expected_tokens(0.0, k) == 1.0   # first draft rejected: the correction only
+    # reference points: 3.95 tokens at alpha 0.8 and 4.93 at 0.88 (k = 6)
+    assert round(cm.expected_tokens(0.8, k), 2) == 3.95 and round(cm.expected_tokens(0.88, k), 2) == 4.93
+
+
+def test_expected_tokens_matches_simulated_rounds():
+    rng = np.random.default_rng(4)
+    k, a, n = 6, 0.7, 200_000
+    acc = rng.random((n, k)) < a
+    first_reject = np.where(acc.all(axis=1), k, acc.argmin(axis=1))
+    tokens = first_reject + 1
+    assert abs(tokens.mean() - cm.expected_tokens(a, k)) < 4 * tokens.std() / np.sqrt(n)

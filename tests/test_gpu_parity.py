@@ -202,12 +202,18 @@ def test_verify_c1_f32():
     _verify_case(cfg, batch, t, range(cfg.B), True)
 
 
+def test_verify_k0_f32_is_one_decoding_step():
+    cfg, batch, t = _batch("c1k0", 1, parts=("kv", "q"), k=0)
+    _verify_case(cfg, batch, t, range(cfg.B), True)
+
+
 @pytest.mark.parametrize("key,cid,ov", [
     ("c2v", 2, {"B": 4}),                       # G=2, 14 rows (one row tile)
     ("c3v", 3, {"B": 3}),                       # G=4, 28 rows (two row tiles)
     ("c5k2", 5, {"B": 2, "k": 2, "lengths": ("uniform", 900, 3000)}),   # 12 rows
     ("c5k8", 5, {"B": 2, "k": 8, "lengths": ("uniform", 900, 3000)}),   # 36 rows (three row tiles)
     ("c3k15", 3, {"B": 2, "k": 15, "lengths": ("uniform", 100, 2100)}),  # 64 rows (four row tiles)
+    ("c5k0", 5, {"B": 3, "k": 0, "lengths": ("uniform", 900, 9000)}),    # k = 0: one dense decoding step
     # long contexts: 16-19 splits per (sequence, KV head)
     ("c3long", 3, {"B": 2, "lengths": ("uniform", 62000, 66000)}),
     ("c3xlong", 3, {"B": 1, "lengths": ("uniform", 75000, 76000)}),
