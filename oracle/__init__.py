@@ -36,3 +36,4 @@ from .attention import attend, gather, sparse_decode, verify, dense_decode  # no
 from .sampling import softmax_t, invcdf, spec_decide, spec_sample  # noqa: F401
 from .round import commit, next_lengths, verified_tokens  # noqa: F401
 from .cache import kv_append  # noqa: F401
+from .select_variants import grouped_count, select_grouped  # noqa: F401

@@ -94,6 +94,26 @@ def _pin_append(orc):
         return False
 
 
+def _pin_pages(orc):
+    from tests.test_oracle_select_variants import _brute_pages, _int_scores
+    rng = np.random.default_rng(2)
+    for L in (17, 200, 777):
+        for (sn, sd, W) in ((1, 20, 64), (1, 5, 1), (1, 2, 30)):
+            sc = _int_scores(rng, 3, L, hi=6)
+            got = orc.select_grouped(sc, L, sn, sd, W, 16, False)
+            for h in range(3):
+                if got[h].tolist() != _brute_pages(sc[h].astype(np.int64), L, sn, sd, W):
+                    return False
+    return True
+
+
+def _pin_all_heads(orc):
+    rng = np.random.default_rng(1)
+    sc = rng.integers(0, 50, size=(8, 333)).astype(np.float32)
+    ref = orc.select(sc.astype(np.int64).sum(axis=0).astype(np.float32), 333, 1, 10, 16)
+    return all(np.array_equal(g, ref) for g in orc.select_grouped(sc, 333, 1, 10, 16, 1, True))
+
+
 MUTANTS = [
     ("budget.py", "frac = -((-s_num * L) // s_den)", "frac = (s_num * L) // s_den", _pin_budget),
     ("budget.py", "return min(L, max(newest, frac))", "return min(L, newest + frac)", _pin_budget),
@@ -111,13 +131,19 @@ MUTANTS = [
     ("cache.py", "k_pages[page, :, j % P, :] = k_rows[t]", "k_pages[page, :, j % P, :] = k_rows[n - 1 - t]", _pin_append),
     ("cache.py", "v_pages[page, :, j % P, :] = v_rows[t]", "v_pages[page, :, j % P, :] = k_rows[t]", _pin_append),
     ("cache.py", "page = int(bt_row[j // P])", "page = int(bt_row[j % P])", _pin_append),
+    ("select_variants.py", "key=lambda p: (-vals[p], p))", "key=lambda p: (-vals[p], -p))", _pin_pages),
+    ("select_variants.py", "n_top = min(f, -(-max(0, n - wc) // unit))", "n_top = min(f, max(0, n - wc) // unit)",
+     _pin_pages),
+    ("select_variants.py", "f = (L - w) // unit", "f = -(-(L - w) // unit)", _pin_pages),
+    ("select_variants.py", "acc = (acc + np.asarray(scores_rows[h][:L], dtype=np.float32)).astype(np.float32)",
+     "acc = np.maximum(acc, np.asarray(scores_rows[h][:L], dtype=np.float32))", _pin_all_heads),
 ]
 
 
 def test_unmutated_oracle_passes_pins():
     import oracle
     assert _pin_budget(oracle) and _pin_select(oracle) and _pin_verify(oracle) and _pin_decode(oracle)
-    assert _pin_append(oracle)
+    assert _pin_append(oracle) and _pin_pages(oracle) and _pin_all_heads(oracle)
 
 
 @pytest.mark.parametrize("case", range(len(MUTANTS)))
