@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--rounds", action="store_true",
                     help="consecutive rounds through the multi-round driver (K/V append, device-side commit, "
                          "growing lengths), eager and replayed from one captured HIP graph")
+    ap.add_argument("--select-unit", type=int, default=1, choices=(1, 16),
+                    help="selection granularity: single positions (1) or whole pages (16)")
+    ap.add_argument("--select-all-heads", action="store_true",
+                    help="one kept set per sequence from the summed scores of its KV heads")
     ap.add_argument("--cost-model", action="store_true",
                     help="round cost against dense decoding: dense single-token attention step, draft step and "
                          "verification timed on the workload, break-even tokens and acceptance, attention speedup")
@@ -150,7 +154,9 @@ def measure_round(args, cfg, batch, t, s3r, torch):
     B, k, Hq, Hkv, D = cfg.B, cfg.k, cfg.Hq, cfg.Hkv, cfg.D
     max_ctx = int(batch.ctx_len.max())
     max_seq = int(batch.seq_len.max())
-    cap = s3r.budget(max_ctx, cfg.s_num, cfg.s_den, cfg.window)
+    plain_select = args.select_unit == 1 and not args.select_all_heads
+    cap = s3r.budget(max_ctx, cfg.s_num, cfg.s_den, cfg.window) if plain_select else \
+        s3r.select_grouped_capacity(max_ctx, cfg.s_num, cfg.s_den, cfg.window, args.select_unit)
     max_attend = cap + k
     scale = float(batch.scale)
     T = float(batch.temperature)
@@ -177,7 +183,11 @@ def measure_round(args, cfg, batch, t, s3r, torch):
     def step(ev=None, sev=None):
         if ev is not None:
             ev[0].record()
-        s3r.select(scores, t["ctx_len"], max_ctx, cfg.s_num, cfg.s_den, cfg.window, idx=idx, n_sel=n_sel)
+        if plain_select:
+            s3r.select(scores, t["ctx_len"], max_ctx, cfg.s_num, cfg.s_den, cfg.window, idx=idx, n_sel=n_sel)
+        else:
+            s3r.select_grouped(scores, t["ctx_len"], max_ctx, cfg.s_num, cfg.s_den, cfg.window,
+                               unit=args.select_unit, all_heads=args.select_all_heads, idx=idx, n_sel=n_sel, ws=ws)
         if ev is not None:
             ev[1].record()
         for j in range(k):
@@ -564,7 +574,8 @@ def run_rounds(args, cfg, torch, s3r):
         kv = s3r.PagedKV(st(b.k_pages), st(b.v_pages), torch.from_numpy(b.block_table).cuda())
         drv = RoundDriver(kv, torch.from_numpy(L0.astype(np.int32)).cuda(), torch.from_numpy(b.scores).cuda(), k=k,
                           Hq=cfg.Hq, V=cfg.V, s_num=cfg.s_num, s_den=cfg.s_den, window=cfg.window,
-                          scale=float(b.scale), temperature=float(b.temperature), max_len=max_len)
+                          scale=float(b.scale), temperature=float(b.temperature), max_len=max_len,
+                          select_unit=args.select_unit, select_all_heads=args.select_all_heads)
         drv.set_inputs(st(ri.q_draft), st(ri.k_draft), st(ri.v_draft), st(ri.q_verify), st(ri.k_block),
                        st(ri.v_block), st(ri.zt), st(ri.zd), st(ri.d), st(ri.u))
         drv.prepare()
@@ -743,7 +754,10 @@ def main():
         "config": {
             "workload": f"{cfg.name}: one attention layer, B={B}, Hq={Hq}, Hkv={Hkv}, head_dim={D}, {cfg.dtype} paged KV "
                         f"(page 16), context {cfg.lengths}, s={cfg.s_num}/{cfg.s_den}, window {cfg.window}, k={k}, "
-                        f"V={cfg.V}, target N(0,{cfg.target_std}), draft noise {cfg.noise_std}, T={cfg.temperature}",
+                        f"V={cfg.V}, target N(0,{cfg.target_std}), draft noise {cfg.noise_std}, T={cfg.temperature}"
+                        + ("" if args.select_unit == 1 and not args.select_all_heads else
+                           f", selection of {'whole pages' if args.select_unit == 16 else 'positions'}"
+                           f"{', one set per sequence from all KV heads' if args.select_all_heads else ''}"),
             "global_batch": B,
             "seq_len": r["max_seq"],
             "parallelism": "single GPU",

@@ -139,6 +139,39 @@ s3r_status s3r_select(const float* scores, int32_t score_stride, const int32_t* 
                       hipStream_t stream);
 
 /*
+ * s3r_select_grouped - selection variants. [explainer], mechanism paragraph:
+ * the drafter reads the newest positions plus the top-scoring pages of the
+ * verifier's last attention pass; [news], Perspective: adaptive context
+ * selection as a direction beyond the reported configuration.
+ *
+ * Arguments as for s3r_select, plus:
+ *   unit      1: single positions (the s3r_select rule);
+ *             16: whole pages. The newest min(window, L) positions are kept as
+ *             whole pages from page f = floor((L - min(window, L)) / 16) on
+ *             (wc = L - 16 f positions); of the f full older pages, the
+ *             min(f, ceil(max(0, n - wc) / 16)) with the largest float32 sum of
+ *             their 16 scores (slot order) are kept, ties to the lower page,
+ *             where n = s3r_budget(L, ...). Every KV head keeps
+ *             n_sel[b] = wc + 16 x (pages kept) positions, ascending.
+ *   all_heads 0: one kept set per KV head; 1: one kept set per sequence,
+ *             chosen on the float32 sum of the KV heads' scores (heads in
+ *             ascending order, before the page sum), written for every KV head.
+ *   nsel_cap  >= s3r_select_grouped_capacity(max_ctx_len, s_num, s_den,
+ *             window, unit) (INVALID_ARG otherwise).
+ *   ws        workspace of s3r_select_grouped_workspace_bytes(...) bytes (none
+ *             for unit 1 with all_heads 0, which is s3r_select).
+ * INVALID_ARG also for unit not in {1, 16}.
+ */
+int32_t s3r_select_grouped_capacity(int32_t max_ctx_len, int32_t s_num, int32_t s_den, int32_t window,
+                                    int32_t unit);
+size_t s3r_select_grouped_workspace_bytes(int32_t B, int32_t Hkv, int32_t max_ctx_len, int32_t s_num,
+                                          int32_t s_den, int32_t window, int32_t unit, int32_t all_heads);
+s3r_status s3r_select_grouped(const float* scores, int32_t score_stride, const int32_t* ctx_len, int32_t B,
+                              int32_t Hkv, int32_t max_ctx_len, int32_t s_num, int32_t s_den, int32_t window,
+                              int32_t unit, int32_t all_heads, int32_t* idx, int32_t nsel_cap, int32_t* n_sel,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * s3r_sparse_decode_attn - one sparse draft step. [news], Interpretation:
  * drafting uses the policy's own weights and attends to the selected KV
  * entries; [explainer], mechanism paragraph: k fast draft steps from the

@@ -17,6 +17,8 @@ from .s3r import (  # noqa: F401
     lib_path,
     load,
     select,
+    select_grouped,
+    select_grouped_capacity,
     sparse_decode_attn,
     sparse_decode_workspace_bytes,
     spec_sample,

@@ -69,6 +69,42 @@ s3r_status s3r_select(const float* scores, int32_t score_stride, const int32_t* 
                                      s_den, window, idx, nsel_cap, n_sel, stream));
 }
 
+int32_t s3r_select_grouped_capacity(int32_t max_ctx_len, int32_t s_num, int32_t s_den, int32_t window,
+                                    int32_t unit) {
+  if (max_ctx_len < 1 || s_den <= 0 || s_num < 0 || s_num > s_den || window < 0) return -1;
+  if (unit != 1 && unit != 16) return -1;
+  return s3r::grouped_select_capacity(max_ctx_len, s_num, s_den, window, unit);
+}
+
+size_t s3r_select_grouped_workspace_bytes(int32_t B, int32_t Hkv, int32_t max_ctx_len, int32_t s_num,
+                                          int32_t s_den, int32_t window, int32_t unit, int32_t all_heads) {
+  if (B < 1 || Hkv < 1 || max_ctx_len < 1 || s_den <= 0 || s_num < 0 || s_num > s_den || window < 0) return 0;
+  if (unit != 1 && unit != 16) return 0;
+  if (unit == 1 && !all_heads) return 0;  // the plain selection needs none
+  return s3r::grouped_select_plan(B, Hkv, max_ctx_len, s_num, s_den, window, unit, all_heads ? 1 : 0).bytes;
+}
+
+s3r_status s3r_select_grouped(const float* scores, int32_t score_stride, const int32_t* ctx_len, int32_t B,
+                              int32_t Hkv, int32_t max_ctx_len, int32_t s_num, int32_t s_den, int32_t window,
+                              int32_t unit, int32_t all_heads, int32_t* idx, int32_t nsel_cap, int32_t* n_sel,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!scores || !ctx_len || !idx || !n_sel) return S3R_ERR_INVALID_ARG;
+  if (B < 1 || Hkv < 1 || max_ctx_len < 1 || B > 65535 || Hkv > 65535) return S3R_ERR_INVALID_ARG;
+  if (s_den <= 0 || s_num < 0 || s_num > s_den || window < 0) return S3R_ERR_INVALID_ARG;
+  if (unit != 1 && unit != 16) return S3R_ERR_INVALID_ARG;
+  if (score_stride < max_ctx_len) return S3R_ERR_INVALID_ARG;
+  if (nsel_cap < 1 || nsel_cap < s3r::grouped_select_capacity(max_ctx_len, s_num, s_den, window, unit))
+    return S3R_ERR_INVALID_ARG;
+  if (unit == 1 && !all_heads)
+    return from_hip(s3r::launch_select(scores, score_stride, ctx_len, B, Hkv, max_ctx_len, s_num, s_den,
+                                       window, idx, nsel_cap, n_sel, stream));
+  const size_t need = s3r::grouped_select_plan(B, Hkv, max_ctx_len, s_num, s_den, window, unit,
+                                               all_heads ? 1 : 0).bytes;
+  if (ws_bytes < need || ws == nullptr) return S3R_ERR_WORKSPACE;
+  return from_hip(s3r::launch_select_grouped(scores, score_stride, ctx_len, B, Hkv, max_ctx_len, s_num, s_den,
+                                             window, unit, all_heads ? 1 : 0, idx, nsel_cap, n_sel, ws, stream));
+}
+
 size_t s3r_sparse_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head_dim, int32_t max_attend) {
   if (B < 1 || Hq < 1 || head_dim < 1 || max_attend < 1) return 0;
   return s3r::decode_workspace_bytes(B, Hq, head_dim, max_attend);

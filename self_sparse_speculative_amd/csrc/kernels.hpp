@@ -76,6 +76,17 @@ hipError_t launch_spec_sample(const float* zt, const float* zd, const int* dtok,
                               int B, int k, int V, float temperature, int* tokens, int* n_out,
                               int8_t* accepted, void* ws, hipStream_t stream);
 
+struct GroupedSelectPlan {
+  int G, kstride, cap_u;
+  size_t off_keys, off_units, off_top, off_wc, off_sel, off_nsel, bytes;
+};
+GroupedSelectPlan grouped_select_plan(int B, int Hkv, int max_ctx_len, int s_num, int s_den, int window,
+                                      int unit, int all_heads);
+int grouped_select_capacity(int max_ctx_len, int s_num, int s_den, int window, int unit);
+hipError_t launch_select_grouped(const float* scores, int stride, const int* ctx_len, int B, int Hkv,
+                                 int max_ctx_len, int s_num, int s_den, int window, int unit, int all_heads,
+                                 int* idx, int nsel_cap, int* n_sel, void* ws, hipStream_t stream);
+
 hipError_t launch_kv_append(const void* k_rows, const void* v_rows, void* k_pages, void* v_pages,
                             const int* bt, int max_pages, const int* pos, int B, int n, int Hkv,
                             int row_bytes, hipStream_t stream);

@@ -99,9 +99,12 @@ __device__ __forceinline__ void find_rank_bucket(const uint32_t* hist, int nbins
   __syncthreads();
 }
 
+// top_count (nullable): keep exactly min(L, top_count[b]) of the L candidates
+// and no window (the page variant passes its candidate pages this way).
 __global__ __launch_bounds__(kFsThreads) void select_stream_kernel(
     const float* __restrict__ scores, int stride, const int* __restrict__ ctx_len, int Hkv,
-    int s_num, int s_den, int window, int* __restrict__ idx, int nsel_cap, int* __restrict__ n_sel) {
+    int s_num, int s_den, int window, int* __restrict__ idx, int nsel_cap, int* __restrict__ n_sel,
+    const int* __restrict__ top_count) {
   __shared__ uint32_t hist[kFsBins];
   __shared__ uint32_t lkey[kFsCap];
   __shared__ int wsum[kFsWaves];
@@ -112,9 +115,15 @@ __global__ __launch_bounds__(kFsThreads) void select_stream_kernel(
   const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int L = ctx_len[b];
-  const int newest = min(window, L);
-  const long long frac = ((long long)s_num * L + s_den - 1) / s_den;
-  const int n = (int)min((long long)L, max((long long)newest, frac));
+  int newest, n;
+  if (top_count != nullptr) {
+    newest = 0;
+    n = min(L, max(0, top_count[b]));
+  } else {
+    newest = min(window, L);
+    const long long frac = ((long long)s_num * L + s_den - 1) / s_den;
+    n = (int)min((long long)L, max((long long)newest, frac));
+  }
   if (kv == 0 && tid == 0) n_sel[b] = n;
   const int ncand = L - newest, ntop = n - newest;
   int* out = idx + ((long long)b * Hkv + kv) * nsel_cap;
@@ -280,7 +289,176 @@ hipError_t launch_select(const float* scores, int stride, const int* ctx_len, in
                          int* n_sel, hipStream_t stream) {
   (void)max_ctx_len;
   hipLaunchKernelGGL(select_stream_kernel, dim3(Hkv, B), dim3(kFsThreads), 0, stream, scores, stride,
-                     ctx_len, Hkv, s_num, s_den, window, idx, nsel_cap, n_sel);
+                     ctx_len, Hkv, s_num, s_den, window, idx, nsel_cap, n_sel, (const int*)nullptr);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Selection variants. [explainer], mechanism paragraph: the drafter reads the
+// newest positions plus the top-scoring pages of the verifier's last pass.
+//   all heads: one kept set per sequence from the float32 sum of its KV heads'
+//              scores (heads in ascending order), copied to every KV head;
+//   pages:     the newest min(window, L) positions are kept as whole pages
+//              from page f = floor((L - min(window, L)) / 16) on (wc = L - 16 f
+//              positions); of the f full older pages, the
+//              min(f, ceil(max(0, n - wc) / 16)) with the largest float32 sum of
+//              their 16 scores (slot order) are kept, ties to the lower page,
+//              n = the position budget. Every KV head keeps wc + 16 x that many.
+// group_keys_kernel forms the summed keys (one thread per position or page,
+// additions in the stated order) and each sequence's plan; the streaming
+// selector picks on the keys; expand_kernel writes the kept positions.
+
+struct PagePlan {
+  int f, wc, ntop;
+};
+
+__device__ __forceinline__ PagePlan page_plan(int L, int s_num, int s_den, int window) {
+  const int w = min(window, L);
+  PagePlan pp;
+  pp.f = (L - w) / kPage;
+  pp.wc = L - pp.f * kPage;
+  const long long frac = ((long long)s_num * L + s_den - 1) / s_den;
+  const int n = (int)min((long long)L, max((long long)w, frac));
+  pp.ntop = min(pp.f, ceil_div(max(0, n - pp.wc), kPage));
+  return pp;
+}
+
+// Lanes per unit: the page sums over all heads use 16 lanes per page (one per
+// position: coalesced reads of every head, then the page sum in slot order
+// through shuffles); one head's page sums use one lane per page (16 reads).
+template <bool PAGES, bool ALL>
+constexpr int group_lanes() { return PAGES && ALL ? kPage : 1; }
+
+template <bool PAGES, bool ALL>
+__global__ __launch_bounds__(256) void group_keys_kernel(
+    const float* __restrict__ scores, int stride, const int* __restrict__ ctx_len, int Hkv, int s_num,
+    int s_den, int window, float* __restrict__ keys, int kstride, int* __restrict__ units,
+    int* __restrict__ top, int* __restrict__ wcount) {
+  constexpr int LPU = group_lanes<PAGES, ALL>();
+  const int b = blockIdx.y, g = blockIdx.z;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int L = ctx_len[b];
+  const PagePlan pp = page_plan(L, s_num, s_den, window);
+  const int nunits = PAGES ? pp.f : L;
+  if (t == 0 && g == 0) {
+    units[b] = nunits;
+    top[b] = pp.ntop;
+    wcount[b] = pp.wc;
+  }
+  const int u = t / LPU;
+  if (u >= nunits) return;  // a unit's lanes leave together
+  const float* row = scores + (size_t)b * Hkv * stride;
+  auto pos_key = [&](int j) {
+    if (!ALL) return row[(size_t)g * stride + j];
+    float a = 0.f;
+    for (int h = 0; h < Hkv; ++h) a += row[(size_t)h * stride + j];
+    return a;
+  };
+  float v;
+  if (!PAGES) {
+    v = pos_key(u);
+  } else if (LPU == 1) {
+    v = 0.f;
+#pragma unroll
+    for (int s = 0; s < kPage; ++s) v += pos_key(u * kPage + s);
+  } else {
+    // candidate pages are full: position t < 16 f
+    const float x = pos_key(t);
+    v = __shfl(x, 0, kPage);
+#pragma unroll
+    for (int s = 1; s < kPage; ++s) v += __shfl(x, s, kPage);
+    if ((t & (kPage - 1)) != 0) return;
+  }
+  keys[((size_t)b * gridDim.z + g) * kstride + u] = v;
+}
+
+template <bool PAGES>
+__global__ __launch_bounds__(256) void expand_kernel(
+    const int* __restrict__ sel_u, int cap_u, int G, const int* __restrict__ n_u, const int* __restrict__ units,
+    const int* __restrict__ wcount, int Hkv, int* __restrict__ idx, int nsel_cap, int* __restrict__ n_sel) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int g = G == 1 ? 0 : h;
+  const int* src = sel_u + ((size_t)b * G + g) * cap_u;
+  const int nt = n_u[b];
+  const int total = PAGES ? nt * kPage + wcount[b] : nt;
+  const int wstart = PAGES ? units[b] * kPage : 0;
+  int* out = idx + ((size_t)b * Hkv + h) * nsel_cap;
+  for (int i = threadIdx.x; i < total; i += 256) {
+    int v;
+    if (!PAGES) v = src[i];
+    else v = i < nt * kPage ? src[i / kPage] * kPage + (i % kPage) : wstart + (i - nt * kPage);
+    out[i] = v;
+  }
+  if (h == 0 && threadIdx.x == 0) n_sel[b] = total;
+}
+
+GroupedSelectPlan grouped_select_plan(int B, int Hkv, int max_ctx_len, int s_num, int s_den, int window,
+                                      int unit, int all_heads) {
+  GroupedSelectPlan p;
+  p.G = all_heads ? 1 : Hkv;
+  const long long w = min(window, max_ctx_len);
+  const long long frac = ((long long)s_num * max_ctx_len + s_den - 1) / s_den;
+  const int n_max = (int)min((long long)max_ctx_len, max(w, frac));
+  p.kstride = unit == 1 ? max_ctx_len : max(1, max_ctx_len / kPage);
+  p.cap_u = unit == 1 ? max(1, n_max) : max(1, ceil_div(n_max, kPage) + 1);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  p.off_keys = take((size_t)B * p.G * p.kstride * sizeof(float));
+  p.off_units = take((size_t)B * sizeof(int));
+  p.off_top = take((size_t)B * sizeof(int));
+  p.off_wc = take((size_t)B * sizeof(int));
+  p.off_sel = take((size_t)B * p.G * p.cap_u * sizeof(int));
+  p.off_nsel = take((size_t)B * sizeof(int));
+  p.bytes = off;
+  return p;
+}
+
+int grouped_select_capacity(int max_ctx_len, int s_num, int s_den, int window, int unit) {
+  const long long w = min(window, max_ctx_len);
+  const long long frac = ((long long)s_num * max_ctx_len + s_den - 1) / s_den;
+  const long long n_max = min((long long)max_ctx_len, max(w, frac));
+  if (unit == 1) return (int)n_max;
+  // at most window + 15 positions of window pages, and whole older pages
+  // rounding the rest of the budget up by at most 15 positions
+  return (int)min((long long)max_ctx_len, max(w + kPage - 1, n_max) + kPage - 1);
+}
+
+hipError_t launch_select_grouped(const float* scores, int stride, const int* ctx_len, int B, int Hkv,
+                                 int max_ctx_len, int s_num, int s_den, int window, int unit, int all_heads,
+                                 int* idx, int nsel_cap, int* n_sel, void* ws, hipStream_t stream) {
+  const GroupedSelectPlan p = grouped_select_plan(B, Hkv, max_ctx_len, s_num, s_den, window, unit, all_heads);
+  char* w = static_cast<char*>(ws);
+  float* keys = reinterpret_cast<float*>(w + p.off_keys);
+  int* units = reinterpret_cast<int*>(w + p.off_units);
+  int* top = reinterpret_cast<int*>(w + p.off_top);
+  int* wc = reinterpret_cast<int*>(w + p.off_wc);
+  int* sel = reinterpret_cast<int*>(w + p.off_sel);
+  int* nsel_u = reinterpret_cast<int*>(w + p.off_nsel);
+  const int lanes = (unit == 16 && all_heads) ? kPage : 1;
+  const dim3 kgrid(ceil_div(p.kstride * lanes, 256), B, p.G);
+  if (unit == 1) {
+    hipLaunchKernelGGL((group_keys_kernel<false, true>), kgrid, dim3(256), 0, stream, scores, stride, ctx_len, Hkv,
+                       s_num, s_den, window, keys, p.kstride, units, top, wc);
+    hipLaunchKernelGGL(select_stream_kernel, dim3(1, B), dim3(kFsThreads), 0, stream, keys, p.kstride, ctx_len, 1,
+                       s_num, s_den, window, sel, p.cap_u, nsel_u, (const int*)nullptr);
+    hipLaunchKernelGGL(expand_kernel<false>, dim3(Hkv, B), dim3(256), 0, stream, sel, p.cap_u, 1, nsel_u, units,
+                       wc, Hkv, idx, nsel_cap, n_sel);
+  } else {
+    if (all_heads)
+      hipLaunchKernelGGL((group_keys_kernel<true, true>), kgrid, dim3(256), 0, stream, scores, stride, ctx_len,
+                         Hkv, s_num, s_den, window, keys, p.kstride, units, top, wc);
+    else
+      hipLaunchKernelGGL((group_keys_kernel<true, false>), kgrid, dim3(256), 0, stream, scores, stride, ctx_len,
+                         Hkv, s_num, s_den, window, keys, p.kstride, units, top, wc);
+    hipLaunchKernelGGL(select_stream_kernel, dim3(p.G, B), dim3(kFsThreads), 0, stream, keys, p.kstride, units, p.G,
+                       s_num, s_den, 0, sel, p.cap_u, nsel_u, (const int*)top);
+    hipLaunchKernelGGL(expand_kernel<true>, dim3(Hkv, B), dim3(256), 0, stream, sel, p.cap_u, p.G, nsel_u, units,
+                       wc, Hkv, idx, nsel_cap, n_sel);
+  }
   return hipGetLastError();
 }
 

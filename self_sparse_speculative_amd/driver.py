@@ -44,7 +44,8 @@ class RoundDriver:
     """
 
     def __init__(self, kv: s3r.PagedKV, ctx_len: torch.Tensor, scores: torch.Tensor, *, k: int, Hq: int, V: int,
-                 s_num: int, s_den: int, window: int, scale: float, temperature: float, max_len: int):
+                 s_num: int, s_den: int, window: int, scale: float, temperature: float, max_len: int,
+                 select_unit: int = 1, select_all_heads: bool = False):
         dev = ctx_len.device
         B = ctx_len.shape[0]
         Hkv, D = kv.num_kv_heads, kv.head_dim
@@ -57,7 +58,10 @@ class RoundDriver:
         self.s_num, self.s_den, self.window = s_num, s_den, window
         self.scale, self.temperature, self.max_len = float(scale), float(temperature), int(max_len)
         i32 = dict(dtype=torch.int32, device=dev)
-        self.cap = max(1, s3r.budget(self.max_len, s_num, s_den, window))
+        self.select_unit, self.select_all_heads = int(select_unit), bool(select_all_heads)
+        self.plain_select = self.select_unit == 1 and not self.select_all_heads
+        self.cap = max(1, s3r.budget(self.max_len, s_num, s_den, window) if self.plain_select else
+                       s3r.select_grouped_capacity(self.max_len, s_num, s_den, window, self.select_unit))
         self.max_attend = self.cap + k
         # lengths of the next round, derived once here; s3r_commit keeps them current
         self.cur_len = torch.stack([ctx_len + j for j in range(1, k + 1)]).to(torch.int32).contiguous() if k > 0 \
@@ -105,8 +109,13 @@ class RoundDriver:
     def step(self):
         """Enqueue one round on the current stream."""
         k, ml = self.k, self.max_len
-        s3r.select(self.scores, self.ctx_len, ml, self.s_num, self.s_den, self.window, idx=self.idx,
-                   n_sel=self.n_sel)
+        if self.plain_select:
+            s3r.select(self.scores, self.ctx_len, ml, self.s_num, self.s_den, self.window, idx=self.idx,
+                       n_sel=self.n_sel)
+        else:
+            s3r.select_grouped(self.scores, self.ctx_len, ml, self.s_num, self.s_den, self.window,
+                               unit=self.select_unit, all_heads=self.select_all_heads, idx=self.idx,
+                               n_sel=self.n_sel, ws=self.ws)
         for j in range(1, k + 1):
             pos = self.ctx_len if j == 1 else self.cur_len[j - 2]
             s3r.kv_append(self.k_draft[j - 1], self.v_draft[j - 1], self.kv, pos, ml)
@@ -124,6 +133,11 @@ class RoundDriver:
     def prepare(self):
         """Allocate the workspace of every call at the run's bounds (nothing is enqueued)."""
         B, k, Hq, D = self.B, self.k, self.Hq, self.D
+        if not self.plain_select:
+            lib = s3r.load()
+            self.ws.get("select", max(1, int(lib.s3r_select_grouped_workspace_bytes(
+                B, self.Hkv, self.max_len, self.s_num, self.s_den, self.window, self.select_unit,
+                int(self.select_all_heads)))))
         self.ws.get("decode", s3r.sparse_decode_workspace_bytes(B, Hq, D, self.max_attend))
         self.ws.get("verify", s3r.verify_workspace_bytes(B, k, Hq, self.Hkv, D, self.kv.dtype_code, self.max_len))
         self.ws.get("sample", s3r.spec_sample_workspace_bytes(B, k, self.V))

@@ -27,6 +27,7 @@ S3R_F32, S3R_BF16 = 0, 1
 
 EXPORTED = (
     "s3r_status_string", "s3r_version", "s3r_budget", "s3r_select",
+    "s3r_select_grouped_capacity", "s3r_select_grouped_workspace_bytes", "s3r_select_grouped",
     "s3r_sparse_decode_workspace_bytes", "s3r_sparse_decode_attn",
     "s3r_verify_workspace_bytes", "s3r_verify_attn", "s3r_verify_attn_deferred", "s3r_verify_scores",
     "s3r_spec_sample_workspace_bytes", "s3r_spec_sample", "s3r_kv_append", "s3r_commit",
@@ -77,6 +78,13 @@ def load():
         L.s3r_budget.argtypes = [i32, i32, i32, i32]
         L.s3r_select.restype = ctypes.c_int
         L.s3r_select.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp, vp]
+        L.s3r_select_grouped_capacity.restype = i32
+        L.s3r_select_grouped_capacity.argtypes = [i32, i32, i32, i32, i32]
+        L.s3r_select_grouped_workspace_bytes.restype = sz
+        L.s3r_select_grouped_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+        L.s3r_select_grouped.restype = ctypes.c_int
+        L.s3r_select_grouped.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, i32, vp, vp, sz,
+                                         vp]
         L.s3r_sparse_decode_workspace_bytes.restype = sz
         L.s3r_sparse_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.s3r_sparse_decode_attn.restype = ctypes.c_int
@@ -201,6 +209,32 @@ def select(scores, ctx_len, max_ctx_len, s_num, s_den, window, idx=None, n_sel=N
         n_sel = torch.empty((B,), dtype=torch.int32, device=scores.device)
     _check(L.s3r_select(_ptr(scores), stride, _ptr(ctx_len), B, Hkv, int(max_ctx_len), int(s_num), int(s_den),
                         int(window), _ptr(idx), int(nsel_cap), _ptr(n_sel), _stream(stream)), "s3r_select")
+    return idx, n_sel
+
+
+def select_grouped_capacity(max_ctx_len, s_num, s_den, window, unit) -> int:
+    return int(load().s3r_select_grouped_capacity(int(max_ctx_len), int(s_num), int(s_den), int(window), int(unit)))
+
+
+def select_grouped(scores, ctx_len, max_ctx_len, s_num, s_den, window, unit=16, all_heads=False, idx=None,
+                   n_sel=None, nsel_cap=None, ws=None, stream=None):
+    """s3r_select_grouped: whole pages (unit 16) and/or one kept set per sequence (all_heads).
+    Returns (idx [B][Hkv][cap], n_sel [B])."""
+    L = load()
+    B, Hkv, stride = scores.shape
+    if nsel_cap is None:
+        nsel_cap = idx.shape[2] if idx is not None else max(1, select_grouped_capacity(max_ctx_len, s_num, s_den,
+                                                                                        window, unit))
+    if idx is None:
+        idx = torch.empty((B, Hkv, nsel_cap), dtype=torch.int32, device=scores.device)
+    if n_sel is None:
+        n_sel = torch.empty((B,), dtype=torch.int32, device=scores.device)
+    nb = int(L.s3r_select_grouped_workspace_bytes(B, Hkv, int(max_ctx_len), int(s_num), int(s_den), int(window),
+                                                  int(unit), int(bool(all_heads))))
+    buf = _ws(ws, scores.device).get("select", max(nb, 1))
+    _check(L.s3r_select_grouped(_ptr(scores), stride, _ptr(ctx_len), B, Hkv, int(max_ctx_len), int(s_num),
+                                int(s_den), int(window), int(unit), int(bool(all_heads)), _ptr(idx), int(nsel_cap),
+                                _ptr(n_sel), _ptr(buf), buf.numel(), _stream(stream)), "s3r_select_grouped")
     return idx, n_sel
 
 

@@ -90,6 +90,27 @@ def test_select_validation(lib):
     assert f(FAKE, 100, FAKE, 2, 2, 100, 1, 20, -1, FAKE, 16, FAKE, None) == INVALID     # window < 0
 
 
+def test_select_grouped_validation_and_capacity(lib):
+    f = lib.s3r_select_grouped
+    ws = lib.s3r_select_grouped_workspace_bytes(2, 2, 100, 1, 20, 16, 16, 0)
+    cap = lib.s3r_select_grouped_capacity(100, 1, 20, 16, 16)
+    args = lambda unit=16, ah=0, cap_=cap, ws_b=ws, stride=100, W=16: (FAKE, stride, FAKE, 2, 2, 100, 1, 20, W, unit,
+                                                                        ah, FAKE, cap_, FAKE, FAKE, ws_b, None)
+    assert f(*args(unit=8)) == INVALID
+    assert f(*args(cap_=cap - 1)) == INVALID
+    assert f(*args(stride=99)) == INVALID
+    assert f(*args(W=-1)) == INVALID
+    assert f(*args(ws_b=ws - 1)) == WORKSPACE
+    assert lib.s3r_select_grouped_workspace_bytes(2, 2, 100, 1, 20, 16, 1, 0) == 0  # plain selection
+    assert lib.s3r_select_grouped_capacity(100, 1, 20, 16, 3) == -1
+    # the capacity covers every context up to the bound
+    for (sn, sd, W) in ((1, 20, 64), (1, 5, 1), (1, 50, 0), (1, 1, 16)):
+        for M in (1, 15, 16, 17, 100, 1000, 5000):
+            c16 = lib.s3r_select_grouped_capacity(M, sn, sd, W, 16)
+            assert c16 >= max(oracle.grouped_count(L, sn, sd, W, 16) for L in range(1, M + 1))
+            assert lib.s3r_select_grouped_capacity(M, sn, sd, W, 1) == oracle.budget(M, sn, sd, W)
+
+
 def test_decode_validation(lib):
     f = lib.s3r_sparse_decode_attn
     kv = _kv()

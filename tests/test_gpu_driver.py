@@ -81,7 +81,7 @@ def test_commit_matches_oracle():
     assert int(ver.item()) == total
 
 
-def _setup(cfg, L0, R):
+def _setup(cfg, L0, R, unit=1, all_heads=False):
     """The cache with room for R rounds, first-round scores, and the driver over it."""
     k = cfg.k
     b = make_batch(cfg, lengths=L0 + (R - 1) * (k + 1), parts=("kv", "scores"))
@@ -90,7 +90,8 @@ def _setup(cfg, L0, R):
     max_len = int(L0.max()) + R * (k + 1)
     assert int(b.seq_len.max()) == max_len
     drv = RoundDriver(t["kv"], ctx, t["scores"], k=k, Hq=cfg.Hq, V=cfg.V, s_num=cfg.s_num, s_den=cfg.s_den,
-                      window=cfg.window, scale=float(b.scale), temperature=float(b.temperature), max_len=max_len)
+                      window=cfg.window, scale=float(b.scale), temperature=float(b.temperature), max_len=max_len,
+                      select_unit=unit, select_all_heads=all_heads)
     return b, drv
 
 
@@ -101,11 +102,12 @@ def _set_round(drv, ri):
                    torch.from_numpy(ri.u).cuda())
 
 
-@pytest.mark.parametrize("cid,B,lo,hi,R", [(1, 2, 480, 512, 4), (2, 3, 300, 700, 3)])
-def test_rounds_match_oracle_loop(cid, B, lo, hi, R):
+@pytest.mark.parametrize("cid,B,lo,hi,R,unit,all_heads", [(1, 2, 480, 512, 4, 1, False), (2, 3, 300, 700, 3, 1, False),
+                                                         (2, 3, 300, 700, 3, 16, True), (1, 2, 480, 512, 3, 16, False)])
+def test_rounds_match_oracle_loop(cid, B, lo, hi, R, unit, all_heads):
     cfg = get_config(cid, B=B)
     L0 = np.random.default_rng(9).integers(lo, hi + 1, size=B).astype(np.int64)
-    b, drv = _setup(cfg, L0, R)
+    b, drv = _setup(cfg, L0, R, unit, all_heads)
     k, bt, scale, T = cfg.k, b.block_table, float(b.scale), b.temperature
     bf16 = cfg.dtype == "bf16"
     kp, vp = b.k_pages.copy(), b.v_pages.copy()
@@ -125,9 +127,9 @@ def test_rounds_match_oracle_loop(cid, B, lo, hi, R):
         cur, seq = drv.cur_len.cpu().numpy(), drv.seq_len.cpu().numpy()
         for s in range(B):
             Ls = int(L[s])
+            refs = oracle.select_grouped(sc_in[s], Ls, cfg.s_num, cfg.s_den, cfg.window, unit, all_heads)
             for h in range(cfg.Hkv):
-                ref = oracle.select(sc_in[s, h], Ls, cfg.s_num, cfg.s_den, cfg.window)
-                assert nsel[s] == len(ref) and np.array_equal(idx[s, h, :nsel[s]], ref)
+                assert nsel[s] == len(refs[h]) and np.array_equal(idx[s, h, :nsel[s]], refs[h])
             for j in range(1, k + 1):
                 oracle.kv_append(kp, vp, bt[s], Ls + j - 1, ri.k_draft[j - 1, s][None], ri.v_draft[j - 1, s][None])
                 o, _ = oracle.sparse_decode(ri.q_draft[j - 1, s], kp, vp, bt[s], idx[s], int(nsel[s]), Ls, Ls + j,
