@@ -19,6 +19,15 @@ Readings (the pages give the table and the example, not the formulas):
 * with an acceptance probability alpha at every position, a round outputs
   1 + alpha + ... + alpha^k tokens on average (the first rejection ends it).
 
+Adaptive draft length ([digest], the section on per-position acceptance:
+acceptance falls along the draft positions, more so for the last ones and
+as training proceeds, and the authors propose shortening the draft horizon
+when late positions degrade, as future work). Reading adopted: estimate the
+acceptance of each draft position given that the earlier ones were
+accepted, from the decisions of recent rounds, and pick the k that maximises
+the speedup above; a round of k drafts then outputs on average
+sum_{i=0..k} prod_{m<i} alpha_m tokens.
+
 Host arithmetic on measured or printed times only; nothing here runs on the
 device.
 """
@@ -52,3 +61,52 @@ def expected_tokens(alpha: float, k: int) -> float:
 def from_table_row(ar_total: float, draft_total: float, verify: float, k: int):
     """Per-step times from a row given as (k+1) dense steps, k draft steps and one verification."""
     return ar_total / (k + 1), draft_total / k, verify
+
+
+def expected_tokens_by_position(alpha_pos, k: int) -> float:
+    """Mean output of a round of k drafts when draft m+1 is accepted with probability alpha_pos[m]
+    given that drafts 1..m were."""
+    total, run = 1.0, 1.0
+    for m in range(k):
+        run *= float(alpha_pos[m])
+        total += run
+    return total
+
+
+def choose_draft_length(alpha_pos, t_dense_step: float, t_draft_step: float, t_verify_of_k, k_max: int,
+                        k_min: int = 1):
+    """The k in [k_min, k_max] with the largest speedup (ties to the shorter horizon).
+
+    t_verify_of_k: verification time for a block of k + 1 rows (a callable or a mapping).
+    Returns (k, {k: speedup})."""
+    tv = t_verify_of_k if callable(t_verify_of_k) else (lambda k: t_verify_of_k[k])
+    gains = {k: speedup(expected_tokens_by_position(alpha_pos, k), t_dense_step, k, t_draft_step, tv(k))
+             for k in range(k_min, k_max + 1)}
+    best = max(gains, key=lambda k: (gains[k], -k))
+    return best, gains
+
+
+class AcceptanceTracker:
+    """Per-position acceptance from the decisions of recent rounds.
+
+    update() takes the accepted array of a round ([B][k], 1 accepted, 0 the first reject,
+    -1 not reached). The estimate of position m is accepted / reached over that round,
+    blended into an exponential moving average (weight `decay` on the past)."""
+
+    def __init__(self, k_max: int, decay: float = 0.8, prior: float = 1.0):
+        self.k_max, self.decay = int(k_max), float(decay)
+        self.alpha = [float(prior)] * self.k_max
+        self.seen = [False] * self.k_max
+
+    def update(self, accepted):
+        import numpy as np
+        a = np.asarray(accepted)
+        for m in range(min(a.shape[1], self.k_max)):
+            col = a[:, m]
+            reached = int((col >= 0).sum())
+            if reached == 0:
+                continue
+            rate = float((col == 1).sum()) / reached
+            self.alpha[m] = rate if not self.seen[m] else self.decay * self.alpha[m] + (1 - self.decay) * rate
+            self.seen[m] = True
+        return list(self.alpha)

@@ -59,3 +59,45 @@ def test_expected_tokens_matches_simulated_rounds():
     first_reject = np.where(acc.all(axis=1), k, acc.argmin(axis=1))
     tokens = first_reject + 1
     assert abs(tokens.mean() - cm.expected_tokens(a, k)) < 4 * tokens.std() / np.sqrt(n)
+
+
+def test_position_profile_reduces_to_constant_acceptance():
+    for a in (0.5, 0.9):
+        for k in range(0, 9):
+            assert abs(cm.expected_tokens_by_position([a] * 8, k) - cm.expected_tokens(a, k)) < 1e-12
+
+
+def test_choose_draft_length_is_the_brute_force_argmax():
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        kmax = int(rng.integers(1, 12))
+        alpha = np.sort(rng.random(kmax))[::-1]  # declining along the draft
+        t_dense, t_draft = 1.0, float(rng.uniform(0.05, 0.5))
+        tv = {k: float(rng.uniform(0.8, 2.0)) + 0.05 * k for k in range(1, kmax + 1)}
+        k, gains = cm.choose_draft_length(alpha, t_dense, t_draft, tv, kmax)
+        # brute force with exact per-round enumeration of the accepted prefix
+        best, best_k = -1.0, None
+        for kk in range(1, kmax + 1):
+            p_prefix = [np.prod(alpha[:i]) * (1 - (alpha[i] if i < kk else 0.0)) for i in range(kk + 1)]
+            tokens = sum((i + 1) * p for i, p in enumerate(p_prefix))
+            g = tokens * t_dense / (kk * t_draft + tv[kk])
+            if g > best + 1e-12:
+                best, best_k = g, kk
+        assert k == best_k and abs(gains[k] - best) < 1e-9
+
+
+def test_degrading_late_positions_shorten_the_horizon():
+    t_dense, t_draft = 2.2, 0.12
+    tv = {k: 2.9 + 0.1 * k for k in range(1, 9)}
+    flat, _ = cm.choose_draft_length([0.9] * 8, t_dense, t_draft, tv, 8)
+    steep, _ = cm.choose_draft_length([0.96, 0.9, 0.8, 0.6, 0.4, 0.25, 0.15, 0.1], t_dense, t_draft, tv, 8)
+    assert steep < flat
+
+
+def test_acceptance_tracker_counts():
+    tr = cm.AcceptanceTracker(4, decay=0.5)
+    acc = np.array([[1, 1, 0, -1], [1, 0, -1, -1], [0, -1, -1, -1], [1, 1, 1, 1]], dtype=np.int8)
+    est = tr.update(acc)
+    assert est[:4] == [3 / 4, 2 / 3, 1 / 2, 1 / 1]
+    est = tr.update(np.array([[0, -1, -1, -1]], dtype=np.int8))
+    assert est[0] == 0.5 * 0.75 and est[1:] == [2 / 3, 1 / 2, 1.0]  # unreached positions keep their estimate
