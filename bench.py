@@ -59,6 +59,9 @@ def parse():
                     help="selection granularity: single positions (1) or whole pages (16)")
     ap.add_argument("--select-all-heads", action="store_true",
                     help="one kept set per sequence from the summed scores of its KV heads")
+    ap.add_argument("--adaptive-k", action="store_true",
+                    help="draft noise rising along the draft: per-position acceptance measured on the GPU, "
+                         "the draft length the cost model picks, and timed rounds at every k up to 8")
     ap.add_argument("--cost-model", action="store_true",
                     help="round cost against dense decoding: dense single-token attention step, draft step and "
                          "verification timed on the workload, break-even tokens and acceptance, attention speedup")
@@ -681,6 +684,93 @@ def run_cost_model(args, cfg, batch, t, torch, s3r):
     }
 
 
+def run_adaptive(args, torch, s3r):
+    """Adaptive draft length on the 24K workload with acceptance falling along the draft: measure the
+    per-position acceptance (GPU sampling at k = 8 under 16 sets of uniforms), time the round's pieces,
+    let the cost model pick k, then time whole rounds at every k (the k = 8 cache and inputs, sliced)."""
+    from types import SimpleNamespace
+
+    from s3r_inputs import get_config, make_batch
+    from s3r_inputs.configs import DEGRADING_NOISE
+    from s3r_inputs.gen import exact_uniform_f32, unit_rng
+    from self_sparse_speculative_amd import cost_model as cm
+
+    kmax = len(DEGRADING_NOISE)
+    cfg8 = get_config(args.config, k=kmax, noise_by_position=DEGRADING_NOISE, layers=1)
+    batch = make_batch(cfg8, seed=args.seed)
+    t8 = to_dev(batch, s3r, torch)
+    B = cfg8.B
+    # per-position acceptance under several uniform sets (the same draft tokens), pooled
+    accs = []
+    for rep in range(16):
+        u = torch.from_numpy(exact_uniform_f32(unit_rng(args.seed, cfg8.cid, 1 << 21, rep, 99), (B, kmax + 1))).cuda()
+        _, _, acc = s3r.spec_sample(t8["zt"], t8["zd"], t8["d"], u, float(batch.temperature))
+        accs.append(acc.cpu().numpy())
+    a_all = np.concatenate(accs)
+    alpha = cm.AcceptanceTracker(kmax).update(a_all)
+    pref = np.where((a_all == 1).all(axis=1), kmax, (a_all != 1).argmax(axis=1))  # accepted prefix per round
+    tokens_k = {k: float((np.minimum(pref, k) + 1).mean()) for k in range(1, kmax + 1)}
+
+    def sliced(k):
+        t = dict(t8)
+        t["q_draft"] = t8["q_draft"][:k]
+        t["q_verify"] = t8["q_verify"][:, :k + 1].contiguous()
+        t["seq_len"] = (t8["ctx_len"] + (k + 1)).to(torch.int32)
+        t["zt"] = t8["zt"][:, :k + 1].contiguous()
+        t["zd"] = t8["zd"][:, :k].contiguous()
+        t["d"] = t8["d"][:, :k].contiguous()
+        t["u"] = t8["u"][:, :k + 1].contiguous()
+        b = SimpleNamespace(ctx_len=batch.ctx_len, seq_len=(batch.ctx_len + k + 1).astype(np.int32),
+                            scale=batch.scale, temperature=batch.temperature)
+        return get_config(args.config, k=k, noise_by_position=DEGRADING_NOISE[:k], layers=1), b, t
+
+    scores0 = t8["scores"].clone()
+    rounds = {}
+    for k in range(1, kmax + 1):
+        cfg, b, t = sliced(k)
+        t["scores"].copy_(scores0)
+        r = measure_round(args, cfg, b, t, s3r, torch)
+        ms = r["breakdown"]["ms"]
+        rounds[k] = {"ms_per_round": round(r["ms_step"], 4), "verify_ms": ms["verify"],
+                     "draft_step_ms": round(ms["draft_k_steps"] / k, 4), "select_ms": ms["select"],
+                     "sample_ms": ms["spec_sample"], "tokens_per_round_measured": round(tokens_k[k], 4),
+                     "verified_tokens_per_s": round(tokens_k[k] * B / (r["ms_step"] * 1e-3), 1)}
+        print(f"[bench] k={k}: {rounds[k]}", file=sys.stderr, flush=True)
+    # dense decoding step (one-row verification, no scores)
+    q1 = t8["q_verify"][:, :1].contiguous()
+    seq1 = (t8["ctx_len"] + 1).to(torch.int32)
+    out = torch.empty((B, 1, cfg8.Hq, cfg8.D), dtype=torch.float32, device="cuda")
+    ws = s3r.Workspace()
+    dense = lambda: s3r.verify_attn(q1, t8["kv"], seq1, 0, float(batch.scale), int(batch.ctx_len.max()) + 1,
+                                    out=out, want_scores=False, want_lse=False, ws=ws)
+    for _ in range(3):
+        dense()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        dense()
+    e1.record()
+    torch.cuda.synchronize()
+    t_dense = e0.elapsed_time(e1) / args.steps
+    t_draft = float(np.mean([rounds[k]["draft_step_ms"] for k in rounds]))
+    # the policy sees the verification plus the per-round overheads (selection, sampling) as the fixed cost
+    t_fixed = {k: rounds[k]["verify_ms"] + rounds[k]["select_ms"] + rounds[k]["sample_ms"] for k in rounds}
+    k_star, gains = cm.choose_draft_length(alpha, t_dense, t_draft, t_fixed, kmax)
+    best_measured = max(rounds, key=lambda k: rounds[k]["verified_tokens_per_s"])
+    return {
+        "adaptive_k": cfg8.name, "B": B, "s": f"{cfg8.s_num}/{cfg8.s_den}",
+        "draft_noise_by_position": list(DEGRADING_NOISE),
+        "acceptance_by_position_measured": [round(a, 4) for a in alpha],
+        "t_dense_step_ms": round(t_dense, 4), "t_draft_step_ms": round(t_draft, 4),
+        "model_speedup_by_k": {k: round(v, 4) for k, v in gains.items()},
+        "k_chosen": k_star, "k_best_measured": best_measured,
+        "tokens_per_s_at_chosen": rounds[k_star]["verified_tokens_per_s"],
+        "tokens_per_s_at_k6": rounds[6]["verified_tokens_per_s"] if 6 in rounds else None,
+        "rounds": rounds,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -695,6 +785,9 @@ def main():
     torch.cuda.set_device(0)
     if args.sweep:
         run_sweep(args, torch, s3r)
+        return
+    if args.adaptive_k:
+        print(json.dumps(run_adaptive(args, torch, s3r)))
         return
     ov = {}
     if args.s:

@@ -11,7 +11,8 @@ Recipe (one independent PCG64 stream per (seed, config, layer, seq, tag)):
   seeded random permutation; in the rollout config the prompt-prefix pages
   of the 8 responses of one prompt are the same physical pages;
 * first-round selector scores ~ U[0, 1) (float32, exact 24-bit values);
-* target logits N(0, target_std) and draft logits = target + N(0, noise_std),
+* target logits N(0, target_std) and draft logits = target + N(0, noise_std)
+  (or a noise level per draft position),
   float32;
 * uniforms u_b,i = (uint32 >> 8) * 2^-24, exact in float32;
 * draft tokens d_b,i are drawn from softmax(zd_b,i / T) by the Gumbel-max
@@ -258,7 +259,11 @@ def _logits(cfg: Config, seed: int, layer: int, B: int, threads: int):
     def do_logits(b):
         zt[b] = np.float32(cfg.target_std) * unit_rng(seed, cfg.cid, layer, b, TAG_ZT).standard_normal((k + 1, V), dtype=np.float32)
         noise = unit_rng(seed, cfg.cid, layer, b, TAG_ZD).standard_normal((k, V), dtype=np.float32)
-        zd[b] = zt[b, :k] + np.float32(cfg.noise_std) * noise
+        if cfg.noise_by_position:
+            sig = np.asarray(cfg.noise_by_position[:k], dtype=np.float32)[:, None]
+            zd[b] = zt[b, :k] + sig * noise
+        else:
+            zd[b] = zt[b, :k] + np.float32(cfg.noise_std) * noise
         u[b] = exact_uniform_f32(unit_rng(seed, cfg.cid, layer, b, TAG_U), (k + 1,))
         rg = unit_rng(seed, cfg.cid, layer, b, TAG_DTOK)
         for i in range(k):
