@@ -51,6 +51,11 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Keeps the loads issued before it where they are in program order (no
+// instruction of its own): software pipelining needs the next step's loads
+// issued early, and the compiler otherwise sinks each load to its first use.
+__device__ __forceinline__ void pin_issued_loads() { asm volatile("" ::: "memory"); }
+
 // Ordered split of [0, n) into `parts` contiguous chunks of `chunk` elements.
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 

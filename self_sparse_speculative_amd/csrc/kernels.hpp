@@ -38,6 +38,10 @@ constexpr bool kVerBalance = S3R_VERIFY_BALANCE != 0;  // equal-size verify spli
 // workgroups share a CU instead of one (36 rows at 24K: 3.90 -> 3.64 ms).
 // At two row tiles the same change spills and is slower (3.39 -> 3.48 ms).
 constexpr bool kVerQLds = S3R_VERIFY_Q_LDS != 0;
+#ifndef S3R_SELECT_SAMPLED
+#define S3R_SELECT_SAMPLED 1
+#endif
+constexpr bool kSelSampled = S3R_SELECT_SAMPLED != 0;  // sampled-threshold path for long rows
 constexpr int kVerChunkGeneric = 256;  // context positions per verify split (generic path)
 constexpr int kSmpChunks = 64;         // vocabulary chunks of the final draw
 

@@ -99,6 +99,181 @@ __device__ __forceinline__ void find_rank_bucket(const uint32_t* hist, int nbins
   __syncthreads();
 }
 
+// ---------------------------------------------------------------------------
+// Sampled-threshold path for long rows (one full pass over the row instead of
+// four). A sample of the keys (runs of 16 consecutive positions spread evenly
+// over the row) gives a key t0 that about 1.45 x the wanted count of keys
+// exceed (20-bit resolution: a 12-bit and an 8-bit histogram of the sample).
+// The margin keeps falling back rare: a single row that falls back sets the
+// launch's critical path.
+// One ordered pass collects every key >= t0 with its position into LDS
+// (position order). If the list holds at least the wanted count and fits,
+// an exact radix select on the list gives the threshold key T and how many
+// keys equal to T are kept, and an ordered scan of the list writes the
+// result; otherwise the row takes the streaming path. Both paths give the
+// same kept set: the rule is exact either way.
+constexpr int kSpMinRow = 2048;  // shorter rows take the streaming path directly
+constexpr int kSpCap = 2560;     // candidate list capacity (keys + positions in LDS)
+constexpr int kSpRun = 16;       // consecutive positions per sample run
+#ifndef S3R_SELECT_SEG
+#define S3R_SELECT_SEG 4
+#endif
+constexpr int kSpSeg = S3R_SELECT_SEG;  // consecutive keys per thread per step of the collecting pass
+
+
+// Exclusive prefix of v over the workgroup, in thread order; *total is the sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int u = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += u;
+  }
+  __syncthreads();  // wsum may still be read by a previous scan
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < kFsWaves; ++w) {
+    const int x = wsum[w];
+    before += w < wave ? x : 0;
+    all += x;
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+__device__ bool sampled_select(const float* __restrict__ row, int ncand, int ntop, int* __restrict__ out,
+                               uint32_t* hist, uint32_t* sp_key, int* sp_pos, int* wsum, int* res) {
+  const int tid = threadIdx.x;
+  // 1. the sample: nrun runs of 16 keys, run i starting at i * stride
+  const int nrun = min(ncand / 128, kSpCap / kSpRun);
+  const int stride = ncand / nrun;
+  const int ns = nrun * kSpRun;
+  for (int t = tid; t < kFsBins; t += kFsThreads) hist[t] = 0u;
+  __syncthreads();
+  constexpr int kSpPerThread = kSpCap / kFsThreads;  // sample keys per thread (all loads issued first)
+  uint32_t skey[kSpPerThread];
+#pragma unroll
+  for (int q = 0; q < kSpPerThread; ++q) {
+    const int s = tid + q * kFsThreads;
+    skey[q] = s < ns ? score_key(row[(s / kSpRun) * stride + (s % kSpRun)]) : 0u;
+  }
+#pragma unroll
+  for (int q = 0; q < kSpPerThread; ++q) {
+    const int s = tid + q * kFsThreads;
+    if (s < ns) {
+      sp_key[s] = skey[q];
+      atomicAdd(&hist[skey[q] >> 20], 1u);
+    }
+  }
+  __syncthreads();
+  // sample rank of t0: 1.45 x the wanted share of the sample, plus 12 (the
+  // list then holds ~1.45 x the wanted count, several standard deviations
+  // from both too few and the capacity at the budgets used here)
+  const long long want = (145LL * ntop * ns + 100LL * ncand - 1) / (100LL * ncand) + 12;
+  if (want >= ns) {
+    __syncthreads();
+    return false;
+  }
+  find_rank_bucket(hist, kFsBins, (int)want, wsum, res);
+  const uint32_t tb = (uint32_t)res[0];
+  const int rin = res[1];
+  for (int t = tid; t < 256; t += kFsThreads) hist[t] = 0u;
+  __syncthreads();
+  for (int s = tid; s < ns; s += kFsThreads) {
+    const uint32_t key = sp_key[s];
+    if ((key >> 20) == tb) atomicAdd(&hist[(key >> 12) & 0xffu], 1u);
+  }
+  __syncthreads();
+  find_rank_bucket(hist, 256, rin, wsum, res);
+  const uint32_t t0 = (tb << 20) | ((uint32_t)res[0] << 12);
+  // 2. ordered collection of the keys >= t0: each thread takes kSpSeg
+  // consecutive positions per step, so thread order is position order
+  int total = 0;
+  for (int base = 0; base < ncand; base += kSpSeg * kFsThreads) {
+    const int j0 = base + kSpSeg * tid;
+    uint32_t kk[kSpSeg];
+#pragma unroll
+    for (int v = 0; v < kSpSeg; ++v) kk[v] = j0 + v < ncand ? score_key(row[j0 + v]) : 0u;
+    int c = 0;
+#pragma unroll
+    for (int v = 0; v < kSpSeg; ++v) c += (j0 + v < ncand && kk[v] >= t0) ? 1 : 0;
+    int chunk_total;
+    int off = total + block_excl_scan(c, wsum, &chunk_total);
+#pragma unroll
+    for (int v = 0; v < kSpSeg; ++v) {
+      if (j0 + v < ncand && kk[v] >= t0) {
+        if (off < kSpCap) {
+          sp_key[off] = kk[v];
+          sp_pos[off] = j0 + v;
+        }
+        ++off;
+      }
+    }
+    total += chunk_total;
+    if (total > kSpCap) break;  // uniform: every thread holds the same total
+  }
+  __syncthreads();
+  if (total > kSpCap || total < ntop) {
+    __syncthreads();
+    return false;
+  }
+  // 3. exact rank select on the list: T and how many keys equal to T are kept
+  uint32_t prefix = 0u, pmask = 0u;
+  int remaining = ntop;
+  const int shifts[3] = {20, 8, 0};
+  const uint32_t widths[3] = {0xfffu, 0xfffu, 0xffu};
+  for (int ps = 0; ps < 3; ++ps) {
+    const int sh = shifts[ps];
+    const int nb = (int)widths[ps] + 1;
+    for (int t = tid; t < nb; t += kFsThreads) hist[t] = 0u;
+    __syncthreads();
+    for (int i = tid; i < total; i += kFsThreads) {
+      const uint32_t key = sp_key[i];
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & widths[ps]], 1u);
+    }
+    __syncthreads();
+    find_rank_bucket(hist, nb, remaining, wsum, res);
+    prefix |= (uint32_t)res[0] << sh;
+    pmask |= widths[ps] << sh;
+    remaining = res[1];
+    if (res[2] == remaining) break;  // the whole bucket is kept
+  }
+  const uint32_t T = prefix;
+  const int need_eq = remaining;
+  // 4. ordered output: the list is in position order; each thread takes a run of entries
+  const int per = ceil_div(total, kFsThreads);
+  const int e0 = min(total, tid * per), e1 = min(total, e0 + per);
+  int ceq = 0;
+  for (int i = e0; i < e1; ++i) ceq += (sp_key[i] & pmask) == T ? 1 : 0;
+  int dummy;
+  int eq_before = block_excl_scan(ceq, wsum, &dummy);
+  int csel = 0;
+  for (int i = e0; i < e1; ++i) {
+    const uint32_t km = sp_key[i] & pmask;
+    if (km > T) {
+      ++csel;
+    } else if (km == T) {
+      csel += eq_before < need_eq ? 1 : 0;
+      ++eq_before;
+    }
+  }
+  int nsel_all;
+  int pos = block_excl_scan(csel, wsum, &nsel_all);
+  eq_before -= ceq;  // back to this thread's first equal key
+  for (int i = e0; i < e1; ++i) {
+    const uint32_t km = sp_key[i] & pmask;
+    bool sel = km > T;
+    if (km == T) {
+      sel = eq_before < need_eq;
+      ++eq_before;
+    }
+    if (sel && pos < ntop) out[pos++] = sp_pos[i];
+  }
+  return true;
+}
+
 // top_count (nullable): keep exactly min(L, top_count[b]) of the L candidates
 // and no window (the page variant passes its candidate pages this way).
 __global__ __launch_bounds__(kFsThreads) void select_stream_kernel(
@@ -106,7 +281,10 @@ __global__ __launch_bounds__(kFsThreads) void select_stream_kernel(
     int s_num, int s_den, int window, int* __restrict__ idx, int nsel_cap, int* __restrict__ n_sel,
     const int* __restrict__ top_count) {
   __shared__ uint32_t hist[kFsBins];
-  __shared__ uint32_t lkey[kFsCap];
+  // the sampled path's candidate keys and positions; the streaming path's
+  // bucket list reuses the key half
+  __shared__ uint32_t cand[2 * kSpCap];
+  uint32_t* lkey = cand;
   __shared__ int wsum[kFsWaves];
   __shared__ int wave_cnt[2][kFsWaves];
   __shared__ int res[3];
@@ -134,6 +312,9 @@ __global__ __launch_bounds__(kFsThreads) void select_stream_kernel(
     return;
   }
   const float* row = scores + ((long long)b * Hkv + kv) * stride;
+  if (kSelSampled && ncand >= kSpMinRow &&
+      sampled_select(row, ncand, ntop, out, hist, cand, reinterpret_cast<int*>(cand + kSpCap), wsum, res))
+    return;
 
   // A. histogram of the top 12 bits
   for (int t = tid; t < kFsBins; t += kFsThreads) hist[t] = 0u;
