@@ -66,7 +66,8 @@ def test_select_matches_oracle(key, cid, ov):
 
 @pytest.mark.parametrize("long_row", [40000, 24000])
 def test_select_edge_cases(long_row):
-    # a 40000-position row takes the streaming kernel, 24000 the register-resident one
+    # long rows take the sampled-threshold path; its fallback (the streaming
+    # passes) on the 3000-key tie bucket
     cfg = get_config(2, B=7, Hkv=2)
     rng = np.random.default_rng(7)
     L = np.array([1, 5, 64, 65, 200, long_row, 1000], dtype=np.int32)  # window 64
@@ -95,6 +96,36 @@ def test_select_edge_cases(long_row):
                 ref = oracle.select(sc[b, kv], int(L[b]), s_num, s_den, cfg.window)
                 assert n_sel[b] == len(ref)
                 assert np.array_equal(idx[b, kv, :n_sel[b]], ref), (s_num, s_den, b, kv)
+
+
+def test_select_sampled_path_falls_back_exactly():
+    """Rows built against the sampled-threshold path: the sample sees only large keys (too few
+    kept keys above its threshold), only small keys (more than the list holds), or nothing but
+    ties. Each row must fall back and still match the oracle."""
+    cfg = get_config(5, B=4, Hkv=2)
+    L = 24576
+    ncand = L - cfg.window
+    nrun = min(ncand // 128, 160)  # the sample the kernel takes: runs of 16 every `stride` positions
+    stride_s = ncand // nrun
+    j = np.arange(L)
+    sampled = (j < nrun * stride_s) & (j % stride_s < 16)
+    rng = np.random.default_rng(12)
+    sc = np.empty((4, 2, L), np.float32)
+    sc[0] = np.where(sampled, 10.0 + rng.random(L), rng.random(L))   # the sample overstates the threshold
+    sc[1] = np.where(sampled, rng.random(L), 10.0 + rng.random(L))   # the sample understates it
+    sc[2] = 0.5                                                       # every key tied
+    sc[3] = rng.random((2, L))                                        # the plain case
+    ctx = np.full(4, L, dtype=np.int32)
+    for s_num, s_den in [(1, 20), (1, 50), (1, 5)]:
+        cap = s3r.budget(L, s_num, s_den, cfg.window)
+        idx, n_sel = s3r.select(torch.from_numpy(sc).cuda(), torch.from_numpy(ctx).cuda(), L, s_num, s_den,
+                                cfg.window, nsel_cap=cap)
+        torch.cuda.synchronize()
+        idx, n_sel = idx.cpu().numpy(), n_sel.cpu().numpy()
+        for b in range(4):
+            for kv in range(2):
+                ref = oracle.select(sc[b, kv], L, s_num, s_den, cfg.window)
+                assert n_sel[b] == len(ref) and np.array_equal(idx[b, kv, :n_sel[b]], ref), (s_num, b, kv)
 
 
 # ----------------------------------------------------------------- draft
