@@ -276,7 +276,12 @@ __global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
   __shared__ float ml_sh[kWaves][2][16];
   __shared__ int rows[kDecChunkMfma];
 
-  const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  // Draft steps alternate the order of the sequences (odd steps from the last),
+  // so a step starts on the rows the previous step read last, which the
+  // Infinity Cache may still hold.
+  const int split = blockIdx.x, kv = blockIdx.y;
+  const int b = (kDecAlternate && ((cur_len[0] - sel_len[0]) & 1)) ? (int)gridDim.z - 1 - (int)blockIdx.z
+                                                                     : (int)blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, g4 = lane >> 4;
   const int ns = n_sel[b], L = sel_len[b], cur = cur_len[b];

@@ -22,6 +22,10 @@ constexpr int kDecChunkMfma = S3R_DRAFT_CHUNK;  // most attended positions per d
 #define S3R_DRAFT_BALANCE 1
 #endif
 constexpr bool kDecBalance = S3R_DRAFT_BALANCE != 0;  // equal-size draft splits
+#ifndef S3R_DRAFT_ALTERNATE
+#define S3R_DRAFT_ALTERNATE 1
+#endif
+constexpr bool kDecAlternate = S3R_DRAFT_ALTERNATE != 0;  // odd draft steps visit the sequences backwards
 #ifndef S3R_VERIFY_CHUNK
 #define S3R_VERIFY_CHUNK 4096
 #endif
