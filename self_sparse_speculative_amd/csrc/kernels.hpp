@@ -26,6 +26,11 @@ constexpr bool kDecBalance = S3R_DRAFT_BALANCE != 0;  // equal-size draft splits
 #define S3R_DRAFT_ALTERNATE 1
 #endif
 constexpr bool kDecAlternate = S3R_DRAFT_ALTERNATE != 0;  // odd draft steps visit the sequences backwards
+#ifndef S3R_VERIFY_FOLLOW_DRAFT
+#define S3R_VERIFY_FOLLOW_DRAFT 1
+#endif
+// the verification starts on the sequences the last draft step read last
+constexpr bool kVerFollowDraft = S3R_VERIFY_FOLLOW_DRAFT != 0;
 #ifndef S3R_VERIFY_CHUNK
 #define S3R_VERIFY_CHUNK 4096
 #endif

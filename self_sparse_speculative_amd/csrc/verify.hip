@@ -79,10 +79,15 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
   __shared__ uint4 q_sh[QL ? NT * 4 * 64 : 1];
 
   // Workgroups are dispatched round-robin over the XCDs; consecutive splits of
-  // one (sequence, KV head) pair go to the same XCD.
+  // one (sequence, KV head) pair go to the same XCD. Draft step j of a round
+  // visits the sequences backwards when j is odd, so after k draft steps the
+  // last sequence was read last when k is even: the pairs are then taken from
+  // the last, and the first workgroups may find their pages in the Infinity
+  // Cache.
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-  const int pair = (local / nsplit) * 8 + xcd, split = local % nsplit;
-  if (pair >= npairs) return;
+  const int pair0 = (local / nsplit) * 8 + xcd, split = local % nsplit;
+  if (pair0 >= npairs) return;
+  const int pair = (kVerFollowDraft && !(k & 1)) ? npairs - 1 - pair0 : pair0;
   const int b = pair / Hkv, kv = pair % Hkv;
   const int S = seq_len[b];
   // `chunk` is the most positions a split holds; each sequence spreads its
