@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kSmpThreads) void row_stats_kernel(
   if ((V & 3) == 0) {
     const float4* z4 = reinterpret_cast<const float4*>(z);
     const int n4 = V >> 2;
-    constexpr int U = 4;  // float4 loads in flight per thread
+    constexpr int U = 8;  // float4 loads in flight per thread
     for (int t0 = tid; t0 < n4; t0 += U * kSmpThreads) {
       float4 vv[U];
 #pragma unroll
