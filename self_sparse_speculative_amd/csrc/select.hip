@@ -13,8 +13,9 @@
 // equal to T are kept; an ordered pass with wave ballots then writes every key
 // above T plus the lowest-position keys equal to T, in position order. The row
 // is re-read from global memory (L2 / Infinity Cache) for each pass, which
-// keeps the LDS footprint small enough for four workgroups per CU. Everything
-// is integer work on the keys, so the result is exact.
+// keeps the LDS footprint small. Long rows first try the sampled-threshold
+// path below (one pass over the row, the rest in LDS). Everything is integer
+// work on the keys, so the result is exact.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -102,24 +103,62 @@ __device__ __forceinline__ void find_rank_bucket(const uint32_t* hist, int nbins
 // ---------------------------------------------------------------------------
 // Sampled-threshold path for long rows (one full pass over the row instead of
 // four). A sample of the keys (runs of 16 consecutive positions spread evenly
-// over the row) gives a key t0 that about 1.45 x the wanted count of keys
-// exceed (20-bit resolution: a 12-bit and an 8-bit histogram of the sample).
-// The margin keeps falling back rare: a single row that falls back sets the
-// launch's critical path.
+// over the row) gives a key t0 (19-bit resolution: an 11-bit and an 8-bit
+// histogram of the sample) at sample rank r + 5 sqrt(r) + 12, r being the wanted count's
+// share of the sample: about five standard deviations of the sample rank
+// above it, so that rows falling back stay rare (a single row that falls back
+// sets the launch's critical path).
 // One ordered pass collects every key >= t0 with its position into LDS
 // (position order). If the list holds at least the wanted count and fits,
 // an exact radix select on the list gives the threshold key T and how many
 // keys equal to T are kept, and an ordered scan of the list writes the
 // result; otherwise the row takes the streaming path. Both paths give the
 // same kept set: the rule is exact either way.
-constexpr int kSpMinRow = 2048;  // shorter rows take the streaming path directly
-constexpr int kSpCap = 2560;     // candidate list capacity (keys + positions in LDS)
-constexpr int kSpRun = 16;       // consecutive positions per sample run
+// The list capacity is a launch argument: the host sizes it (and the dynamic
+// LDS) for the largest row's expected list, so large budgets keep the path.
+// Positions are 16-bit offsets, so rows of more than 65536 candidates take the
+// streaming path.
+constexpr int kSpMinRow = 2048;   // shorter rows take the streaming path directly
+constexpr int kSpMaxRow = 65536;  // longer rows do too (16-bit list positions)
+constexpr int kSpSample = 2560;   // most sample keys
+constexpr int kSpRun = 16;        // consecutive positions per sample run
+constexpr int kSpBins = 2048;     // 11-bit digits
+constexpr int kSpCapMin = 2560;   // list capacity bounds (entries of 6 B)
+constexpr int kSpCapMax = 8192;
 #ifndef S3R_SELECT_SEG
 #define S3R_SELECT_SEG 4
 #endif
 constexpr int kSpSeg = S3R_SELECT_SEG;  // consecutive keys per thread per step of the collecting pass
 
+// Sample rank of t0 for `ntop` wanted keys out of `ncand`, sampling `ns` keys.
+__host__ __device__ __forceinline__ int sampled_want(int ntop, int ncand, int ns) {
+  const float r = (float)ntop * (float)ns / (float)ncand;
+  return (int)ceilf(r + 5.0f * sqrtf(r)) + 12;
+}
+
+__host__ __device__ __forceinline__ int sampled_count(int ncand) {
+  return min(ncand / 128, kSpSample / kSpRun) * kSpRun;
+}
+
+// Dynamic LDS of select_stream_kernel for list capacity `cap`: the streaming
+// path's 12-bit histogram and bucket list, or the sampled path's 11-bit
+// histogram, list keys and 16-bit list positions.
+static inline size_t select_lds_bytes(int cap) {
+  return sizeof(uint32_t) * (size_t)max(kFsBins + kFsCap, kSpBins + cap + cap / 2);
+}
+
+// List capacity for rows of up to ncand_max candidates keeping up to
+// ntop_max: the expected list of the largest row plus four standard
+// deviations (the sample rank of t0 is about binomial), within the bounds.
+static inline int sampled_list_cap(int ncand_max, int ntop_max) {
+  if (ncand_max < kSpMinRow || ntop_max < 1) return kSpCapMin;
+  const int ns = sampled_count(ncand_max);
+  const double want = sampled_want(ntop_max, ncand_max, ns);
+  const double per = (double)ncand_max / ns;
+  const double list = (want + 4.0 * sqrt(want)) * per + 64.0;
+  const int cap = ((int)list + 63) / 64 * 64;
+  return min(kSpCapMax, max(kSpCapMin, cap));
+}
 
 // Exclusive prefix of v over the workgroup, in thread order; *total is the sum.
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
@@ -144,50 +183,41 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
 }
 
 __device__ bool sampled_select(const float* __restrict__ row, int ncand, int ntop, int* __restrict__ out,
-                               uint32_t* hist, uint32_t* sp_key, int* sp_pos, int* wsum, int* res) {
+                               uint32_t* hist, uint32_t* lkey, uint16_t* lpos, int cap, int* wsum, int* res) {
   const int tid = threadIdx.x;
   // 1. the sample: nrun runs of 16 keys, run i starting at i * stride
-  const int nrun = min(ncand / 128, kSpCap / kSpRun);
-  const int stride = ncand / nrun;
-  const int ns = nrun * kSpRun;
-  for (int t = tid; t < kFsBins; t += kFsThreads) hist[t] = 0u;
-  __syncthreads();
-  constexpr int kSpPerThread = kSpCap / kFsThreads;  // sample keys per thread (all loads issued first)
+  const int ns = sampled_count(ncand);
+  const int stride = ncand / (ns / kSpRun);
+  const int want = sampled_want(ntop, ncand, ns);
+  // uniform decisions, taken before any LDS is touched
+  if (want >= ns) return false;
+  if ((long long)want * ncand > (long long)cap * ns) return false;  // the expected list does not fit
+  constexpr int kSpPerThread = kSpSample / kFsThreads;  // sample keys per thread (all loads issued first)
   uint32_t skey[kSpPerThread];
 #pragma unroll
   for (int q = 0; q < kSpPerThread; ++q) {
-    const int s = tid + q * kFsThreads;
-    skey[q] = s < ns ? score_key(row[(s / kSpRun) * stride + (s % kSpRun)]) : 0u;
+    const int i = tid + q * kFsThreads;
+    skey[q] = i < ns ? score_key(row[(i / kSpRun) * stride + (i % kSpRun)]) : 0u;
   }
-#pragma unroll
-  for (int q = 0; q < kSpPerThread; ++q) {
-    const int s = tid + q * kFsThreads;
-    if (s < ns) {
-      sp_key[s] = skey[q];
-      atomicAdd(&hist[skey[q] >> 20], 1u);
-    }
-  }
+  // t0: the 19-bit prefix of the sample key of rank `want` (an 11-bit, then an
+  // 8-bit histogram of the sample)
+  for (int t = tid; t < kSpBins; t += kFsThreads) hist[t] = 0u;
   __syncthreads();
-  // sample rank of t0: 1.45 x the wanted share of the sample, plus 12 (the
-  // list then holds ~1.45 x the wanted count, several standard deviations
-  // from both too few and the capacity at the budgets used here)
-  const long long want = (145LL * ntop * ns + 100LL * ncand - 1) / (100LL * ncand) + 12;
-  if (want >= ns) {
-    __syncthreads();
-    return false;
-  }
-  find_rank_bucket(hist, kFsBins, (int)want, wsum, res);
+#pragma unroll
+  for (int q = 0; q < kSpPerThread; ++q)
+    if (tid + q * kFsThreads < ns) atomicAdd(&hist[skey[q] >> 21], 1u);
+  __syncthreads();
+  find_rank_bucket(hist, kSpBins, want, wsum, res);
   const uint32_t tb = (uint32_t)res[0];
   const int rin = res[1];
   for (int t = tid; t < 256; t += kFsThreads) hist[t] = 0u;
   __syncthreads();
-  for (int s = tid; s < ns; s += kFsThreads) {
-    const uint32_t key = sp_key[s];
-    if ((key >> 20) == tb) atomicAdd(&hist[(key >> 12) & 0xffu], 1u);
-  }
+#pragma unroll
+  for (int q = 0; q < kSpPerThread; ++q)
+    if (tid + q * kFsThreads < ns && (skey[q] >> 21) == tb) atomicAdd(&hist[(skey[q] >> 13) & 0xffu], 1u);
   __syncthreads();
   find_rank_bucket(hist, 256, rin, wsum, res);
-  const uint32_t t0 = (tb << 20) | ((uint32_t)res[0] << 12);
+  const uint32_t t0 = (tb << 21) | ((uint32_t)res[0] << 13);
   // 2. ordered collection of the keys >= t0: each thread takes kSpSeg
   // consecutive positions per step, so thread order is position order
   int total = 0;
@@ -204,33 +234,30 @@ __device__ bool sampled_select(const float* __restrict__ row, int ncand, int nto
 #pragma unroll
     for (int v = 0; v < kSpSeg; ++v) {
       if (j0 + v < ncand && kk[v] >= t0) {
-        if (off < kSpCap) {
-          sp_key[off] = kk[v];
-          sp_pos[off] = j0 + v;
+        if (off < cap) {
+          lkey[off] = kk[v];
+          lpos[off] = (uint16_t)(j0 + v);
         }
         ++off;
       }
     }
     total += chunk_total;
-    if (total > kSpCap) break;  // uniform: every thread holds the same total
+    if (total > cap) break;  // uniform: every thread holds the same total
   }
   __syncthreads();
-  if (total > kSpCap || total < ntop) {
-    __syncthreads();
-    return false;
-  }
+  if (total > cap || total < ntop) return false;
   // 3. exact rank select on the list: T and how many keys equal to T are kept
   uint32_t prefix = 0u, pmask = 0u;
   int remaining = ntop;
-  const int shifts[3] = {20, 8, 0};
-  const uint32_t widths[3] = {0xfffu, 0xfffu, 0xffu};
+  const int shifts[3] = {21, 10, 0};
+  const uint32_t widths[3] = {0x7ffu, 0x7ffu, 0x3ffu};
   for (int ps = 0; ps < 3; ++ps) {
     const int sh = shifts[ps];
     const int nb = (int)widths[ps] + 1;
     for (int t = tid; t < nb; t += kFsThreads) hist[t] = 0u;
     __syncthreads();
     for (int i = tid; i < total; i += kFsThreads) {
-      const uint32_t key = sp_key[i];
+      const uint32_t key = lkey[i];
       if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & widths[ps]], 1u);
     }
     __syncthreads();
@@ -246,12 +273,12 @@ __device__ bool sampled_select(const float* __restrict__ row, int ncand, int nto
   const int per = ceil_div(total, kFsThreads);
   const int e0 = min(total, tid * per), e1 = min(total, e0 + per);
   int ceq = 0;
-  for (int i = e0; i < e1; ++i) ceq += (sp_key[i] & pmask) == T ? 1 : 0;
+  for (int i = e0; i < e1; ++i) ceq += (lkey[i] & pmask) == T ? 1 : 0;
   int dummy;
   int eq_before = block_excl_scan(ceq, wsum, &dummy);
   int csel = 0;
   for (int i = e0; i < e1; ++i) {
-    const uint32_t km = sp_key[i] & pmask;
+    const uint32_t km = lkey[i] & pmask;
     if (km > T) {
       ++csel;
     } else if (km == T) {
@@ -263,13 +290,13 @@ __device__ bool sampled_select(const float* __restrict__ row, int ncand, int nto
   int pos = block_excl_scan(csel, wsum, &nsel_all);
   eq_before -= ceq;  // back to this thread's first equal key
   for (int i = e0; i < e1; ++i) {
-    const uint32_t km = sp_key[i] & pmask;
+    const uint32_t km = lkey[i] & pmask;
     bool sel = km > T;
     if (km == T) {
       sel = eq_before < need_eq;
       ++eq_before;
     }
-    if (sel && pos < ntop) out[pos++] = sp_pos[i];
+    if (sel && pos < ntop) out[pos++] = (int)lpos[i];
   }
   return true;
 }
@@ -279,12 +306,12 @@ __device__ bool sampled_select(const float* __restrict__ row, int ncand, int nto
 __global__ __launch_bounds__(kFsThreads) void select_stream_kernel(
     const float* __restrict__ scores, int stride, const int* __restrict__ ctx_len, int Hkv,
     int s_num, int s_den, int window, int* __restrict__ idx, int nsel_cap, int* __restrict__ n_sel,
-    const int* __restrict__ top_count) {
-  __shared__ uint32_t hist[kFsBins];
-  // the sampled path's candidate keys and positions; the streaming path's
-  // bucket list reuses the key half
-  __shared__ uint32_t cand[2 * kSpCap];
-  uint32_t* lkey = cand;
+    const int* __restrict__ top_count, int sp_cap) {
+  // select_lds_bytes(sp_cap) of dynamic LDS: the streaming path's histogram
+  // and bucket list, or the sampled path's histogram and candidate list
+  extern __shared__ uint32_t lds[];
+  uint32_t* hist = lds;
+  uint32_t* lkey = lds + kFsBins;
   __shared__ int wsum[kFsWaves];
   __shared__ int wave_cnt[2][kFsWaves];
   __shared__ int res[3];
@@ -312,8 +339,9 @@ __global__ __launch_bounds__(kFsThreads) void select_stream_kernel(
     return;
   }
   const float* row = scores + ((long long)b * Hkv + kv) * stride;
-  if (kSelSampled && ncand >= kSpMinRow &&
-      sampled_select(row, ncand, ntop, out, hist, cand, reinterpret_cast<int*>(cand + kSpCap), wsum, res))
+  if (kSelSampled && ncand >= kSpMinRow && ncand <= kSpMaxRow &&
+      sampled_select(row, ncand, ntop, out, lds, lds + kSpBins, reinterpret_cast<uint16_t*>(lds + kSpBins + sp_cap),
+                     sp_cap, wsum, res))
     return;
 
   // A. histogram of the top 12 bits
@@ -468,9 +496,12 @@ __global__ __launch_bounds__(kFsThreads) void select_stream_kernel(
 hipError_t launch_select(const float* scores, int stride, const int* ctx_len, int B, int Hkv,
                          int max_ctx_len, int s_num, int s_den, int window, int* idx, int nsel_cap,
                          int* n_sel, hipStream_t stream) {
-  (void)max_ctx_len;
-  hipLaunchKernelGGL(select_stream_kernel, dim3(Hkv, B), dim3(kFsThreads), 0, stream, scores, stride,
-                     ctx_len, Hkv, s_num, s_den, window, idx, nsel_cap, n_sel, (const int*)nullptr);
+  const int w = min(window, max_ctx_len);
+  const long long frac = ((long long)s_num * max_ctx_len + s_den - 1) / s_den;
+  const int n_max = (int)min((long long)max_ctx_len, max((long long)w, frac));
+  const int cap = sampled_list_cap(max_ctx_len - w, n_max - w);
+  hipLaunchKernelGGL(select_stream_kernel, dim3(Hkv, B), dim3(kFsThreads), select_lds_bytes(cap), stream, scores,
+                     stride, ctx_len, Hkv, s_num, s_den, window, idx, nsel_cap, n_sel, (const int*)nullptr, cap);
   return hipGetLastError();
 }
 
@@ -624,8 +655,10 @@ hipError_t launch_select_grouped(const float* scores, int stride, const int* ctx
   if (unit == 1) {
     hipLaunchKernelGGL((group_keys_kernel<false, true>), kgrid, dim3(256), 0, stream, scores, stride, ctx_len, Hkv,
                        s_num, s_den, window, keys, p.kstride, units, top, wc);
-    hipLaunchKernelGGL(select_stream_kernel, dim3(1, B), dim3(kFsThreads), 0, stream, keys, p.kstride, ctx_len, 1,
-                       s_num, s_den, window, sel, p.cap_u, nsel_u, (const int*)nullptr);
+    const int w = min(window, max_ctx_len);
+    const int cap = sampled_list_cap(max_ctx_len - w, p.cap_u - w);
+    hipLaunchKernelGGL(select_stream_kernel, dim3(1, B), dim3(kFsThreads), select_lds_bytes(cap), stream, keys,
+                       p.kstride, ctx_len, 1, s_num, s_den, window, sel, p.cap_u, nsel_u, (const int*)nullptr, cap);
     hipLaunchKernelGGL(expand_kernel<false>, dim3(Hkv, B), dim3(256), 0, stream, sel, p.cap_u, 1, nsel_u, units,
                        wc, Hkv, idx, nsel_cap, n_sel);
   } else {
@@ -635,8 +668,9 @@ hipError_t launch_select_grouped(const float* scores, int stride, const int* ctx
     else
       hipLaunchKernelGGL((group_keys_kernel<true, false>), kgrid, dim3(256), 0, stream, scores, stride, ctx_len,
                          Hkv, s_num, s_den, window, keys, p.kstride, units, top, wc);
-    hipLaunchKernelGGL(select_stream_kernel, dim3(p.G, B), dim3(kFsThreads), 0, stream, keys, p.kstride, units, p.G,
-                       s_num, s_den, 0, sel, p.cap_u, nsel_u, (const int*)top);
+    const int cap = sampled_list_cap(p.kstride, p.cap_u);
+    hipLaunchKernelGGL(select_stream_kernel, dim3(p.G, B), dim3(kFsThreads), select_lds_bytes(cap), stream, keys,
+                       p.kstride, units, p.G, s_num, s_den, 0, sel, p.cap_u, nsel_u, (const int*)top, cap);
     hipLaunchKernelGGL(expand_kernel<true>, dim3(Hkv, B), dim3(256), 0, stream, sel, p.cap_u, p.G, nsel_u, units,
                        wc, Hkv, idx, nsel_cap, n_sel);
   }

@@ -116,7 +116,7 @@ def test_select_sampled_path_falls_back_exactly():
     sc[2] = 0.5                                                       # every key tied
     sc[3] = rng.random((2, L))                                        # the plain case
     ctx = np.full(4, L, dtype=np.int32)
-    for s_num, s_den in [(1, 20), (1, 50), (1, 5)]:
+    for s_num, s_den in [(1, 20), (1, 50), (1, 10), (1, 5)]:
         cap = s3r.budget(L, s_num, s_den, cfg.window)
         idx, n_sel = s3r.select(torch.from_numpy(sc).cuda(), torch.from_numpy(ctx).cuda(), L, s_num, s_den,
                                 cfg.window, nsel_cap=cap)
@@ -126,6 +126,28 @@ def test_select_sampled_path_falls_back_exactly():
             for kv in range(2):
                 ref = oracle.select(sc[b, kv], L, s_num, s_den, cfg.window)
                 assert n_sel[b] == len(ref) and np.array_equal(idx[b, kv, :n_sel[b]], ref), (s_num, b, kv)
+
+
+def test_select_rows_around_the_sampled_path_limits():
+    """The sampled path holds 16-bit positions and a list sized for the largest row: a row of
+    70000 positions (beyond it), one of exactly 65536 candidates (its last position is 65535),
+    shorter rows, and a budget of 1/5 whose list would outgrow the largest capacity. Every kept
+    set must match the oracle."""
+    window = 64
+    L = np.array([70000, 65536 + window, 65000, 24576, 3000], np.int32)
+    max_l = int(L.max())
+    rng = np.random.default_rng(21)
+    sc = rng.random((len(L), 2, max_l), dtype=np.float32)
+    for s_num, s_den in [(1, 20), (1, 10), (1, 5)]:
+        cap = s3r.budget(max_l, s_num, s_den, window)
+        idx, n_sel = s3r.select(torch.from_numpy(sc).cuda(), torch.from_numpy(L).cuda(), max_l, s_num, s_den,
+                                window, nsel_cap=cap)
+        torch.cuda.synchronize()
+        idx, n_sel = idx.cpu().numpy(), n_sel.cpu().numpy()
+        for b in range(len(L)):
+            for kv in range(2):
+                ref = oracle.select(sc[b, kv], int(L[b]), s_num, s_den, window)
+                assert n_sel[b] == len(ref) and np.array_equal(idx[b, kv, :n_sel[b]], ref), (s_num, s_den, b, kv)
 
 
 # ----------------------------------------------------------------- draft
