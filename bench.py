@@ -168,6 +168,7 @@ def measure_round(args, cfg, batch, t, s3r, torch):
     n_sel = torch.empty((B,), dtype=torch.int32, device="cuda")
     cur = [t["ctx_len"] + j for j in range(1, k + 1)]
     dout = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    order = torch.empty((B,), dtype=torch.int32, device="cuda")  # draft dispatch order, longest first
     dlse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
     vout = torch.empty((B, k + 1, Hq, D), dtype=torch.float32, device="cuda")
     vlse = torch.empty((B, k + 1, Hq), dtype=torch.float32, device="cuda")
@@ -187,15 +188,17 @@ def measure_round(args, cfg, batch, t, s3r, torch):
         if ev is not None:
             ev[0].record()
         if plain_select:
-            s3r.select(scores, t["ctx_len"], max_ctx, cfg.s_num, cfg.s_den, cfg.window, idx=idx, n_sel=n_sel)
+            s3r.select(scores, t["ctx_len"], max_ctx, cfg.s_num, cfg.s_den, cfg.window, idx=idx, n_sel=n_sel,
+                       order=order)
         else:
             s3r.select_grouped(scores, t["ctx_len"], max_ctx, cfg.s_num, cfg.s_den, cfg.window,
-                               unit=args.select_unit, all_heads=args.select_all_heads, idx=idx, n_sel=n_sel, ws=ws)
+                               unit=args.select_unit, all_heads=args.select_all_heads, idx=idx, n_sel=n_sel, ws=ws,
+                               order=order)
         if ev is not None:
             ev[1].record()
         for j in range(k):
             s3r.sparse_decode_attn(t["q_draft"][j], t["kv"], idx, n_sel, t["ctx_len"], cur[j], scale, max_attend,
-                                   out=dout, lse=dlse, ws=ws)
+                                   out=dout, lse=dlse, ws=ws, order=order)
         if ev is not None:
             ev[2].record()
         if not args.overlap_scores:
@@ -414,6 +417,7 @@ def run_rollout(args, cfg, torch, s3r):
     n_sel = [torch.empty((B,), dtype=torch.int32, device="cuda") for _ in range(L_layers)]
     cur = [ctx_len + j for j in range(1, k + 1)]
     dout = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    order = torch.empty((B,), dtype=torch.int32, device="cuda")  # draft dispatch order, longest first
     dlse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
     vout = torch.empty((B, k + 1, Hq, D), dtype=torch.float32, device="cuda")
     vlse = torch.empty((B, k + 1, Hq), dtype=torch.float32, device="cuda")
@@ -425,12 +429,13 @@ def run_rollout(args, cfg, torch, s3r):
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
         rec(0)
         for l, ly in enumerate(layers):
-            s3r.select(ly["scores"], ctx_len, max_ctx, cfg.s_num, cfg.s_den, cfg.window, idx=idx[l], n_sel=n_sel[l])
+            s3r.select(ly["scores"], ctx_len, max_ctx, cfg.s_num, cfg.s_den, cfg.window, idx=idx[l], n_sel=n_sel[l],
+                       order=order if l == 0 else None)
         rec(1)
         for j in range(k):
             for l, ly in enumerate(layers):
                 s3r.sparse_decode_attn(ly["q_draft"][j], ly["kv"], idx[l], n_sel[l], ctx_len, cur[j], scale,
-                                       max_attend, out=dout, lse=dlse, ws=ws)
+                                       max_attend, out=dout, lse=dlse, ws=ws, order=order)
         rec(2)
         for ly in layers:
             s3r.verify_attn(ly["q_verify"], ly["kv"], seq_len, k, scale, max_seq, out=vout, lse=vlse,

@@ -19,7 +19,9 @@
  *                           from the normalised residual max(0, p - q); a fully
  *                           accepted round adds a bonus token drawn from p.
  * Rounds are joined on the device by s3r_kv_append (new K/V rows into the
- * cache) and s3r_commit (lengths and pending token for the next round).
+ * cache) and s3r_commit (lengths and pending token for the next round);
+ * s3r_length_order gives the draft steps a dispatch order for batches of
+ * mixed lengths.
  *
  * Sources (web pages about the method, cited by title and section):
  *   [news]      "Long-context RL training stops waiting on autoregressive
@@ -129,13 +131,15 @@ int32_t s3r_budget(int32_t L, int32_t s_num, int32_t s_den, int32_t window);
  *             top n_sel - window older positions by score, ties to the lower
  *             position). Entries at and beyond n_sel[b] are not written.
  *   n_sel     device i32 [B] output: s3r_budget(L_b, s_num, s_den, window).
+ *   order     device i32 [B] output or NULL: the draft steps' dispatch order,
+ *             as s3r_length_order(ctx_len) writes it (formed by the same launch).
  *   nsel_cap  >= s3r_budget(max_ctx_len, ...) (INVALID_ARG otherwise);
  *   score_stride >= max_ctx_len.
  * No workspace. UNSUPPORTED: none.
  */
 s3r_status s3r_select(const float* scores, int32_t score_stride, const int32_t* ctx_len,
                       int32_t B, int32_t Hkv, int32_t max_ctx_len, int32_t s_num, int32_t s_den,
-                      int32_t window, int32_t* idx, int32_t nsel_cap, int32_t* n_sel,
+                      int32_t window, int32_t* idx, int32_t nsel_cap, int32_t* n_sel, int32_t* order,
                       hipStream_t stream);
 
 /*
@@ -160,6 +164,7 @@ s3r_status s3r_select(const float* scores, int32_t score_stride, const int32_t* 
  *             window, unit) (INVALID_ARG otherwise).
  *   ws        workspace of s3r_select_grouped_workspace_bytes(...) bytes (none
  *             for unit 1 with all_heads 0, which is s3r_select).
+ *   order     as for s3r_select (NULL: not written).
  * INVALID_ARG also for unit not in {1, 16}.
  */
 int32_t s3r_select_grouped_capacity(int32_t max_ctx_len, int32_t s_num, int32_t s_den, int32_t window,
@@ -169,7 +174,7 @@ size_t s3r_select_grouped_workspace_bytes(int32_t B, int32_t Hkv, int32_t max_ct
 s3r_status s3r_select_grouped(const float* scores, int32_t score_stride, const int32_t* ctx_len, int32_t B,
                               int32_t Hkv, int32_t max_ctx_len, int32_t s_num, int32_t s_den, int32_t window,
                               int32_t unit, int32_t all_heads, int32_t* idx, int32_t nsel_cap, int32_t* n_sel,
-                              void* ws, size_t ws_bytes, hipStream_t stream);
+                              int32_t* order, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * s3r_sparse_decode_attn - one sparse draft step. [news], Interpretation:
@@ -189,6 +194,14 @@ s3r_status s3r_select_grouped(const float* scores, int32_t score_stride, const i
  *   sel_len   device i32 [B]: L_b, the context length the selection used.
  *   cur_len   device i32 [B]: L_b + j at draft step j (1..k); K/V of positions
  *             [L_b, cur_len) must already be in the cache.
+ *   order     device i32 [B] or NULL: a permutation of 0..B-1, the order in
+ *             which workgroups take the sequences (NULL: 0..B-1). It changes
+ *             when each sequence is computed, never a result. Entries outside
+ *             [0, B) are skipped (their sequence is not computed); a repeated
+ *             entry computes that sequence twice, identically. s3r_length_order
+ *             writes the order that takes long contexts first, which keeps
+ *             workgroups of similar length together on batches of mixed
+ *             lengths.
  *   max_attend host bound on n_sel[b] + cur_len[b] - sel_len[b] (>= 1).
  *   out       device f32 [B][Hq][head_dim]; lse device f32 [B][Hq] or NULL.
  *   ws        workspace of s3r_sparse_decode_workspace_bytes(B, Hq, head_dim,
@@ -199,9 +212,23 @@ s3r_status s3r_select_grouped(const float* scores, int32_t score_stride, const i
 size_t s3r_sparse_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head_dim, int32_t max_attend);
 s3r_status s3r_sparse_decode_attn(const void* q, const s3r_paged_kv* kv, const int32_t* idx,
                                   int32_t nsel_cap, const int32_t* n_sel, const int32_t* sel_len,
-                                  const int32_t* cur_len, int32_t B, int32_t Hq, float scale,
-                                  int32_t max_attend, float* out, float* lse, void* ws,
+                                  const int32_t* cur_len, const int32_t* order, int32_t B, int32_t Hq,
+                                  float scale, int32_t max_attend, float* out, float* lse, void* ws,
                                   size_t ws_bytes, hipStream_t stream);
+
+/*
+ * s3r_length_order - the dispatch order for s3r_sparse_decode_attn: order[r]
+ * is the sequence of rank r when the sequences are sorted by descending
+ * len[b], ties by ascending b (a stable sort). Not part of the method's
+ * arithmetic: it only arranges when each sequence's workgroups run.
+ * s3r_select forms the same order in its own launch.
+ *
+ *   len    device i32 [B] (e.g. the context lengths L_b of the round);
+ *   order  device i32 [B], written.
+ * INVALID_ARG: null pointers, B < 1 or B > 65535. One kernel; O(B^2) compares
+ * spread over ceil(B / 256) workgroups.
+ */
+s3r_status s3r_length_order(const int32_t* len, int32_t B, int32_t* order, hipStream_t stream);
 
 /*
  * s3r_verify_attn - dense block verification. [news], Interpretation:

@@ -14,6 +14,7 @@ from .s3r import (  # noqa: F401
     budget,
     commit,
     kv_append,
+    length_order,
     lib_path,
     load,
     select,

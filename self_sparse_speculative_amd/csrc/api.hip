@@ -58,7 +58,7 @@ int32_t s3r_budget(int32_t L, int32_t s_num, int32_t s_den, int32_t window) {
 
 s3r_status s3r_select(const float* scores, int32_t score_stride, const int32_t* ctx_len, int32_t B,
                       int32_t Hkv, int32_t max_ctx_len, int32_t s_num, int32_t s_den,
-                      int32_t window, int32_t* idx, int32_t nsel_cap, int32_t* n_sel,
+                      int32_t window, int32_t* idx, int32_t nsel_cap, int32_t* n_sel, int32_t* order,
                       hipStream_t stream) {
   if (!scores || !ctx_len || !idx || !n_sel) return S3R_ERR_INVALID_ARG;
   if (B < 1 || Hkv < 1 || max_ctx_len < 1 || B > 65535 || Hkv > 65535) return S3R_ERR_INVALID_ARG;
@@ -66,7 +66,7 @@ s3r_status s3r_select(const float* scores, int32_t score_stride, const int32_t* 
   if (score_stride < max_ctx_len) return S3R_ERR_INVALID_ARG;
   if (nsel_cap < 1 || nsel_cap < budget_ll(max_ctx_len, s_num, s_den, window)) return S3R_ERR_INVALID_ARG;
   return from_hip(s3r::launch_select(scores, score_stride, ctx_len, B, Hkv, max_ctx_len, s_num,
-                                     s_den, window, idx, nsel_cap, n_sel, stream));
+                                     s_den, window, idx, nsel_cap, n_sel, order, stream));
 }
 
 int32_t s3r_select_grouped_capacity(int32_t max_ctx_len, int32_t s_num, int32_t s_den, int32_t window,
@@ -87,7 +87,7 @@ size_t s3r_select_grouped_workspace_bytes(int32_t B, int32_t Hkv, int32_t max_ct
 s3r_status s3r_select_grouped(const float* scores, int32_t score_stride, const int32_t* ctx_len, int32_t B,
                               int32_t Hkv, int32_t max_ctx_len, int32_t s_num, int32_t s_den, int32_t window,
                               int32_t unit, int32_t all_heads, int32_t* idx, int32_t nsel_cap, int32_t* n_sel,
-                              void* ws, size_t ws_bytes, hipStream_t stream) {
+                              int32_t* order, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!scores || !ctx_len || !idx || !n_sel) return S3R_ERR_INVALID_ARG;
   if (B < 1 || Hkv < 1 || max_ctx_len < 1 || B > 65535 || Hkv > 65535) return S3R_ERR_INVALID_ARG;
   if (s_den <= 0 || s_num < 0 || s_num > s_den || window < 0) return S3R_ERR_INVALID_ARG;
@@ -97,10 +97,14 @@ s3r_status s3r_select_grouped(const float* scores, int32_t score_stride, const i
     return S3R_ERR_INVALID_ARG;
   if (unit == 1 && !all_heads)
     return from_hip(s3r::launch_select(scores, score_stride, ctx_len, B, Hkv, max_ctx_len, s_num, s_den,
-                                       window, idx, nsel_cap, n_sel, stream));
+                                       window, idx, nsel_cap, n_sel, order, stream));
   const size_t need = s3r::grouped_select_plan(B, Hkv, max_ctx_len, s_num, s_den, window, unit,
                                                all_heads ? 1 : 0).bytes;
   if (ws_bytes < need || ws == nullptr) return S3R_ERR_WORKSPACE;
+  if (order != nullptr) {
+    const hipError_t e = s3r::launch_length_order(ctx_len, B, order, stream);
+    if (e != hipSuccess) return from_hip(e);
+  }
   return from_hip(s3r::launch_select_grouped(scores, score_stride, ctx_len, B, Hkv, max_ctx_len, s_num, s_den,
                                              window, unit, all_heads ? 1 : 0, idx, nsel_cap, n_sel, ws, stream));
 }
@@ -110,10 +114,15 @@ size_t s3r_sparse_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head_dim
   return s3r::decode_workspace_bytes(B, Hq, head_dim, max_attend);
 }
 
+s3r_status s3r_length_order(const int32_t* len, int32_t B, int32_t* order, hipStream_t stream) {
+  if (!len || !order || B < 1 || B > 65535) return S3R_ERR_INVALID_ARG;
+  return from_hip(s3r::launch_length_order(len, B, order, stream));
+}
+
 s3r_status s3r_sparse_decode_attn(const void* q, const s3r_paged_kv* kv, const int32_t* idx,
                                   int32_t nsel_cap, const int32_t* n_sel, const int32_t* sel_len,
-                                  const int32_t* cur_len, int32_t B, int32_t Hq, float scale,
-                                  int32_t max_attend, float* out, float* lse, void* ws,
+                                  const int32_t* cur_len, const int32_t* order, int32_t B, int32_t Hq,
+                                  float scale, int32_t max_attend, float* out, float* lse, void* ws,
                                   size_t ws_bytes, hipStream_t stream) {
   if (!q || !kv_ok(kv) || !idx || !n_sel || !sel_len || !cur_len || !out) return S3R_ERR_INVALID_ARG;
   if (B < 1 || Hq < 1 || nsel_cap < 1 || max_attend < 1 || B > 65535) return S3R_ERR_INVALID_ARG;
@@ -128,7 +137,7 @@ s3r_status s3r_sparse_decode_attn(const void* q, const s3r_paged_kv* kv, const i
   if (ws_bytes < need || (need > 0 && ws == nullptr)) return S3R_ERR_WORKSPACE;
   return from_hip(s3r::launch_sparse_decode(kv->dtype, kv->head_dim, G, q, kv->k_pages, kv->v_pages,
                                             kv->block_table, kv->max_pages_per_seq, Hkv, idx,
-                                            nsel_cap, n_sel, sel_len, cur_len, B, scale,
+                                            nsel_cap, n_sel, sel_len, cur_len, order, B, scale,
                                             max_attend, out, lse, ws, stream));
 }
 

@@ -117,12 +117,14 @@ __global__ __launch_bounds__(kDecThreads) void sparse_decode_kernel(
     const T* __restrict__ q, const T* __restrict__ kp, const T* __restrict__ vp,
     const int* __restrict__ bt, int max_pages, int Hkv, const int* __restrict__ idx, int nsel_cap,
     const int* __restrict__ n_sel, const int* __restrict__ sel_len, const int* __restrict__ cur_len,
-    float scale_log2, int chunk, int nsplit, float* __restrict__ part) {
+    const int* __restrict__ order, float scale_log2, int chunk, int nsplit, float* __restrict__ part) {
   constexpr int EPL = D / 16;
   __shared__ float red[kDecThreads / kWave][G][D + 2];
   __shared__ int rows[kDecChunk];  // cache row (page, KV head, slot) of each attended position
 
-  const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, kv = blockIdx.y;
+  const int b = order != nullptr ? order[blockIdx.z] : (int)blockIdx.z;
+  if ((unsigned)b >= gridDim.z) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane & 15;
   const int stream = wave * 4 + (lane >> 4);
@@ -268,20 +270,23 @@ __global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
     const int* __restrict__ bt, int max_pages, int Hkv, int G, const int* __restrict__ idx,
     int nsel_cap, const int* __restrict__ n_sel, const int* __restrict__ sel_len,
-    const int* __restrict__ cur_len, float scale_log2, int chunk, int nsplit, float* __restrict__ part,
-    float* __restrict__ out, float* __restrict__ lse) {
+    const int* __restrict__ cur_len, const int* __restrict__ order, float scale_log2, int chunk, int nsplit,
+    float* __restrict__ part, float* __restrict__ out, float* __restrict__ lse) {
   constexpr int D = 128;
   constexpr int kWaves = kDecThreads / kWave;
   __shared__ __attribute__((aligned(16))) uint16_t vt[kWaves][D * kDvtStride];
   __shared__ float ml_sh[kWaves][2][16];
   __shared__ int rows[kDecChunkMfma];
 
-  // Draft steps alternate the order of the sequences (odd steps from the last),
-  // so a step starts on the rows the previous step read last, which the
-  // Infinity Cache may still hold.
+  // Workgroups take the sequences in `order` (when given: longest first keeps
+  // workgroups of similar length together). Draft steps alternate the
+  // direction (odd steps from the last), so a step starts on the rows the
+  // previous step read last, which the Infinity Cache may still hold.
   const int split = blockIdx.x, kv = blockIdx.y;
-  const int b = (kDecAlternate && ((cur_len[0] - sel_len[0]) & 1)) ? (int)gridDim.z - 1 - (int)blockIdx.z
+  const int z = (kDecAlternate && ((cur_len[0] - sel_len[0]) & 1)) ? (int)gridDim.z - 1 - (int)blockIdx.z
                                                                      : (int)blockIdx.z;
+  const int b = order != nullptr ? order[z] : z;
+  if ((unsigned)b >= gridDim.z) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, g4 = lane >> 4;
   const int ns = n_sel[b], L = sel_len[b], cur = cur_len[b];
@@ -515,12 +520,12 @@ size_t decode_workspace_bytes(int B, int Hq, int D, int max_attend) {
 template <typename T, int D, int G>
 static hipError_t launch_decode_t(const void* q, const void* kp, const void* vp, const int* bt,
                                   int max_pages, int Hkv, const int* idx, int nsel_cap,
-                                  const int* n_sel, const int* sel_len, const int* cur_len, int B,
-                                  float scale_log2, int nsplit, float* part, float* out, float* lse,
-                                  hipStream_t stream) {
+                                  const int* n_sel, const int* sel_len, const int* cur_len,
+                                  const int* order, int B, float scale_log2, int nsplit, float* part,
+                                  float* out, float* lse, hipStream_t stream) {
   hipLaunchKernelGGL((sparse_decode_kernel<T, D, G>), dim3(nsplit, Hkv, B), dim3(kDecThreads), 0,
                      stream, (const T*)q, (const T*)kp, (const T*)vp, bt, max_pages, Hkv, idx,
-                     nsel_cap, n_sel, sel_len, cur_len, scale_log2, kDecChunk, nsplit, part);
+                     nsel_cap, n_sel, sel_len, cur_len, order, scale_log2, kDecChunk, nsplit, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(Hkv * G, B), dim3(D), 0, stream, part, n_sel,
@@ -532,13 +537,13 @@ template <typename T, int D>
 static hipError_t launch_decode_d(int G, const void* q, const void* kp, const void* vp,
                                   const int* bt, int max_pages, int Hkv, const int* idx,
                                   int nsel_cap, const int* n_sel, const int* sel_len,
-                                  const int* cur_len, int B, float scale_log2, int nsplit,
-                                  float* part, float* out, float* lse, hipStream_t stream) {
+                                  const int* cur_len, const int* order, int B, float scale_log2,
+                                  int nsplit, float* part, float* out, float* lse, hipStream_t stream) {
 #define S3R_DEC_CASE(GG)                                                                       \
   case GG:                                                                                     \
     return launch_decode_t<T, D, GG>(q, kp, vp, bt, max_pages, Hkv, idx, nsel_cap, n_sel,      \
-                                     sel_len, cur_len, B, scale_log2, nsplit, part, out, lse, \
-                                     stream);
+                                     sel_len, cur_len, order, B, scale_log2, nsplit, part, out, \
+                                     lse, stream);
   switch (G) {
     S3R_DEC_CASE(1)
     S3R_DEC_CASE(2)
@@ -558,8 +563,8 @@ bool decode_supported(int dtype, int D, int G) {
 hipError_t launch_sparse_decode(int dtype, int D, int G, const void* q, const void* kp,
                                 const void* vp, const int* bt, int max_pages, int Hkv,
                                 const int* idx, int nsel_cap, const int* n_sel, const int* sel_len,
-                                const int* cur_len, int B, float scale, int max_attend, float* out,
-                                float* lse, void* ws, hipStream_t stream) {
+                                const int* cur_len, const int* order, int B, float scale, int max_attend,
+                                float* out, float* lse, void* ws, hipStream_t stream) {
   const int nsplit = decode_nsplit(dtype, D, max_attend);
   const float sl2 = scale * kLog2e;
   float* part = (float*)ws;
@@ -572,7 +577,7 @@ hipError_t launch_sparse_decode(int dtype, int D, int G, const void* q, const vo
     const int chunk = kDecBalance ? ceil_div(ceil_div(att, ns), kDsub) * kDsub : kDecChunkMfma;
     hipLaunchKernelGGL(sparse_decode_mfma_kernel, dim3(ns, Hkv, B), dim3(kDecThreads), 0, stream,
                        (const bf16_t*)q, (const bf16_t*)kp, (const bf16_t*)vp, bt, max_pages, Hkv, G, idx,
-                       nsel_cap, n_sel, sel_len, cur_len, sl2, chunk, ns, part, out, lse);
+                       nsel_cap, n_sel, sel_len, cur_len, order, sl2, chunk, ns, part, out, lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;  // one split writes the output itself
     hipLaunchKernelGGL((decode_combine_kernel<128>), dim3(Hkv * G, B), dim3(128), 0, stream, part, n_sel,
@@ -582,15 +587,15 @@ hipError_t launch_sparse_decode(int dtype, int D, int G, const void* q, const vo
   if (dtype == 1) {
     if (D == 128)
       return launch_decode_d<bf16_t, 128>(G, q, kp, vp, bt, max_pages, Hkv, idx, nsel_cap, n_sel,
-                                          sel_len, cur_len, B, sl2, nsplit, part, out, lse, stream);
+                                          sel_len, cur_len, order, B, sl2, nsplit, part, out, lse, stream);
     return launch_decode_d<bf16_t, 64>(G, q, kp, vp, bt, max_pages, Hkv, idx, nsel_cap, n_sel,
-                                       sel_len, cur_len, B, sl2, nsplit, part, out, lse, stream);
+                                       sel_len, cur_len, order, B, sl2, nsplit, part, out, lse, stream);
   }
   if (D == 128)
     return launch_decode_d<float, 128>(G, q, kp, vp, bt, max_pages, Hkv, idx, nsel_cap, n_sel,
-                                       sel_len, cur_len, B, sl2, nsplit, part, out, lse, stream);
+                                       sel_len, cur_len, order, B, sl2, nsplit, part, out, lse, stream);
   return launch_decode_d<float, 64>(G, q, kp, vp, bt, max_pages, Hkv, idx, nsel_cap, n_sel,
-                                    sel_len, cur_len, B, sl2, nsplit, part, out, lse, stream);
+                                    sel_len, cur_len, order, B, sl2, nsplit, part, out, lse, stream);
 }
 
 }  // namespace s3r

@@ -56,15 +56,16 @@ constexpr int kSmpChunks = 64;         // vocabulary chunks of the final draw
 
 hipError_t launch_select(const float* scores, int stride, const int* ctx_len, int B, int Hkv,
                          int max_ctx_len, int s_num, int s_den, int window, int* idx, int nsel_cap,
-                         int* n_sel, hipStream_t stream);
+                         int* n_sel, int* order, hipStream_t stream);
 
 bool decode_supported(int dtype, int D, int G);
 size_t decode_workspace_bytes(int B, int Hq, int D, int max_attend);
 hipError_t launch_sparse_decode(int dtype, int D, int G, const void* q, const void* kp,
                                 const void* vp, const int* bt, int max_pages, int Hkv,
                                 const int* idx, int nsel_cap, const int* n_sel, const int* sel_len,
-                                const int* cur_len, int B, float scale, int max_attend, float* out,
-                                float* lse, void* ws, hipStream_t stream);
+                                const int* cur_len, const int* order, int B, float scale, int max_attend,
+                                float* out, float* lse, void* ws, hipStream_t stream);
+hipError_t launch_length_order(const int* len, int B, int* order, hipStream_t stream);
 
 struct VerifyPlan {
   int G, R, NT, RP, chunk, nsplit, ntile_cap;

@@ -306,7 +306,7 @@ __device__ bool sampled_select(const float* __restrict__ row, int ncand, int nto
 __global__ __launch_bounds__(kFsThreads) void select_stream_kernel(
     const float* __restrict__ scores, int stride, const int* __restrict__ ctx_len, int Hkv,
     int s_num, int s_den, int window, int* __restrict__ idx, int nsel_cap, int* __restrict__ n_sel,
-    const int* __restrict__ top_count, int sp_cap) {
+    const int* __restrict__ top_count, int sp_cap, int* __restrict__ order) {
   // select_lds_bytes(sp_cap) of dynamic LDS: the streaming path's histogram
   // and bucket list, or the sampled path's histogram and candidate list
   extern __shared__ uint32_t lds[];
@@ -330,6 +330,19 @@ __global__ __launch_bounds__(kFsThreads) void select_stream_kernel(
     n = (int)min((long long)L, max((long long)newest, frac));
   }
   if (kv == 0 && tid == 0) n_sel[b] = n;
+  if (order != nullptr && kv == 0) {
+    // the draft steps' dispatch order: rank of this sequence among all by
+    // descending length, ties by index (a stable sort)
+    const int B = gridDim.y;
+    int c = 0;
+    for (int j = tid; j < B; j += kFsThreads) {
+      const int lj = ctx_len[j];
+      c += (lj > L || (lj == L && j < b)) ? 1 : 0;
+    }
+    int rank;
+    block_excl_scan(c, wsum, &rank);
+    if (tid == 0) order[rank] = b;
+  }
   const int ncand = L - newest, ntop = n - newest;
   int* out = idx + ((long long)b * Hkv + kv) * nsel_cap;
   for (int t = tid; t < newest; t += kFsThreads) out[ntop + t] = ncand + t;
@@ -495,13 +508,14 @@ __global__ __launch_bounds__(kFsThreads) void select_stream_kernel(
 
 hipError_t launch_select(const float* scores, int stride, const int* ctx_len, int B, int Hkv,
                          int max_ctx_len, int s_num, int s_den, int window, int* idx, int nsel_cap,
-                         int* n_sel, hipStream_t stream) {
+                         int* n_sel, int* order, hipStream_t stream) {
   const int w = min(window, max_ctx_len);
   const long long frac = ((long long)s_num * max_ctx_len + s_den - 1) / s_den;
   const int n_max = (int)min((long long)max_ctx_len, max((long long)w, frac));
   const int cap = sampled_list_cap(max_ctx_len - w, n_max - w);
   hipLaunchKernelGGL(select_stream_kernel, dim3(Hkv, B), dim3(kFsThreads), select_lds_bytes(cap), stream, scores,
-                     stride, ctx_len, Hkv, s_num, s_den, window, idx, nsel_cap, n_sel, (const int*)nullptr, cap);
+                     stride, ctx_len, Hkv, s_num, s_den, window, idx, nsel_cap, n_sel, (const int*)nullptr, cap,
+                     order);
   return hipGetLastError();
 }
 
@@ -658,7 +672,8 @@ hipError_t launch_select_grouped(const float* scores, int stride, const int* ctx
     const int w = min(window, max_ctx_len);
     const int cap = sampled_list_cap(max_ctx_len - w, p.cap_u - w);
     hipLaunchKernelGGL(select_stream_kernel, dim3(1, B), dim3(kFsThreads), select_lds_bytes(cap), stream, keys,
-                       p.kstride, ctx_len, 1, s_num, s_den, window, sel, p.cap_u, nsel_u, (const int*)nullptr, cap);
+                       p.kstride, ctx_len, 1, s_num, s_den, window, sel, p.cap_u, nsel_u, (const int*)nullptr, cap,
+                       (int*)nullptr);
     hipLaunchKernelGGL(expand_kernel<false>, dim3(Hkv, B), dim3(256), 0, stream, sel, p.cap_u, 1, nsel_u, units,
                        wc, Hkv, idx, nsel_cap, n_sel);
   } else {
@@ -670,7 +685,8 @@ hipError_t launch_select_grouped(const float* scores, int stride, const int* ctx
                          Hkv, s_num, s_den, window, keys, p.kstride, units, top, wc);
     const int cap = sampled_list_cap(p.kstride, p.cap_u);
     hipLaunchKernelGGL(select_stream_kernel, dim3(p.G, B), dim3(kFsThreads), select_lds_bytes(cap), stream, keys,
-                       p.kstride, units, p.G, s_num, s_den, 0, sel, p.cap_u, nsel_u, (const int*)top, cap);
+                       p.kstride, units, p.G, s_num, s_den, 0, sel, p.cap_u, nsel_u, (const int*)top, cap,
+                       (int*)nullptr);
     hipLaunchKernelGGL(expand_kernel<true>, dim3(Hkv, B), dim3(256), 0, stream, sel, p.cap_u, p.G, nsel_u, units,
                        wc, Hkv, idx, nsel_cap, n_sel);
   }

@@ -3,7 +3,8 @@
 A round is the library's calls in order (no computation here: this module
 only sequences calls and owns the buffers they read and write):
 
-    s3r_select                  on the scores the previous verification wrote;
+    s3r_select                  on the scores the previous verification wrote (and the
+                                draft steps' dispatch order, longest first);
     k x (s3r_kv_append          the draft token's K/V row at L + j - 1,
          s3r_sparse_decode_attn draft step j, attending up to L + j);
     s3r_kv_append               the k + 1 block rows at L .. L + k (they replace
@@ -71,6 +72,7 @@ class RoundDriver:
         self.verified = torch.zeros((1,), dtype=torch.int64, device=dev)
         self.idx = torch.empty((B, Hkv, self.cap), **i32)
         self.n_sel = torch.empty((B,), **i32)
+        self.order = torch.empty((B,), **i32)
         self.draft_out = torch.empty((k, B, Hq, D), dtype=torch.float32, device=dev)
         self.draft_lse = torch.empty((k, B, Hq), dtype=torch.float32, device=dev)
         self.ver_out = torch.empty((B, k + 1, Hq, D), dtype=torch.float32, device=dev)
@@ -111,17 +113,17 @@ class RoundDriver:
         k, ml = self.k, self.max_len
         if self.plain_select:
             s3r.select(self.scores, self.ctx_len, ml, self.s_num, self.s_den, self.window, idx=self.idx,
-                       n_sel=self.n_sel)
+                       n_sel=self.n_sel, order=self.order)
         else:
             s3r.select_grouped(self.scores, self.ctx_len, ml, self.s_num, self.s_den, self.window,
                                unit=self.select_unit, all_heads=self.select_all_heads, idx=self.idx,
-                               n_sel=self.n_sel, ws=self.ws)
+                               n_sel=self.n_sel, ws=self.ws, order=self.order)
         for j in range(1, k + 1):
             pos = self.ctx_len if j == 1 else self.cur_len[j - 2]
             s3r.kv_append(self.k_draft[j - 1], self.v_draft[j - 1], self.kv, pos, ml)
             s3r.sparse_decode_attn(self.q_draft[j - 1], self.kv, self.idx, self.n_sel, self.ctx_len,
                                    self.cur_len[j - 1], self.scale, self.max_attend, out=self.draft_out[j - 1],
-                                   lse=self.draft_lse[j - 1], ws=self.ws)
+                                   lse=self.draft_lse[j - 1], ws=self.ws, order=self.order)
         s3r.kv_append(self.k_block, self.v_block, self.kv, self.ctx_len, ml)
         s3r.verify_attn(self.q_verify, self.kv, self.seq_len, k, self.scale, ml, out=self.ver_out,
                         lse=self.ver_lse, scores=self.scores, ws=self.ws)

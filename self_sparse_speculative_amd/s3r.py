@@ -31,6 +31,7 @@ EXPORTED = (
     "s3r_sparse_decode_workspace_bytes", "s3r_sparse_decode_attn",
     "s3r_verify_workspace_bytes", "s3r_verify_attn", "s3r_verify_attn_deferred", "s3r_verify_scores",
     "s3r_spec_sample_workspace_bytes", "s3r_spec_sample", "s3r_kv_append", "s3r_commit",
+    "s3r_length_order",
 )
 
 
@@ -77,19 +78,21 @@ def load():
         L.s3r_budget.restype = i32
         L.s3r_budget.argtypes = [i32, i32, i32, i32]
         L.s3r_select.restype = ctypes.c_int
-        L.s3r_select.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp, vp]
+        L.s3r_select.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp, vp, vp]
         L.s3r_select_grouped_capacity.restype = i32
         L.s3r_select_grouped_capacity.argtypes = [i32, i32, i32, i32, i32]
         L.s3r_select_grouped_workspace_bytes.restype = sz
         L.s3r_select_grouped_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
         L.s3r_select_grouped.restype = ctypes.c_int
-        L.s3r_select_grouped.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, i32, vp, vp, sz,
-                                         vp]
+        L.s3r_select_grouped.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, i32, vp, vp, vp,
+                                         sz, vp]
         L.s3r_sparse_decode_workspace_bytes.restype = sz
         L.s3r_sparse_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.s3r_sparse_decode_attn.restype = ctypes.c_int
-        L.s3r_sparse_decode_attn.argtypes = [vp, ctypes.POINTER(PagedKVStruct), vp, i32, vp, vp, vp, i32,
+        L.s3r_sparse_decode_attn.argtypes = [vp, ctypes.POINTER(PagedKVStruct), vp, i32, vp, vp, vp, vp, i32,
                                              i32, f32, i32, vp, vp, vp, sz, vp]
+        L.s3r_length_order.restype = ctypes.c_int
+        L.s3r_length_order.argtypes = [vp, i32, vp, vp]
         L.s3r_verify_workspace_bytes.restype = sz
         L.s3r_verify_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.s3r_verify_attn.restype = ctypes.c_int
@@ -197,8 +200,10 @@ def budget(L: int, s_num: int, s_den: int, window: int) -> int:
     return int(load().s3r_budget(int(L), int(s_num), int(s_den), int(window)))
 
 
-def select(scores, ctx_len, max_ctx_len, s_num, s_den, window, idx=None, n_sel=None, nsel_cap=None, stream=None):
-    """s3r_select. scores f32 [B][Hkv][stride], ctx_len i32 [B]. Returns (idx, n_sel)."""
+def select(scores, ctx_len, max_ctx_len, s_num, s_den, window, idx=None, n_sel=None, nsel_cap=None, stream=None,
+           order=None):
+    """s3r_select. scores f32 [B][Hkv][stride], ctx_len i32 [B]; order: i32 [B] written with the draft
+    dispatch order when given. Returns (idx, n_sel)."""
     L = load()
     B, Hkv, stride = scores.shape
     if nsel_cap is None:
@@ -208,7 +213,8 @@ def select(scores, ctx_len, max_ctx_len, s_num, s_den, window, idx=None, n_sel=N
     if n_sel is None:
         n_sel = torch.empty((B,), dtype=torch.int32, device=scores.device)
     _check(L.s3r_select(_ptr(scores), stride, _ptr(ctx_len), B, Hkv, int(max_ctx_len), int(s_num), int(s_den),
-                        int(window), _ptr(idx), int(nsel_cap), _ptr(n_sel), _stream(stream)), "s3r_select")
+                        int(window), _ptr(idx), int(nsel_cap), _ptr(n_sel), _ptr(order), _stream(stream)),
+           "s3r_select")
     return idx, n_sel
 
 
@@ -217,7 +223,7 @@ def select_grouped_capacity(max_ctx_len, s_num, s_den, window, unit) -> int:
 
 
 def select_grouped(scores, ctx_len, max_ctx_len, s_num, s_den, window, unit=16, all_heads=False, idx=None,
-                   n_sel=None, nsel_cap=None, ws=None, stream=None):
+                   n_sel=None, nsel_cap=None, ws=None, stream=None, order=None):
     """s3r_select_grouped: whole pages (unit 16) and/or one kept set per sequence (all_heads).
     Returns (idx [B][Hkv][cap], n_sel [B])."""
     L = load()
@@ -234,7 +240,8 @@ def select_grouped(scores, ctx_len, max_ctx_len, s_num, s_den, window, unit=16, 
     buf = _ws(ws, scores.device).get("select", max(nb, 1))
     _check(L.s3r_select_grouped(_ptr(scores), stride, _ptr(ctx_len), B, Hkv, int(max_ctx_len), int(s_num),
                                 int(s_den), int(window), int(unit), int(bool(all_heads)), _ptr(idx), int(nsel_cap),
-                                _ptr(n_sel), _ptr(buf), buf.numel(), _stream(stream)), "s3r_select_grouped")
+                                _ptr(n_sel), _ptr(order), _ptr(buf), buf.numel(), _stream(stream)),
+           "s3r_select_grouped")
     return idx, n_sel
 
 
@@ -242,9 +249,20 @@ def sparse_decode_workspace_bytes(B, Hq, head_dim, max_attend) -> int:
     return int(load().s3r_sparse_decode_workspace_bytes(B, Hq, head_dim, max_attend))
 
 
+def length_order(lengths, out=None, stream=None):
+    """s3r_length_order: int32 [B] device permutation, longest first (stable)."""
+    L = load()
+    B = lengths.shape[0]
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=lengths.device)
+    _check(L.s3r_length_order(_ptr(lengths), B, _ptr(out), _stream(stream)), "s3r_length_order")
+    return out
+
+
 def sparse_decode_attn(q, kv: PagedKV, idx, n_sel, sel_len, cur_len, scale, max_attend, out=None, lse=None,
-                       want_lse=True, ws=None, stream=None):
-    """s3r_sparse_decode_attn. q [B][Hq][D]. Returns (out f32 [B][Hq][D], lse f32 [B][Hq] or None)."""
+                       want_lse=True, ws=None, stream=None, order=None):
+    """s3r_sparse_decode_attn. q [B][Hq][D]; order: int32 [B] dispatch permutation or None.
+    Returns (out f32 [B][Hq][D], lse f32 [B][Hq] or None)."""
     L = load()
     B, Hq, D = q.shape
     if out is None:
@@ -254,7 +272,7 @@ def sparse_decode_attn(q, kv: PagedKV, idx, n_sel, sel_len, cur_len, scale, max_
     nb = sparse_decode_workspace_bytes(B, Hq, D, int(max_attend))
     buf = _ws(ws, q.device).get("decode", nb)
     _check(L.s3r_sparse_decode_attn(_ptr(q), ctypes.byref(kv.struct), _ptr(idx), idx.shape[2], _ptr(n_sel),
-                                    _ptr(sel_len), _ptr(cur_len), B, Hq, float(scale), int(max_attend),
+                                    _ptr(sel_len), _ptr(cur_len), _ptr(order), B, Hq, float(scale), int(max_attend),
                                     _ptr(out), _ptr(lse), _ptr(buf), buf.numel(), _stream(stream)),
            "s3r_sparse_decode_attn")
     return out, lse

@@ -43,13 +43,13 @@ def run_select(cfg, batch, t, scores=None):
                       nsel_cap=nsel_cap(cfg, batch))
 
 
-def run_draft_steps(cfg, batch, t, idx, n_sel):
+def run_draft_steps(cfg, batch, t, idx, n_sel, order=None):
     outs = []
     max_attend = nsel_cap(cfg, batch) + cfg.k
     for j in range(1, cfg.k + 1):
         cur = t["ctx_len"] + j
         o, lse = s3r.sparse_decode_attn(t["q_draft"][j - 1], t["kv"], idx, n_sel, t["ctx_len"], cur,
-                                        float(batch.scale), max_attend)
+                                        float(batch.scale), max_attend, order=order)
         outs.append((o, lse))
     return outs
 

@@ -81,13 +81,13 @@ def _kv(page=16, D=128, dtype=1, hkv=8, null=False):
 
 def test_select_validation(lib):
     f = lib.s3r_select
-    assert f(None, 100, FAKE, 2, 2, 100, 1, 20, 16, FAKE, 16, FAKE, None) == INVALID
-    assert f(FAKE, 100, FAKE, 0, 2, 100, 1, 20, 16, FAKE, 16, FAKE, None) == INVALID
-    assert f(FAKE, 100, FAKE, 2, 2, 100, 1, 0, 16, FAKE, 16, FAKE, None) == INVALID      # s_den = 0
-    assert f(FAKE, 100, FAKE, 2, 2, 100, 3, 2, 16, FAKE, 16, FAKE, None) == INVALID      # s > 1
-    assert f(FAKE, 99, FAKE, 2, 2, 100, 1, 20, 16, FAKE, 16, FAKE, None) == INVALID      # stride < max_ctx
-    assert f(FAKE, 100, FAKE, 2, 2, 100, 1, 2, 16, FAKE, 49, FAKE, None) == INVALID      # cap < 50
-    assert f(FAKE, 100, FAKE, 2, 2, 100, 1, 20, -1, FAKE, 16, FAKE, None) == INVALID     # window < 0
+    assert f(None, 100, FAKE, 2, 2, 100, 1, 20, 16, FAKE, 16, FAKE, None, None) == INVALID
+    assert f(FAKE, 100, FAKE, 0, 2, 100, 1, 20, 16, FAKE, 16, FAKE, None, None) == INVALID
+    assert f(FAKE, 100, FAKE, 2, 2, 100, 1, 0, 16, FAKE, 16, FAKE, None, None) == INVALID      # s_den = 0
+    assert f(FAKE, 100, FAKE, 2, 2, 100, 3, 2, 16, FAKE, 16, FAKE, None, None) == INVALID      # s > 1
+    assert f(FAKE, 99, FAKE, 2, 2, 100, 1, 20, 16, FAKE, 16, FAKE, None, None) == INVALID      # stride < max_ctx
+    assert f(FAKE, 100, FAKE, 2, 2, 100, 1, 2, 16, FAKE, 49, FAKE, None, None) == INVALID      # cap < 50
+    assert f(FAKE, 100, FAKE, 2, 2, 100, 1, 20, -1, FAKE, 16, FAKE, None, None) == INVALID     # window < 0
 
 
 def test_select_grouped_validation_and_capacity(lib):
@@ -95,7 +95,7 @@ def test_select_grouped_validation_and_capacity(lib):
     ws = lib.s3r_select_grouped_workspace_bytes(2, 2, 100, 1, 20, 16, 16, 0)
     cap = lib.s3r_select_grouped_capacity(100, 1, 20, 16, 16)
     args = lambda unit=16, ah=0, cap_=cap, ws_b=ws, stride=100, W=16: (FAKE, stride, FAKE, 2, 2, 100, 1, 20, W, unit,
-                                                                        ah, FAKE, cap_, FAKE, FAKE, ws_b, None)
+                                                                        ah, FAKE, cap_, FAKE, None, FAKE, ws_b, None)
     assert f(*args(unit=8)) == INVALID
     assert f(*args(cap_=cap - 1)) == INVALID
     assert f(*args(stride=99)) == INVALID
@@ -115,8 +115,8 @@ def test_decode_validation(lib):
     f = lib.s3r_sparse_decode_attn
     kv = _kv()
     ws_ok = lib.s3r_sparse_decode_workspace_bytes(4, 32, 128, 100)
-    args = lambda kvs, Hq=32, ws=ws_ok, scale=0.088: (FAKE, ctypes.byref(kvs), FAKE, 16, FAKE, FAKE, FAKE, 4, Hq,
-                                                      scale, 100, FAKE, None, FAKE, ws, None)
+    args = lambda kvs, Hq=32, ws=ws_ok, scale=0.088: (FAKE, ctypes.byref(kvs), FAKE, 16, FAKE, FAKE, FAKE, None, 4,
+                                                      Hq, scale, 100, FAKE, None, FAKE, ws, None)
     assert f(*args(_kv(null=True))) == INVALID
     assert f(*args(kv, Hq=30)) == INVALID                 # Hq % Hkv
     assert f(*args(kv, scale=float("nan"))) == INVALID
@@ -128,6 +128,14 @@ def test_decode_validation(lib):
     assert f(*args(_kv(dtype=7))) == INVALID
     assert f(*args(kv, ws=ws_ok - 1)) == WORKSPACE
     assert ws_ok == 4 * 32 * 1 * 130 * 4
+
+
+def test_length_order_validation(lib):
+    f = lib.s3r_length_order
+    assert f(None, 4, FAKE, None) == INVALID
+    assert f(FAKE, 4, None, None) == INVALID
+    assert f(FAKE, 0, FAKE, None) == INVALID
+    assert f(FAKE, 65536, FAKE, None) == INVALID
 
 
 def test_verify_validation(lib):

@@ -192,6 +192,51 @@ def test_draft_bf16_group_sizes(G):
     _draft_case(cfg, batch, t, [1, cfg.k], range(cfg.B), TOL_BF16, False)
 
 
+@pytest.mark.parametrize("B", [1, 5, 256, 1025, 3000])
+def test_length_order_is_the_stable_descending_sort(B):
+    rng = np.random.default_rng(B)
+    for L in (rng.integers(1, 40, size=B), rng.integers(1, 1 << 30, size=B), np.full(B, 7)):
+        L = L.astype(np.int32)
+        got = s3r.length_order(torch.from_numpy(L).cuda()).cpu().numpy()
+        assert np.array_equal(got, np.argsort(-L.astype(np.int64), kind="stable")), B
+
+
+def test_select_writes_the_dispatch_order():
+    # s3r_select forms the longest-first order in its own launch; s3r_select_grouped through the
+    # order kernel; neither changes the kept sets
+    rng = np.random.default_rng(8)
+    B, Hkv, M = 600, 2, 3000
+    L = rng.choice([100, 777, 2048, 2999, 3000], B).astype(np.int32)  # many ties
+    sc = torch.from_numpy(rng.random((B, Hkv, M), dtype=np.float32)).cuda()
+    ctx = torch.from_numpy(L).cuda()
+    want = np.argsort(-L.astype(np.int64), kind="stable")
+    idx0, n0 = s3r.select(sc, ctx, M, 1, 20, 64)
+    order = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    idx1, n1 = s3r.select(sc, ctx, M, 1, 20, 64, order=order)
+    assert np.array_equal(order.cpu().numpy(), want)
+    assert torch.equal(n0, n1) and all(torch.equal(idx0[b, :, :n0[b]], idx1[b, :, :n0[b]]) for b in range(B))
+    order.fill_(-1)
+    g0, gn0 = s3r.select_grouped(sc, ctx, M, 1, 20, 64, unit=16)
+    g1, gn1 = s3r.select_grouped(sc, ctx, M, 1, 20, 64, unit=16, order=order)
+    assert np.array_equal(order.cpu().numpy(), want)
+    assert torch.equal(gn0, gn1) and all(torch.equal(g0[b, :, :gn0[b]], g1[b, :, :gn0[b]]) for b in range(B))
+
+
+@pytest.mark.parametrize("key,cid,ov", [("c1", 1, {}), ("c3d", 3, {"B": 5}), ("c2d", 2, {"B": 6})])
+def test_draft_dispatch_order_changes_no_result(key, cid, ov):
+    # the vector path (c1) and the MFMA path, with the longest-first order and a shuffled one:
+    # every output and lse bit-identical to the launch without an order
+    cfg, batch, t = _batch(key, cid, **ov)
+    idx, n_sel = run_select(cfg, batch, t)
+    plain = run_draft_steps(cfg, batch, t, idx, n_sel)
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(cfg.B).astype(np.int32)).cuda()
+    for order in (s3r.length_order(t["ctx_len"]), perm):
+        got = run_draft_steps(cfg, batch, t, idx, n_sel, order=order)
+        torch.cuda.synchronize()
+        for (o0, l0), (o1, l1) in zip(plain, got):
+            assert torch.equal(o0, o1) and torch.equal(l0, l1)
+
+
 @pytest.mark.parametrize("key,cid,ov", [("c1", 1, {}), ("c2d", 2, {"B": 6})])
 def test_draft_nothing_attended(key, cid, ov):
     # no kept position and no position of this round: output 0, lse = -inf (both kernel paths)
