@@ -54,6 +54,11 @@ constexpr int kVerWaves = kVerThreads / kWave;
 constexpr int kSub = 32;         // positions per subtile (two pages)
 constexpr int kVtStride = 40;    // LDS row stride (uint16) of a transposed V subtile: 32 slots + pad
 
+// Floats per tile in the row-maxima record: R rounded up to whole 128 B lines,
+// so no two tiles share a line and every line is written whole (lines
+// written in parts by different waves cost measurably more).
+__host__ __device__ __forceinline__ int max_stride(int R) { return (R + 31) & ~31; }
+
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
@@ -252,7 +257,7 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
         f16x4_t h1 = {(_Float16)pv[1][0], (_Float16)pv[1][1], (_Float16)pv[1][2], (_Float16)pv[1][3]};
         *reinterpret_cast<f16x4_t*>(dst + 4 * g4) = h0;
         *reinterpret_cast<f16x4_t*>(dst + 16 + 4 * g4) = h1;
-        if (g4 == 0) sc_max[(bkv * ntile_cap + tile) * R + r] = base;
+        if (g4 == 0) sc_max[(bkv * ntile_cap + tile) * max_stride(R) + r] = base;
       }
     }
 
@@ -414,7 +419,8 @@ __global__ __launch_bounds__(kVerThreads) void verify_generic_kernel(
       if (with_scores && sub == 0) sc_val[((bkv * ntile_cap + j / kSub) * R + r) * kSub + (j % kSub)] = p;
     }
     if (with_scores) {
-      for (int t = c0 / kSub + tid; t < ceil_div(c1, kSub); t += kVerThreads) sc_max[(bkv * ntile_cap + t) * R + r] = base;
+      for (int t = c0 / kSub + tid; t < ceil_div(c1, kSub); t += kVerThreads)
+        sc_max[(bkv * ntile_cap + t) * max_stride(R) + r] = base;
     }
     // reduce l and acc over the 16 streams
     __syncthreads();
@@ -517,7 +523,7 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
   // weights of every (tile, row) of this block, then 4 positions per thread
   for (int e = tid; e < kFinTiles * R; e += kVerThreads) {
     const int et = e / R, r = e % R, tile = tile_beg + et;
-    wt[et][r] = tile < tile_end ? exp2f_fast(sc_max[(bkv * ntile_cap + tile) * R + r] - l2row[r]) : 0.f;
+    wt[et][r] = tile < tile_end ? exp2f_fast(sc_max[(bkv * ntile_cap + tile) * max_stride(R) + r] - l2row[r]) : 0.f;
   }
   __syncthreads();
   const int tl = tid / (kSub / 4), j4 = (tid % (kSub / 4)) * 4;
@@ -567,7 +573,7 @@ VerifyPlan verify_plan(int B, int k, int Hq, int Hkv, int D, int dtype, int max_
   p.off_part_ml = off;
   off = align256(off + nbkv * p.nsplit * p.RP * 2 * sizeof(float));
   p.off_sc_max = off;
-  off = align256(off + nbkv * p.ntile_cap * p.R * sizeof(float));
+  off = align256(off + nbkv * p.ntile_cap * max_stride(p.R) * sizeof(float));
   p.off_sc_val = off;
   off = align256(off + nbkv * p.ntile_cap * p.R * kSub * (p.mfma ? sizeof(_Float16) : sizeof(float)));
   p.bytes = off;
