@@ -150,6 +150,41 @@ def test_select_rows_around_the_sampled_path_limits():
                 assert n_sel[b] == len(ref) and np.array_equal(idx[b, kv, :n_sel[b]], ref), (s_num, s_den, b, kv)
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_select_randomised_rows_and_budgets(seed):
+    """Rows of 2000-30000 positions at budgets from 1/50 to 1/3, with score shapes that stress the
+    sampled threshold: uniform, heavy-tailed, a few distinct values (ties), rising with position,
+    a sawtooth of the sample's period, and spikes. Every kept set matches the oracle."""
+    rng = np.random.default_rng(100 + seed)
+    B, Hkv, window = 12, 2, 64
+    L = rng.integers(2000, 30000, size=B).astype(np.int32)
+    M = int(L.max())
+    sc = np.empty((B, Hkv, M), np.float32)
+    j = np.arange(M)
+    shapes = [
+        lambda: rng.random(M),
+        lambda: rng.standard_cauchy(M),
+        lambda: rng.integers(0, 5, M) / 4.0,
+        lambda: j / M + 1e-3 * rng.random(M),
+        lambda: (j % 153) / 153.0,
+        lambda: np.where(rng.random(M) < 0.01, 100.0, 1e-3 * rng.random(M)),
+    ]
+    for b in range(B):
+        for kv in range(Hkv):
+            sc[b, kv] = shapes[(b * Hkv + kv) % len(shapes)]().astype(np.float32)
+    budgets = [(1, 50), (1, 20), (1, 10), (1, 5), (1, 3)]
+    for s_num, s_den in (budgets[seed], budgets[(seed + 2) % 5], budgets[(seed + 4) % 5]):
+        cap = s3r.budget(M, s_num, s_den, window)
+        idx, n_sel = s3r.select(torch.from_numpy(sc).cuda(), torch.from_numpy(L).cuda(), M, s_num, s_den, window,
+                                nsel_cap=cap)
+        torch.cuda.synchronize()
+        idx, n_sel = idx.cpu().numpy(), n_sel.cpu().numpy()
+        for b in range(B):
+            for kv in range(Hkv):
+                ref = oracle.select(sc[b, kv], int(L[b]), s_num, s_den, window)
+                assert n_sel[b] == len(ref) and np.array_equal(idx[b, kv, :n_sel[b]], ref), (s_num, s_den, b, kv)
+
+
 # ----------------------------------------------------------------- draft
 
 def _draft_case(cfg, batch, t, steps, seqs, tol, absolute):
