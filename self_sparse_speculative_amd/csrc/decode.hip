@@ -10,7 +10,9 @@
 // (2 * head_dim * element bytes) and the work per byte is G multiply-adds per
 // element, so it is bound by HBM gather bandwidth, not by arithmetic. Grid
 // (split, KV head, sequence); a split is a chunk of the attended list
-// (selected positions first, then this round's positions).
+// (selected positions first, then this round's positions). An optional order
+// maps the grid's sequence index to a sequence: workgroups of similar length
+// dispatched together (longest first) finish a batch of mixed lengths sooner.
 //
 // bf16, head_dim 128: sparse_decode_mfma_kernel (below), splits of at most
 // 2048 positions made equal; a lone split writes the output itself.
