@@ -57,6 +57,18 @@ def test_variants_tie_heavy_and_edge_lengths(unit, all_heads):
         _check(cfg, sc, ctx, unit, all_heads, sn, sd, W)
 
 
+@pytest.mark.parametrize("unit,all_heads", VARIANTS)
+def test_variants_on_long_rows(unit, all_heads):
+    # 33K-50K positions: more than 2048 candidate pages, so the page keys and the summed
+    # position keys both take the sampled-threshold path, at two budgets
+    cfg = get_config(3, B=3, Hkv=2)
+    rng = np.random.default_rng(12)
+    ctx = np.array([33000, 41234, 50000], dtype=np.int32)
+    sc = rng.random((3, 2, 50000), dtype=np.float32)
+    for (sn, sd) in ((1, 20), (1, 5)):
+        _check(cfg, sc, ctx, unit, all_heads, sn, sd, 64)
+
+
 def test_draft_over_page_selection():
     cfg = get_config(3, B=4, lengths=("uniform", 2000, 6000))
     b = make_batch(cfg, parts=("kv", "q", "scores"))
