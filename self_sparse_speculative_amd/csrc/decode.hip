@@ -306,16 +306,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
   }
   const int p1 = min(total, p0 + chunk);
 
-  // Resolve the split's positions to cache rows (page, KV head, slot) once.
-  const int* idx_row = idx + ((size_t)b * Hkv + kv) * nsel_cap;
-  const int* bt_row = bt + (size_t)b * max_pages;
-  for (int j = p0 + tid; j < p1; j += kDecThreads) {
-    const int pos = j < ns ? idx_row[j] : L + (j - ns);
-    rows[j - p0] = (bt_row[pos >> 4] * Hkv + kv) * kPage + (pos & 15);
-  }
-  __syncthreads();
-  const int cnt = p1 - p0;
-
+  // Q fragments first: their loads overlap the position resolution below.
   dbf16x8_t qf[4];
   {
     const int r = n16;
@@ -328,6 +319,30 @@ __global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
       for (int kk = 0; kk < 4; ++kk) qf[kk] = dbf16x8_t{};
     }
   }
+  // Resolve the split's positions to cache rows (page, KV head, slot) once:
+  // every position load of the thread is issued, then every block-table load,
+  // so the two dependent round trips are paid once, not once per position.
+  const int* idx_row = idx + ((size_t)b * Hkv + kv) * nsel_cap;
+  const int* bt_row = bt + (size_t)b * max_pages;
+  constexpr int kRes = kDecChunkMfma / kDecThreads;
+  int rpos[kRes], rpg[kRes];
+#pragma unroll
+  for (int u = 0; u < kRes; ++u) {
+    const int j = p0 + tid + u * kDecThreads;
+    rpos[u] = j < p1 ? (j < ns ? idx_row[j] : L + (j - ns)) : 0;
+  }
+#pragma unroll
+  for (int u = 0; u < kRes; ++u) {
+    const int j = p0 + tid + u * kDecThreads;
+    rpg[u] = j < p1 ? bt_row[rpos[u] >> 4] : 0;
+  }
+#pragma unroll
+  for (int u = 0; u < kRes; ++u) {
+    const int j = p0 + tid + u * kDecThreads;
+    if (j < p1) rows[j - p0] = (rpg[u] * Hkv + kv) * kPage + (rpos[u] & 15);
+  }
+  __syncthreads();
+  const int cnt = p1 - p0;
   float m_run = kNegInf, l_run = 0.f;
   df32x4_t oacc[8];
 #pragma unroll
