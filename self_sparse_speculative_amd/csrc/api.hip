@@ -49,7 +49,7 @@ const char* s3r_status_string(s3r_status status) {
   return "S3R: unknown status";
 }
 
-int32_t s3r_version(void) { return 100; }
+int32_t s3r_version(void) { return 200; }
 
 int32_t s3r_budget(int32_t L, int32_t s_num, int32_t s_den, int32_t window) {
   if (L < 0 || s_den <= 0 || s_num < 0 || s_num > s_den || window < 0) return -1;
