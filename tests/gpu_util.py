@@ -37,10 +37,10 @@ def nsel_cap(cfg, batch):
     return s3r.budget(int(batch.ctx_len.max()), cfg.s_num, cfg.s_den, cfg.window)
 
 
-def run_select(cfg, batch, t, scores=None):
+def run_select(cfg, batch, t, scores=None, order=None):
     sc = t["scores"] if scores is None else scores
     return s3r.select(sc, t["ctx_len"], int(batch.ctx_len.max()), cfg.s_num, cfg.s_den, cfg.window,
-                      nsel_cap=nsel_cap(cfg, batch))
+                      nsel_cap=nsel_cap(cfg, batch), order=order)
 
 
 def run_draft_steps(cfg, batch, t, idx, n_sel, order=None):

@@ -540,8 +540,9 @@ def test_full_size_24k_round_sampled():
     select on all units is checked on a sample, draft and verify on sampled sequences, sampling
     on every sequence."""
     cfg, batch, t = _batch("c5full", 5)
-    idx, n_sel = run_select(cfg, batch, t)
-    outs = run_draft_steps(cfg, batch, t, idx, n_sel)
+    order = torch.empty((cfg.B,), dtype=torch.int32, device="cuda")  # as the benchmark: dispatch order from select
+    idx, n_sel = run_select(cfg, batch, t, order=order)
+    outs = run_draft_steps(cfg, batch, t, idx, n_sel, order=order)
     vout, vlse, vsc = run_verify(cfg, batch, t)
     toks, nout, acc = run_sample(cfg, batch, t)
     torch.cuda.synchronize()
