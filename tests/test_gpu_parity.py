@@ -399,6 +399,15 @@ def test_spec_sample_bit_exact(key, cid, ov):
     print(f"mean tokens per round {nout.float().mean().item():.3f}")
 
 
+@pytest.mark.parametrize("T", [0.7, 1.6])
+def test_spec_sample_other_temperatures(T):
+    # the temperature divides every logit before the softmax, on both the target and the draft rows
+    cfg, batch, t = _batch("c2smp", 2, parts=("logits",), B=64)
+    toks, nout, acc = run_sample(cfg, batch, t, temperature=T)
+    torch.cuda.synchronize()
+    _check_sample(cfg, batch, toks, nout, acc, np.float32(T), range(cfg.B))
+
+
 def test_spec_sample_greedy_and_identical():
     cfg, batch, t = _batch("c2smp", 2, parts=("logits",), B=64)
     toks, nout, acc = run_sample(cfg, batch, t, temperature=0.0)
