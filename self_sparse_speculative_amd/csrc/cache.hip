@@ -29,7 +29,7 @@ constexpr int kCommitThreads = 1024;
 __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
     const uint4* __restrict__ k_rows, const uint4* __restrict__ v_rows, uint4* __restrict__ kp,
     uint4* __restrict__ vp, const int* __restrict__ bt, int max_pages, const int* __restrict__ pos,
-    int B, int n, int Hkv, int chunks_per_row, long long total) {
+    int n, int Hkv, int chunks_per_row, long long total) {
   const long long t = (long long)blockIdx.x * kAppendThreads + threadIdx.x;
   if (t >= total) return;
   const int c = (int)(t % chunks_per_row);
@@ -82,7 +82,7 @@ hipError_t launch_kv_append(const void* k_rows, const void* v_rows, void* k_page
   const long long blocks = (total + kAppendThreads - 1) / kAppendThreads;
   hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)blocks), dim3(kAppendThreads), 0, stream,
                      (const uint4*)k_rows, (const uint4*)v_rows, (uint4*)k_pages, (uint4*)v_pages, bt,
-                     max_pages, pos, B, n, Hkv, chunks, total);
+                     max_pages, pos, n, Hkv, chunks, total);
   return hipGetLastError();
 }
 

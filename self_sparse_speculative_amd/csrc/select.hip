@@ -496,7 +496,7 @@ __global__ __launch_bounds__(kFsThreads) void select_stream_kernel(
       const bool valid = j < s1;
       const bool eq = valid && kv4[u] == T;
       const uint64_t beq = __ballot(eq);
-      const bool sel = (valid && kv4[u] > T) || (eq && eq_run + __popcll(beq & lt_mask) < need_eq);
+      const bool sel = (valid && kv4[u] > T) || (eq && eq_run + (int)__popcll(beq & lt_mask) < need_eq);
       const uint64_t bsel = __ballot(sel);
       const int pos = sel_run + __popcll(bsel & lt_mask);
       if (sel && pos < ntop) out[pos] = j;
