@@ -226,36 +226,41 @@ __global__ __launch_bounds__(kWave) void decide_kernel(
     int* __restrict__ desc) {
   __shared__ Exp64Table tab;
   exp64_init(tab);
-  const int b = blockIdx.x;
-  if (threadIdx.x != 0) return;
+  const int b = blockIdx.x, lane = threadIdx.x;
   const size_t so = (size_t)b * (2 * k + 1);
-  int istar = k;
-  for (int i = 0; i < k; ++i) {
-    const int x = dtok[(size_t)b * k + i];
-    bool acc;
+  // Lane i < k runs the ratio test of draft i; the first rejection ends the
+  // round, so tests past it are computed but never used (their results are
+  // the same as if the tests ran one after another and stopped there).
+  int x = 0;
+  bool acc = true;
+  if (lane < k) {
+    x = dtok[(size_t)b * k + lane];
     if (greedy) {
-      acc = x == sarg[so + i];
+      acc = x == sarg[so + lane];
+    } else if ((unsigned)x < (unsigned)V) {
+      const double p = prob(zt[((size_t)b * (k + 1) + lane) * V + x], smax[so + lane], ssum[so + lane], invT, tab);
+      const double qq =
+          prob(zd[((size_t)b * k + lane) * V + x], smax[so + k + 1 + lane], ssum[so + k + 1 + lane], invT, tab);
+      acc = (p >= qq) || ((double)u[(size_t)b * (k + 1) + lane] * qq < p);
     } else {
-      const double p = prob(zt[((size_t)b * (k + 1) + i) * V + x], smax[so + i], ssum[so + i], invT, tab);
-      const double qq = prob(zd[((size_t)b * k + i) * V + x], smax[so + k + 1 + i], ssum[so + k + 1 + i], invT, tab);
-      acc = (p >= qq) || ((double)u[(size_t)b * (k + 1) + i] * qq < p);
+      acc = false;  // a token outside the vocabulary is never accepted
     }
-    if (accepted) accepted[(size_t)b * k + i] = acc ? 1 : 0;
-    if (!acc) {
-      istar = i;
-      break;
-    }
-    tokens[(size_t)b * (k + 1) + i] = x;
   }
-  if (accepted)
-    for (int i = istar + 1; i < k; ++i) accepted[(size_t)b * k + i] = -1;
-  for (int j = istar + 1; j <= k; ++j) tokens[(size_t)b * (k + 1) + j] = -1;
-  n_out[b] = istar + 1;
-  if (greedy) {
-    tokens[(size_t)b * (k + 1) + istar] = sarg[so + istar];
-    desc[b] = -1;
-  } else {
-    desc[b] = istar | ((istar < k ? 1 : 0) << 8);
+  const uint64_t rej = __ballot(lane < k && !acc);
+  const int istar = rej ? __ffsll((unsigned long long)rej) - 1 : k;
+  if (lane < k) {
+    if (accepted) accepted[(size_t)b * k + lane] = lane < istar ? 1 : (lane == istar ? 0 : -1);
+    if (lane < istar) tokens[(size_t)b * (k + 1) + lane] = x;
+  }
+  for (int j = istar + 1 + lane; j <= k; j += kWave) tokens[(size_t)b * (k + 1) + j] = -1;
+  if (lane == 0) {
+    n_out[b] = istar + 1;
+    if (greedy) {
+      tokens[(size_t)b * (k + 1) + istar] = sarg[so + istar];
+      desc[b] = -1;
+    } else {
+      desc[b] = istar | ((istar < k ? 1 : 0) << 8);
+    }
   }
 }
 
