@@ -337,39 +337,48 @@ __global__ __launch_bounds__(kSmpThreads) void final_draw_kernel(
   const int istar = dsc & 0xff;
   const bool resid0 = (dsc >> 8) != 0;
   const double* cs = csum + (size_t)b * kSmpChunks * 2;
-  if (tid == 0) {
-    double Z = 0.0;
-    for (int c = 0; c < kSmpChunks; ++c) Z += cs[2 * c];
+  static_assert(kSmpChunks == kWave, "one lane per vocabulary chunk");
+  if (wave == 0) {
+    // lane c holds chunk c: inclusive scans of the chunk sums give Z and the
+    // chunk in which u * Z falls
+    double cw = cs[2 * lane], cp = cs[2 * lane + 1];
+    double iw = cw, ip = cp;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const double vw = __shfl_up(iw, off, kWave), vp = __shfl_up(ip, off, kWave);
+      if (lane >= off) {
+        iw += vw;
+        ip += vp;
+      }
+    }
+    double Z = __shfl(iw, kWave - 1, kWave);
     int usep = 0;
     if (!(Z > 0.0)) {  // all-zero residual: draw from p
       usep = 1;
-      Z = 0.0;
-      for (int c = 0; c < kSmpChunks; ++c) Z += cs[2 * c + 1];
+      Z = __shfl(ip, kWave - 1, kWave);
+      iw = ip;
+      cw = cp;
     }
     const double t = (double)u[(size_t)b * (k + 1) + k] * Z;
-    double cum = 0.0;
-    int chunk = -1;
-    double carry = 0.0;
-    for (int c = 0; c < kSmpChunks; ++c) {
-      const double after = cum + cs[2 * c + usep];
-      if (after > t) {
-        chunk = c;
-        carry = cum;
-        break;
-      }
-      cum = after;
+    const uint64_t over = __ballot(iw > t);
+    const uint64_t pos = __ballot(cw > 0.0);
+    int chunk;
+    double carry;
+    if (over) {
+      chunk = __ffsll((unsigned long long)over) - 1;
+      carry = __shfl(iw - cw, chunk, kWave);
+    } else {  // rounding left no crossing: last chunk with weight, which never crosses
+      chunk = pos ? 63 - __clzll(pos) : 0;
+      carry = -__builtin_huge_val();
     }
-    if (chunk < 0) {  // rounding left no crossing: last chunk with weight
-      for (int c = kSmpChunks - 1; c >= 0; --c)
-        if (cs[2 * c + usep] > 0.0) { chunk = c; break; }
-      carry = -__builtin_huge_val();  // never crosses; the last positive weight is taken
+    if (lane == 0) {
+      sh_chunk = chunk;
+      sh_usep = usep;
+      sh_carry = carry;
+      sh_t = t;
+      sh_found = -1;
+      sh_lastpos = -1;
     }
-    sh_chunk = chunk;
-    sh_usep = usep;
-    sh_carry = carry;
-    sh_t = t;
-    sh_found = -1;
-    sh_lastpos = -1;
   }
   __syncthreads();
   const int chunk = sh_chunk;
@@ -384,29 +393,53 @@ __global__ __launch_bounds__(kSmpThreads) void final_draw_kernel(
   const double st = ssum[so + istar];
   const float md = resid ? smax[so + k + 1 + istar] : 0.f;
   const double sd = resid ? ssum[so + k + 1 + istar] : 1.0;
-  for (int base = y0; base < y1; base += kSmpThreads) {
-    const int y = base + tid;
-    double w = 0.0;
-    if (y < y1) {
-      w = prob(zr[y], mt, st, invT, tab);
-      if (resid) w = fmax(0.0, w - prob(dr[y], md, sd, invT, tab));
+  // Segments of kSmpThreads x kDrawPer positions; thread tid takes kDrawPer
+  // consecutive ones, so the weights are formed in parallel, one block scan of
+  // the per-thread sums gives each thread its starting cumulative weight, and
+  // the thread scans its own positions in token order.
+  constexpr int kDrawPer = 16;
+  for (int seg = y0; seg < y1; seg += kSmpThreads * kDrawPer) {
+    const int a0 = seg + tid * kDrawPer;
+    double w[kDrawPer];
+    double tsum = 0.0;
+    int tlast = -1;
+#pragma unroll
+    for (int e = 0; e < kDrawPer; ++e) {
+      const int y = a0 + e;
+      double we = 0.0;
+      if (y < y1) {
+        we = prob(zr[y], mt, st, invT, tab);
+        if (resid) we = fmax(0.0, we - prob(dr[y], md, sd, invT, tab));
+      }
+      w[e] = we;
+      tsum += we;
+      tlast = we > 0.0 ? y : tlast;
     }
-    // inclusive scan inside the wave, then across waves
-    double incl = w;
+    // exclusive scan of the thread sums: inside the wave, then across waves
+    double incl = tsum;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
       const double v = __shfl_up(incl, off, kWave);
       if (lane >= off) incl += v;
     }
     if (lane == kWave - 1) wtot[wave] = incl;
-    const uint64_t pos_mask = __ballot(w > 0.0);
-    if (lane == 0) wlast[wave] = pos_mask ? base + wave * kWave + 63 - __clzll(pos_mask) : -1;
+    int wl = tlast;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) wl = max(wl, __shfl_xor(wl, off, kWave));
+    if (lane == 0) wlast[wave] = wl;
     __syncthreads();
-    double before = sh_carry;
-    for (int ww = 0; ww < wave; ++ww) before += wtot[ww];
-    const double cum = before + incl;
-    const uint64_t hit = __ballot(y < y1 && cum > t);
-    if (lane == 0) wfound[wave] = hit ? base + wave * kWave + __ffsll((unsigned long long)hit) - 1 : -1;
+    double cum = sh_carry + incl - tsum;
+    for (int ww = 0; ww < wave; ++ww) cum += wtot[ww];
+    int hit = -1;
+#pragma unroll
+    for (int e = 0; e < kDrawPer; ++e) {
+      cum += w[e];
+      if (hit < 0 && a0 + e < y1 && cum > t) hit = a0 + e;
+    }
+    int wf = hit < 0 ? 0x7fffffff : hit;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) wf = min(wf, __shfl_xor(wf, off, kWave));
+    if (lane == 0) wfound[wave] = wf == 0x7fffffff ? -1 : wf;
     __syncthreads();
     if (tid == 0) {
       for (int ww = 0; ww < kSmpWaves; ++ww) {
