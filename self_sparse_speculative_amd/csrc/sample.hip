@@ -214,8 +214,10 @@ __global__ __launch_bounds__(kSmpThreads) void row_stats_kernel(
   }
 }
 
-__device__ __forceinline__ double prob(float z, float m, double s, double invT, const Exp64Table& tab) {
-  return exp64(((double)z - (double)m) * invT, tab) / s;
+// Probability of logit z in a row with maximum m and normaliser s, given as
+// inv_s = 1 / s (one division per row instead of one per token).
+__device__ __forceinline__ double prob(float z, float m, double inv_s, double invT, const Exp64Table& tab) {
+  return exp64(((double)z - (double)m) * invT, tab) * inv_s;
 }
 
 __global__ __launch_bounds__(kWave) void decide_kernel(
@@ -238,9 +240,9 @@ __global__ __launch_bounds__(kWave) void decide_kernel(
     if (greedy) {
       acc = x == sarg[so + lane];
     } else if ((unsigned)x < (unsigned)V) {
-      const double p = prob(zt[((size_t)b * (k + 1) + lane) * V + x], smax[so + lane], ssum[so + lane], invT, tab);
-      const double qq =
-          prob(zd[((size_t)b * k + lane) * V + x], smax[so + k + 1 + lane], ssum[so + k + 1 + lane], invT, tab);
+      const double p = prob(zt[((size_t)b * (k + 1) + lane) * V + x], smax[so + lane], 1.0 / ssum[so + lane], invT, tab);
+      const double qq = prob(zd[((size_t)b * k + lane) * V + x], smax[so + k + 1 + lane], 1.0 / ssum[so + k + 1 + lane],
+                             invT, tab);
       acc = (p >= qq) || ((double)u[(size_t)b * (k + 1) + lane] * qq < p);
     } else {
       acc = false;  // a token outside the vocabulary is never accepted
@@ -282,9 +284,9 @@ __global__ __launch_bounds__(kSmpThreads) void chunk_sum_kernel(
   const float* zr = zt + ((size_t)b * (k + 1) + istar) * V;
   const float* dr = resid ? zd + ((size_t)b * k + istar) * V : nullptr;
   const float mt = smax[so + istar];
-  const double st = ssum[so + istar];
+  const double inv_st = 1.0 / ssum[so + istar];
   const float md = resid ? smax[so + k + 1 + istar] : 0.f;
-  const double sd = resid ? ssum[so + k + 1 + istar] : 1.0;
+  const double inv_sd = resid ? 1.0 / ssum[so + k + 1 + istar] : 1.0;
   double aw = 0.0, ap = 0.0;
   constexpr int U = 4;  // loads in flight per thread
   for (int y0u = y0 + tid; y0u < y1; y0u += U * kSmpThreads) {
@@ -298,9 +300,9 @@ __global__ __launch_bounds__(kSmpThreads) void chunk_sum_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (y0u + u * kSmpThreads >= y1) continue;
-      const double p = prob(zt_v[u], mt, st, invT, tab);
+      const double p = prob(zt_v[u], mt, inv_st, invT, tab);
       double w = p;
-      if (resid) w = fmax(0.0, p - prob(zd_v[u], md, sd, invT, tab));
+      if (resid) w = fmax(0.0, p - prob(zd_v[u], md, inv_sd, invT, tab));
       aw += w;
       ap += p;
     }
@@ -390,9 +392,9 @@ __global__ __launch_bounds__(kSmpThreads) void final_draw_kernel(
   const float* zr = zt + ((size_t)b * (k + 1) + istar) * V;
   const float* dr = resid ? zd + ((size_t)b * k + istar) * V : nullptr;
   const float mt = smax[so + istar];
-  const double st = ssum[so + istar];
+  const double inv_st = 1.0 / ssum[so + istar];
   const float md = resid ? smax[so + k + 1 + istar] : 0.f;
-  const double sd = resid ? ssum[so + k + 1 + istar] : 1.0;
+  const double inv_sd = resid ? 1.0 / ssum[so + k + 1 + istar] : 1.0;
   // Segments of kSmpThreads x kDrawPer positions; thread tid takes kDrawPer
   // consecutive ones, so the weights are formed in parallel, one block scan of
   // the per-thread sums gives each thread its starting cumulative weight, and
@@ -408,8 +410,8 @@ __global__ __launch_bounds__(kSmpThreads) void final_draw_kernel(
       const int y = a0 + e;
       double we = 0.0;
       if (y < y1) {
-        we = prob(zr[y], mt, st, invT, tab);
-        if (resid) we = fmax(0.0, we - prob(dr[y], md, sd, invT, tab));
+        we = prob(zr[y], mt, inv_st, invT, tab);
+        if (resid) we = fmax(0.0, we - prob(dr[y], md, inv_sd, invT, tab));
       }
       w[e] = we;
       tsum += we;
