@@ -16,14 +16,15 @@
 //   1. row_stats_kernel  (2k+1 rows x B): max, first argmax and the float64
 //      normaliser sum exp((z - max) / T), one pass with per-thread online
 //      rescaling, fixed-order tree merge;
-//   2. decide_kernel     (B): ratio tests in order, first reject, token
-//      counts; greedy (T = 0) finishes here;
+//   2. decide_kernel     (B): the k ratio tests on k lanes, a ballot for the
+//      first reject, token counts; greedy (T = 0) finishes here;
 //   3. chunk_sum_kernel  (chunks x B): float64 sums of the draw weights
 //      (residual max(0, p - q) or p) per vocabulary chunk, plus sums of p for
 //      the all-zero-residual fallback;
-//   4. final_draw_kernel (B): locate u * Z among the chunk sums, then an
-//      ordered block scan inside that chunk finds the first token whose
-//      cumulative weight exceeds u * Z.
+//   4. final_draw_kernel (B): locate u * Z among the chunk sums (a wave scan,
+//      one lane per chunk), then inside that chunk each thread weighs 16
+//      consecutive tokens, a block scan gives its starting cumulative weight,
+//      and the first token whose cumulative weight exceeds u * Z is taken.
 
 #include "common.hpp"
 #include "kernels.hpp"
