@@ -408,6 +408,23 @@ def test_spec_sample_other_temperatures(T):
     _check_sample(cfg, batch, toks, nout, acc, np.float32(T), range(cfg.B))
 
 
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_spec_sample_without_drafts(T):
+    # k = 0: plain decoding, one token per sequence drawn from p_0 with u[0] (greedy: its argmax)
+    cfg, batch, t = _batch("c2smp", 2, parts=("logits",), B=64)
+    zt0 = t["zt"][:, :1].contiguous()
+    u0 = t["u"][:, :1].contiguous()
+    empty_zd = torch.empty((cfg.B, 0, zt0.shape[2]), dtype=torch.float32, device="cuda")
+    empty_d = torch.empty((cfg.B, 0), dtype=torch.int32, device="cuda")
+    toks, nout, acc = s3r.spec_sample(zt0, empty_zd, empty_d, u0, T)
+    torch.cuda.synchronize()
+    assert acc is None
+    toks, nout = toks.cpu().numpy(), nout.cpu().numpy()
+    for b in range(cfg.B):
+        rt, rn, _ = oracle.spec_sample(batch.zt[b, :1], batch.zd[b, :0], batch.d[b, :0], batch.u[b, :1], np.float32(T))
+        assert nout[b] == rn == 1 and np.array_equal(toks[b], rt), (b, toks[b], rt)
+
+
 def test_spec_sample_greedy_and_identical():
     cfg, batch, t = _batch("c2smp", 2, parts=("logits",), B=64)
     toks, nout, acc = run_sample(cfg, batch, t, temperature=0.0)
