@@ -494,6 +494,35 @@ def test_rollout_config_round(layer):
 
 # ----------------------------------------------------------------- robustness
 
+def test_large_batch_of_short_contexts():
+    """1500 sequences of 20-400 positions (Qwen3-1.7B head shapes, a 4096-token vocabulary):
+    grids with many small workgroups; every step on a sample of sequences, sampling on all,
+    against the oracle."""
+    cfg, batch, t = _batch("c2bigB", 2, B=1500, lengths=("uniform", 20, 400), V=4096)
+    order = torch.empty((cfg.B,), dtype=torch.int32, device="cuda")
+    idx, n_sel = run_select(cfg, batch, t, order=order)
+    torch.cuda.synchronize()
+    assert np.array_equal(order.cpu().numpy(), np.argsort(-batch.ctx_len.astype(np.int64), kind="stable"))
+    rng = np.random.default_rng(3)
+    seqs = sorted(set(int(x) for x in rng.integers(cfg.B, size=12)) | {0, cfg.B - 1})
+    _check_select(cfg, batch, batch.scores, idx, n_sel, [(b, kv) for b in seqs for kv in range(cfg.Hkv)])
+    outs = run_draft_steps(cfg, batch, t, idx, n_sel, order=order)
+    torch.cuda.synchronize()
+    idx_np, ns = idx.cpu().numpy(), n_sel.cpu().numpy()
+    for j in (1, cfg.k):
+        o = outs[j - 1][0].cpu().numpy()
+        for b in seqs:
+            L = int(batch.ctx_len[b])
+            ro, _ = oracle.sparse_decode(batch.q_draft[j - 1, b], batch.k_pages, batch.v_pages, batch.block_table[b],
+                                         idx_np[b], int(ns[b]), L, L + j, float(batch.scale))
+            assert rel_err_rows(o[b], ro) <= TOL_BF16, (j, b)
+    _verify_case(cfg, batch, t, seqs, False)
+    toks, nout, acc = run_sample(cfg, batch, t)
+    torch.cuda.synchronize()
+    _check_sample(cfg, batch, toks, nout, acc, batch.temperature, range(cfg.B))
+
+
+
 def test_determinism_and_poisoned_workspace():
     cfg, batch, t = _batch("c2v", 2, parts=("kv", "q"), B=4)
     results = []
