@@ -1,4 +1,4 @@
-"""Round accounting: verified tokens and the next committed lengths.
+"""Round accounting: the state the next round starts from.
 
 [explainer], Jargon, "Block efficiency (tau)": the mean number of tokens
 one draft-and-verify round outputs; the illustration counts accepted
@@ -27,14 +27,6 @@ fixtures of the sampling tests).
 """
 
 import numpy as np
-
-
-def verified_tokens(n_out) -> int:
-    return int(np.asarray(n_out, dtype=np.int64).sum())
-
-
-def next_lengths(L, n_out) -> np.ndarray:
-    return np.asarray(L, dtype=np.int64) + np.asarray(n_out, dtype=np.int64)
 
 
 def commit(L: int, n_out: int, tokens, k: int):

@@ -100,7 +100,13 @@ def test_append_restores_the_generated_cache():
     assert pin_append_against_generator(oracle)
 
 
-def test_commit_after_full_acceptance_and_first_mismatch():
+def pin_commit(orc):
+    """commit() after the golden full-acceptance and first-mismatch rounds (raises on a mismatch)."""
+    test_commit_after_full_acceptance_and_first_mismatch(orc)
+    return True
+
+
+def test_commit_after_full_acceptance_and_first_mismatch(orc=oracle):
     # full acceptance: identical draft and target rows, the bonus becomes pending
     g = json.load(open(os.path.join(GOLDEN, "full_acceptance_k6.json")))
     k = g["k"]
@@ -108,7 +114,7 @@ def test_commit_after_full_acceptance_and_first_mismatch():
     zt = (1.5 * rng.standard_normal((k + 1, 20))).astype(np.float32)
     d = np.arange(k)
     tokens, n_out, _ = oracle.spec_sample(zt, zt[:k].copy(), d, np.full(k + 1, 0.3, np.float32), np.float32(1.0))
-    L1, pending, cur, seq = oracle.commit(100, n_out, tokens, k)
+    L1, pending, cur, seq = orc.commit(100, n_out, tokens, k)
     assert L1 == 100 + k + 1 and pending == tokens[k] and cur == [L1 + j for j in range(1, k + 1)]
     assert seq == L1 + k + 1
     # first mismatch at draft 3 of 5: three accepted plus the correction
@@ -122,6 +128,6 @@ def test_commit_after_full_acceptance_and_first_mismatch():
         zd[i, d[i]] = 5.0
     zt[3, d[3]] = -5.0
     tokens, n_out, _ = oracle.spec_sample(zt, zd, d, np.full(k + 1, 0.5, np.float32), np.float32(1.0))
-    L1, pending, cur, seq = oracle.commit(40, n_out, tokens, k)
+    L1, pending, cur, seq = orc.commit(40, n_out, tokens, k)
     assert n_out == g["n_out"] and L1 == 40 + g["n_out"]
     assert pending == tokens[g["n_accepted"]] and pending != d[g["n_accepted"]]

@@ -114,6 +114,35 @@ def _pin_all_heads(orc):
     return all(np.array_equal(g, ref) for g in orc.select_grouped(sc, 333, 1, 10, 16, 1, True))
 
 
+def _pin_margins(orc):
+    from tests.test_oracle_sampling import _flip_checks, _rows
+    import importlib
+    mod = importlib.import_module(orc.__name__ + ".sampling")
+    p0 = np.array([0.5, 0.25, 0.125, 0.125])
+    q0 = np.array([0.25, 0.5, 0.125, 0.125])
+    if mod.decide_margins([p0, np.full(4, 0.25)], [q0], [1], [0.75, 0.375]) != (0.25, 0.375):
+        return False
+    rng = np.random.default_rng(8)
+    try:
+        for _ in range(60):
+            zt, zd = _rows(12, 3, int(rng.integers(1 << 30)), noise=1.0)
+            p_rows = [mod.softmax_t(zt[i], 1.0) for i in range(4)]
+            q_rows = [mod.softmax_t(zd[i], 1.0) for i in range(3)]
+            d = [int(rng.choice(12, p=q_rows[i])) for i in range(3)]
+            _flip_checks(p_rows, q_rows, d, rng.random(4), S=mod)
+    except AssertionError:
+        return False
+    return True
+
+
+def _pin_commit(orc):
+    from tests.test_oracle_driver import pin_commit
+    try:
+        return pin_commit(orc)
+    except (AssertionError, IndexError):
+        return False
+
+
 MUTANTS = [
     ("budget.py", "frac = -((-s_num * L) // s_den)", "frac = (s_num * L) // s_den", _pin_budget),
     ("budget.py", "return min(L, max(newest, frac))", "return min(L, newest + frac)", _pin_budget),
@@ -131,6 +160,15 @@ MUTANTS = [
     ("cache.py", "k_pages[page, :, j % P, :] = k_rows[t]", "k_pages[page, :, j % P, :] = k_rows[n - 1 - t]", _pin_append),
     ("cache.py", "v_pages[page, :, j % P, :] = v_rows[t]", "v_pages[page, :, j % P, :] = k_rows[t]", _pin_append),
     ("cache.py", "page = int(bt_row[j // P])", "page = int(bt_row[j % P])", _pin_append),
+    ("sampling.py", "return float(min(t - lo, c[y] - t) / Z)", "return float((c[y] - t) / Z)", _pin_margins),
+    ("sampling.py", "ratio = min(ratio, abs(float(u[i]) * q - p) / max(p, q))",
+     "ratio = min(ratio, abs(float(u[i]) * q - p))", _pin_margins),
+    ("sampling.py", "lo = c[y - 1] if y > 0 else 0.0", "lo = c[y - 1] if y > 1 else 0.0", _pin_margins),
+    ("round.py", "L1 = int(L) + n_out", "L1 = int(L) + n_out - 1", _pin_commit),
+    ("round.py", "pending = int(np.asarray(tokens)[n_out - 1])", "pending = int(np.asarray(tokens)[n_out - 2])",
+     _pin_commit),
+    ("round.py", "return L1, pending, [L1 + j for j in range(1, k + 1)], L1 + k + 1",
+     "return L1, pending, [L1 + j for j in range(1, k + 1)], L1 + k", _pin_commit),
     ("select_variants.py", "key=lambda p: (-vals[p], p))", "key=lambda p: (-vals[p], -p))", _pin_pages),
     ("select_variants.py", "n_top = min(f, -(-max(0, n - wc) // unit))", "n_top = min(f, max(0, n - wc) // unit)",
      _pin_pages),
@@ -144,6 +182,7 @@ def test_unmutated_oracle_passes_pins():
     import oracle
     assert _pin_budget(oracle) and _pin_select(oracle) and _pin_verify(oracle) and _pin_decode(oracle)
     assert _pin_append(oracle) and _pin_pages(oracle) and _pin_all_heads(oracle)
+    assert _pin_margins(oracle) and _pin_commit(oracle)
 
 
 @pytest.mark.parametrize("case", range(len(MUTANTS)))

@@ -219,3 +219,71 @@ def test_expected_tokens_per_round():
             a1 = breakpoints(lambda u1: int(oracle.spec_sample(zt, zd, [x0, x1], [0.0, u1, 0.5], T)[2][1])).get(1, 0.0)
             tot += Q[0][x0] * Q[1][x1] * (1 + a0 + a0 * a1)
     assert abs(tot - exp_n) < 1e-12
+
+
+# ----------------------------------------------------------------- decision margins
+
+def test_margins_hand_built_rows():
+    # exact binary fractions: every margin below is exact
+    p0 = np.array([0.5, 0.25, 0.125, 0.125])
+    q0 = np.array([0.25, 0.5, 0.125, 0.125])
+    p1 = np.full(4, 0.25)
+    d = [1]
+    # accepted (0.25 * 0.5 < 0.25): ratio margin 0.125 / 0.5; bonus t = 0.5 lies on a CDF boundary
+    assert S.decide_margins([p0, p1], [q0], d, [0.25, 0.5]) == (0.25, 0.0)
+    # bonus t = 0.375: 0.125 from both ends of token 1's interval [0.25, 0.5)
+    assert S.decide_margins([p0, p1], [q0], d, [0.25, 0.375]) == (0.25, 0.125)
+    # rejected (0.75 * 0.5 >= 0.25): the residual keeps token 0 alone (weight 0.25), t = 0.375 * 0.25
+    assert S.decide_margins([p0, p1], [q0], d, [0.75, 0.375]) == (0.25, 0.375)
+    # greedy has no margin: it compares the float32 logits themselves
+    assert S.spec_margins(np.zeros((2, 4), np.float32), np.zeros((1, 4), np.float32), d, [0.5, 0.5], 0.0) is None
+
+
+def _flip_checks(p_rows, q_rows, d, u, S=S):
+    """The margins are distances to a flip: a change just below each leaves the decision,
+    a change just above it (towards the flip) changes it."""
+    rm, dm = S.decide_margins(p_rows, q_rows, d, u)
+    _, n_out, acc = S.spec_decide(p_rows, q_rows, d, u)
+    k = len(d)
+    reached = range(n_out if n_out <= k else k)
+    # the draft test closest to a flip
+    rel = [abs(float(u[i]) * q_rows[i][d[i]] - p_rows[i][d[i]]) / max(p_rows[i][d[i]], q_rows[i][d[i]]) for i in reached]
+    i = int(np.argmin(rel))
+    x = int(d[i])
+    scale = max(p_rows[i][x], q_rows[i][x])
+    towards = -1.0 if acc[i] == 1 else 1.0  # lower p to reject, raise p to accept
+    for f, flips in ((0.99, False), (1.01, True)):
+        pr = [r.copy() for r in p_rows]
+        pr[i][x] = p_rows[i][x] + towards * f * rm * scale
+        _, _, a2 = S.spec_decide(pr, q_rows, d, u)
+        assert (a2[i] != acc[i]) == flips, (f, i)
+    # the final draw: u_k moved by just under the draw margin keeps the token; moved by just over
+    # it, towards one end or the other, changes it
+    tok = S.spec_decide(p_rows, q_rows, d, u)[0][n_out - 1]
+    for sgn in (-1.0, 1.0):
+        u2 = np.array(u, dtype=np.float64)
+        u2[k] = u[k] + sgn * 0.99 * dm
+        if 0.0 <= u2[k] < 1.0:
+            assert S.spec_decide(p_rows, q_rows, d, u2)[0][n_out - 1] == tok
+    changed = False
+    for sgn in (-1.0, 1.0):
+        u2 = np.array(u, dtype=np.float64)
+        u2[k] = u[k] + sgn * 1.01 * dm
+        if 0.0 <= u2[k] < 1.0:
+            changed |= S.spec_decide(p_rows, q_rows, d, u2)[0][n_out - 1] != tok
+    return changed
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_margins_are_distances_to_a_flip(seed):
+    rng = np.random.default_rng(100 + seed)
+    k, V = 3, 12
+    changed = 0
+    for _ in range(150):
+        zt, zd = _rows(V, k, int(rng.integers(1 << 30)), noise=1.0)
+        p_rows = [S.softmax_t(zt[i], 1.0) for i in range(k + 1)]
+        q_rows = [S.softmax_t(zd[i], 1.0) for i in range(k)]
+        d = [int(rng.choice(V, p=q_rows[i])) for i in range(k)]
+        u = rng.random(k + 1)
+        changed += _flip_checks(p_rows, q_rows, d, u)
+    assert changed >= 120  # the nearer end is inside [0, 1) in most cases (not below token 0 or above the last)
