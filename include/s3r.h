@@ -116,10 +116,10 @@ int32_t s3r_budget(int32_t L, int32_t s_num, int32_t s_den, int32_t window);
 
 /*
  * s3r_select - newest window plus top-scoring older positions, per (sequence,
- * KV head). [explainer], mechanism paragraph: the drafter reads the newest
- * positions plus the top-scoring ones from the verifier's last attention pass,
- * refreshed after every round; [news], Interpretation: drafting selects a
- * small set of historical KV entries using attention scores.
+ * KV head). [explainer], mechanism paragraph: the set the drafter reads is the
+ * most recent positions together with those the previous verification pass
+ * weighted most, chosen again at every round; [news], Interpretation: the
+ * draft attends to a small subset of the cached entries, picked by score.
  *
  *   scores    device f32 [B][Hkv][score_stride]: score of position j of each
  *             (sequence, KV head); only j < ctx_len[b] is read. NaN scores are
@@ -144,9 +144,9 @@ s3r_status s3r_select(const float* scores, int32_t score_stride, const int32_t* 
 
 /*
  * s3r_select_grouped - selection variants. [explainer], mechanism paragraph:
- * the drafter reads the newest positions plus the top-scoring pages of the
- * verifier's last attention pass; [news], Perspective: adaptive context
- * selection as a direction beyond the reported configuration.
+ * the kept set is described there as whole pages (recent ones plus those the
+ * previous verification weighted most); [news], Perspective: choosing the
+ * context adaptively is named as further work.
  *
  * Arguments as for s3r_select, plus:
  *   unit      1: single positions (the s3r_select rule);
@@ -179,8 +179,8 @@ s3r_status s3r_select_grouped(const float* scores, int32_t score_stride, const i
 /*
  * s3r_sparse_decode_attn - one sparse draft step. [news], Interpretation:
  * drafting uses the policy's own weights and attends to the selected KV
- * entries; [explainer], mechanism paragraph: k fast draft steps from the
- * sticky-noted pages.
+ * entries; [explainer], mechanism paragraph: k quick draft steps over the
+ * kept subset of the cache.
  *
  * For sequence b and query head h (KV head kv = h / (Hq / Hkv)) the attended
  * set is S = idx[b][kv][0 .. n_sel[b]) united with [sel_len[b], cur_len[b])
@@ -268,8 +268,8 @@ s3r_status s3r_verify_attn(const void* q, const s3r_paged_kv* kv, const int32_t*
  * The same verification in two calls, so that the scores, which only the
  * next round's selection reads, can be formed on another stream while the
  * output rows go on to sampling. [explainer], mechanism paragraph: the
- * selector's scores come from the verifier's last attention pass, refreshed
- * after every round.
+ * selector ranks positions by the attention of the previous verification
+ * pass, and the ranking is renewed at each round.
  *
  * s3r_verify_attn_deferred writes out and lse exactly as s3r_verify_attn and
  * leaves the score partials in ws. s3r_verify_scores then writes scores

@@ -1,9 +1,10 @@
 """KV selector: newest window plus the top-scoring older positions.
 
-[explainer], mechanism paragraph ending "...refreshed after every round":
-the sparse drafter reads the newest positions plus the top-scoring ones
-from the verifier's last attention pass. [news], Interpretation: drafting
-selects a small set of historical KV entries using attention scores.
+[explainer], mechanism paragraph: the positions the drafter reads are the
+most recent ones together with those the previous verification pass gave
+the most attention weight, chosen again at every round. [news],
+Interpretation: the draft attends to a small subset of the cached entries,
+picked by attention score.
 
 Readings where the pages are silent or disagree:
 * granularity is single positions (one page says "pages"; the others say

@@ -3,10 +3,10 @@ set per sequence from the scores of all its KV heads.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-[explainer], mechanism paragraph: the drafter reads the newest positions
-plus the top-scoring pages of the verifier's last attention pass, refreshed
-after every round. [news], Perspective: adaptive sparse budgets and context
-selection are named as directions beyond the reported configuration.
+[explainer], mechanism paragraph: the kept set is described as whole pages,
+the recent ones plus those the previous verification weighted most, chosen
+again each round. [news], Perspective: adapting the budget and the choice of
+context is named as further work.
 
 Readings (the pages name the variants, not their rules):
 * all heads: the score of position j for the sequence is the float32 sum of

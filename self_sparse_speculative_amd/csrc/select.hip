@@ -2,8 +2,8 @@
 // (sequence, KV head), in ascending position order.
 //
 // [explainer] "S3R - Self-sparse speculative rollouts for RL - What does it
-// mean?", mechanism paragraph: the sparse drafter reads the newest positions
-// plus the top-scoring ones from the verifier's last attention pass.
+// mean?", mechanism paragraph: the draft reads the most recent positions and
+// those that the previous verification pass weighted most.
 //
 // One workgroup (512 threads) per (KV head, sequence). Scores are mapped to
 // order-preserving 32-bit keys (-0.0 folded onto +0.0). A 12-bit histogram
@@ -520,8 +520,8 @@ hipError_t launch_select(const float* scores, int stride, const int* ctx_len, in
 }
 
 // ---------------------------------------------------------------------------
-// Selection variants. [explainer], mechanism paragraph: the drafter reads the
-// newest positions plus the top-scoring pages of the verifier's last pass.
+// Selection variants. [explainer], mechanism paragraph: the kept set is
+// described as whole pages, recent ones and those the verification favoured.
 //   all heads: one kept set per sequence from the float32 sum of its KV heads'
 //              scores (heads in ascending order), copied to every KV head;
 //   pages:     the newest min(window, L) positions are kept as whole pages

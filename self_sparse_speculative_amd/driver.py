@@ -21,8 +21,8 @@ in a HIP graph (torch.cuda.CUDAGraph) and replayed; every host-side bound
 over the whole run, given as ``max_len``.
 
 [explainer] "S3R - Self-sparse speculative rollouts for RL - What does it
-mean?", mechanism paragraph (k draft steps, one verification pass, scores
-refreshed every round) and Jargon "Block efficiency (tau)"; [news] "Long-
+mean?", mechanism paragraph (k draft steps, one verification pass, a new
+ranking of the cache after each round) and Jargon "Block efficiency (tau)"; [news] "Long-
 context RL training stops waiting on autoregressive rollouts...",
 Interpretation (verification recomputes the block against the full cache).
 """
