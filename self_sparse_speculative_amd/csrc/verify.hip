@@ -266,6 +266,21 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
       }
     }
 
+    // The sequence's last subtile: slots at and past S hold whatever the cache
+    // pool holds there. Their probabilities are 0, but 0 * NaN or 0 * Inf is NaN
+    // in the contraction below, so their V words are cleared. (Their K rows only
+    // reach logits that the causal mask above replaces by -inf.)
+    if (pos0 + kSub > S) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int a = (lane + 64 * tt) & 7;
+        const int first = pos0 + (a >> 2) * 16 + (a & 3) * 4;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (first + v >= S) cur.vraw[tt][v] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+
     // V^T into LDS: row d holds 32 slots; slot g*8 + pt*4 + v <- position pt*16 + 4g + v
     wave_lds_sync();  // the previous subtile's reads of the buffer precede these writes
 #pragma unroll

@@ -16,6 +16,7 @@ import self_sparse_speculative_amd as s3r
 from s3r_inputs import get_config, make_batch, make_round_inputs
 from self_sparse_speculative_amd.driver import RoundDriver
 from tests.gpu_util import rel_err_rows, to_dev, to_dev_storage
+from tests.poison import bits, poison_from
 
 pytestmark = pytest.mark.gpu
 
@@ -102,12 +103,20 @@ def _set_round(drv, ri):
                    torch.from_numpy(ri.u).cuda())
 
 
-@pytest.mark.parametrize("cid,B,lo,hi,R,unit,all_heads", [(1, 2, 480, 512, 4, 1, False), (2, 3, 300, 700, 3, 1, False),
-                                                         (2, 3, 300, 700, 3, 16, True), (1, 2, 480, 512, 3, 16, False)])
-def test_rounds_match_oracle_loop(cid, B, lo, hi, R, unit, all_heads):
+@pytest.mark.parametrize("cid,B,lo,hi,R,unit,all_heads,poison", [
+    (1, 2, 480, 512, 4, 1, False, False), (2, 3, 300, 700, 3, 1, False, False),
+    (2, 3, 300, 700, 3, 16, True, False), (1, 2, 480, 512, 3, 16, False, False),
+    # every position the run has not written yet holds NaN / Inf patterns (a pooled cache)
+    (3, 3, 4000, 5000, 3, 1, False, True), (1, 2, 480, 512, 3, 1, False, True)])
+def test_rounds_match_oracle_loop(cid, B, lo, hi, R, unit, all_heads, poison):
     cfg = get_config(cid, B=B)
     L0 = np.random.default_rng(9).integers(lo, hi + 1, size=B).astype(np.int64)
     b, drv = _setup(cfg, L0, R, unit, all_heads)
+    if poison:
+        # up to the end of each sequence's own pages (the rest of a shorter row maps to page 0)
+        poison_from(b.k_pages, b.v_pages, b.block_table, L0, (b.seq_len.astype(np.int64) + 15) // 16 * 16)
+        drv.kv.k_pages.copy_(to_dev_storage(b.k_pages))
+        drv.kv.v_pages.copy_(to_dev_storage(b.v_pages))
     k, bt, scale, T = cfg.k, b.block_table, float(b.scale), b.temperature
     bf16 = cfg.dtype == "bf16"
     kp, vp = b.k_pages.copy(), b.v_pages.copy()
@@ -153,7 +162,8 @@ def test_rounds_match_oracle_loop(cid, B, lo, hi, R, unit, all_heads):
             assert ctx[s] == L1 and pend[s] == pending and cur[:, s].tolist() == cl and seq[s] == sl
             L[s] = L1
             total += rn
-        assert np.array_equal(_host_pages(drv.kv.k_pages), kp) and np.array_equal(_host_pages(drv.kv.v_pages), vp)
+        assert np.array_equal(bits(_host_pages(drv.kv.k_pages)), bits(kp))
+        assert np.array_equal(bits(_host_pages(drv.kv.v_pages)), bits(vp))
     assert int(drv.verified.item()) == total
 
 
