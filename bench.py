@@ -393,15 +393,13 @@ def run_rollout(args, cfg, torch, s3r):
     def bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
+    from s3r_inputs.device import draw_pages_on_device
+
     layers = []
-    gen = torch.Generator(device="cuda")
     for l in range(L_layers):
         b = make_batch(cfg, layer=l, seed=args.seed, parts=("q", "scores"))
         assert np.array_equal(b.seq_len, seq_np)
-        gen.manual_seed(((args.seed * 1000003 + cfg.cid) * 1000003 + l) & ((1 << 63) - 1))
-        shape = (b.num_pages, Hkv, P, D)
-        kp = torch.empty(shape, dtype=torch.bfloat16, device="cuda").normal_(generator=gen)
-        vp = torch.empty(shape, dtype=torch.bfloat16, device="cuda").normal_(generator=gen)
+        kp, vp = draw_pages_on_device(cfg, b.num_pages, l, args.seed, torch)
         layers.append({"kv": s3r.PagedKV(kp, vp, torch.from_numpy(b.block_table).cuda()),
                        "q_draft": bf16(b.q_draft), "q_verify": bf16(b.q_verify),
                        "scores": torch.from_numpy(b.scores).cuda(), "num_pages": b.num_pages})

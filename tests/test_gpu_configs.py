@@ -1,0 +1,162 @@
+"""GPU parity at the launch shapes the sweep and rollout measurements time.
+
+* verification at k = 2, 4 and 8 on the fixed 24576-position context (7 splits
+  per (sequence, KV head); 12, 20 and 36 query rows per KV head: one, two and
+  three MFMA row tiles, the last with its queries in LDS);
+* selection and draft steps at the sweep's largest budget (s = 1/5, k = 8:
+  4916 kept positions, three draft splits merged);
+* speculative sampling on every sequence of every workload (configs 1-4 and
+  the sweep's draft-noise and draft-length points), bit-exact, with the
+  oracle's decision margins reported per workload and required to exceed
+  1e-12 (the float64 agreement of the kernel's exponential and summation
+  order with the oracle's);
+* the 28-layer rollout workload as the benchmark builds it (K/V pages drawn
+  on the device), full batch of 256, one middle layer: selection, draft steps
+  and verification for sequences of the first, a middle and the last prompt
+  group, against the oracle on the pages copied back.
+"""
+
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import self_sparse_speculative_amd as s3r
+from s3r_inputs import get_config, make_batch
+from tests.gpu_util import nsel_cap, rel_err_rows, run_draft_steps, run_select, run_verify, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+MARGIN_FLOOR = 1e-12
+
+
+def _check_verify(cfg, batch, out, lse, sc, seqs):
+    for b in seqs:
+        S = int(batch.seq_len[b])
+        ro, rl, rs = oracle.verify(batch.q_verify[b], batch.k_pages, batch.v_pages, batch.block_table[b], S, cfg.k,
+                                   float(batch.scale))
+        eo = rel_err_rows(out[b], ro)
+        es = float((np.abs(sc[b, :, :S] - rs).max(axis=1) / rs.max(axis=1)).max())
+        assert eo <= TOL_BF16 and es <= TOL_BF16, (b, eo, es)
+        assert np.abs(lse[b] - rl).max() <= 2e-3
+        print(f"  seq {b}: out {eo:.3g}, scores {es:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("k", [2, 4, 8])
+def test_verify_sweep_draft_lengths_at_24k(k):
+    cfg = get_config(5, B=2, k=k)
+    print(f"[sweep verify] k={k} R={(k + 1) * cfg.G} B=2 L=24576", flush=True)
+    batch = make_batch(cfg, parts=("kv", "q"))
+    t = to_dev(batch)
+    out, lse, sc = run_verify(cfg, batch, t)
+    torch.cuda.synchronize()
+    _check_verify(cfg, batch, out.cpu().numpy(), lse.cpu().numpy(), sc.cpu().numpy(), range(cfg.B))
+
+
+def test_select_and_draft_at_the_largest_sweep_budget():
+    cfg = get_config(5, B=2, k=8, s_num=1, s_den=5)
+    print("[sweep draft] s=1/5 k=8 B=2 L=24576", flush=True)
+    batch = make_batch(cfg, parts=("kv", "q", "scores"))
+    t = to_dev(batch)
+    order = torch.empty((cfg.B,), dtype=torch.int32, device="cuda")
+    idx, n_sel = run_select(cfg, batch, t, order=order)
+    outs = run_draft_steps(cfg, batch, t, idx, n_sel, order=order)
+    torch.cuda.synchronize()
+    idx_np, ns = idx.cpu().numpy(), n_sel.cpu().numpy()
+    for b in range(cfg.B):
+        L = int(batch.ctx_len[b])
+        for kv in range(cfg.Hkv):
+            ref = oracle.select(batch.scores[b, kv], L, cfg.s_num, cfg.s_den, cfg.window)
+            assert ns[b] == len(ref) and np.array_equal(idx_np[b, kv, :ns[b]], ref), (b, kv)
+        for j in (1, cfg.k):
+            ro, _ = oracle.sparse_decode(batch.q_draft[j - 1, b], batch.k_pages, batch.v_pages, batch.block_table[b],
+                                         idx_np[b], int(ns[b]), L, L + j, float(batch.scale))
+            assert rel_err_rows(outs[j - 1][0][b].cpu().numpy(), ro) <= TOL_BF16, (b, j)
+
+
+SAMPLING_WORKLOADS = [
+    ("config 1 (tiny, V=512)", 1, {}),
+    ("config 2 (Qwen3-1.7B layer, B=64)", 2, {}),
+    ("config 3 (Qwen3-8B layer, B=128)", 3, {}),
+    ("config 4 (rollout, B=256)", 4, {}),
+    ("config 5 sigma=0.1", 5, {"noise_std": 0.1}),
+    ("config 5 sigma=0.3", 5, {}),
+    ("config 5 sigma=0.6", 5, {"noise_std": 0.6}),
+    ("config 5 k=2", 5, {"k": 2}),
+    ("config 5 k=8", 5, {"k": 8}),
+]
+
+
+@pytest.mark.parametrize("name,cid,ov", SAMPLING_WORKLOADS, ids=[w[0] for w in SAMPLING_WORKLOADS])
+def test_spec_sample_every_sequence_with_margins(name, cid, ov):
+    cfg = get_config(cid, **ov)
+    print(f"[sampling] {name}: B={cfg.B} k={cfg.k} V={cfg.V}", flush=True)
+    batch = make_batch(cfg, parts=("logits",))
+    dev = torch.device("cuda")
+    zt, zd = torch.from_numpy(batch.zt).to(dev), torch.from_numpy(batch.zd).to(dev)
+    toks, nout, acc = s3r.spec_sample(zt, zd, torch.from_numpy(batch.d).to(dev), torch.from_numpy(batch.u).to(dev),
+                                      float(batch.temperature))
+    torch.cuda.synchronize()
+    toks, nout, acc = toks.cpu().numpy(), nout.cpu().numpy(), acc.cpu().numpy()
+    T = batch.temperature
+
+    def one(b):
+        p_rows = [oracle.softmax_t(batch.zt[b, i], T) for i in range(cfg.k + 1)]
+        q_rows = [oracle.softmax_t(batch.zd[b, i], T) for i in range(cfg.k)]
+        rt, rn, ra = oracle.spec_decide(p_rows, q_rows, batch.d[b], batch.u[b])
+        return b, rt, rn, ra, oracle.decide_margins(p_rows, q_rows, batch.d[b], batch.u[b])
+
+    with ThreadPoolExecutor(8) as ex:
+        res = list(ex.map(one, range(cfg.B)))
+    rmin = dmin = np.inf
+    for b, rt, rn, ra, (rm, dm) in res:
+        assert nout[b] == rn and np.array_equal(toks[b], rt) and np.array_equal(acc[b], ra), b
+        rmin, dmin = min(rmin, rm), min(dmin, dm)
+    print(f"[margins] {name}: {cfg.B} sequences bit-exact, {int(nout.sum())} tokens; min ratio-test margin "
+          f"{rmin:.3e}, min draw margin {dmin:.3e}", flush=True)
+    assert rmin > MARGIN_FLOOR and dmin > MARGIN_FLOOR
+
+
+def test_rollout_benchmark_inputs_middle_layer():
+    """The rollout workload exactly as the benchmark times it: full batch of 256 (32 prompts x 8
+    responses, 1024-token prompt pages shared), pages drawn on the device, layer 14."""
+    from s3r_inputs.device import draw_pages_on_device
+    cfg = get_config(4)
+    layer = 14
+    print(f"[rollout] layer {layer}, B={cfg.B}, pages drawn on the device", flush=True)
+    batch = make_batch(cfg, layer=layer, parts=("q", "scores"))
+    kp, vp = draw_pages_on_device(cfg, batch.num_pages, layer, 0, torch)
+    t = to_dev(batch)
+    t["kv"] = s3r.PagedKV(kp, vp, torch.from_numpy(batch.block_table).cuda())
+    order = torch.empty((cfg.B,), dtype=torch.int32, device="cuda")
+    idx, n_sel = run_select(cfg, batch, t, order=order)
+    outs = run_draft_steps(cfg, batch, t, idx, n_sel, order=order)
+    vout, vlse, vsc = run_verify(cfg, batch, t)
+    torch.cuda.synchronize()
+    idx_np, ns = idx.cpu().numpy(), n_sel.cpu().numpy()
+    vout, vlse, vsc = vout.cpu().numpy(), vlse.cpu().numpy(), vsc.cpu().numpy()
+    group = cfg.lengths[5]
+    seqs = [0] + list(range(16 * group, 17 * group)) + [cfg.B - 1]
+    for b in seqs:
+        L, S = int(batch.ctx_len[b]), int(batch.seq_len[b])
+        npg = (S + 15) // 16
+        rows = torch.from_numpy(batch.block_table[b, :npg].astype(np.int64)).cuda()
+        hk = kp.index_select(0, rows).view(torch.int16).cpu().numpy().view(np.uint16)
+        hv = vp.index_select(0, rows).view(torch.int16).cpu().numpy().view(np.uint16)
+        bt = np.arange(npg, dtype=np.int32)
+        for kv in range(cfg.Hkv):
+            ref = oracle.select(batch.scores[b, kv], L, cfg.s_num, cfg.s_den, cfg.window)
+            assert ns[b] == len(ref) and np.array_equal(idx_np[b, kv, :ns[b]], ref), (b, kv)
+        for j in (1, cfg.k):
+            ro, _ = oracle.sparse_decode(batch.q_draft[j - 1, b], hk, hv, bt, idx_np[b], int(ns[b]), L, L + j,
+                                         float(batch.scale))
+            assert rel_err_rows(outs[j - 1][0][b].cpu().numpy(), ro) <= TOL_BF16, (b, j)
+        ro, rl, rs = oracle.verify(batch.q_verify[b], hk, hv, bt, S, cfg.k, float(batch.scale))
+        eo = rel_err_rows(vout[b], ro)
+        es = float((np.abs(vsc[b, :, :S] - rs).max(axis=1) / rs.max(axis=1)).max())
+        assert eo <= TOL_BF16 and es <= TOL_BF16, (b, eo, es)
+        assert np.abs(vlse[b] - rl).max() <= 2e-3
+    print(f"[rollout] {len(seqs)} sequences checked (groups 0, 16, 31)", flush=True)
