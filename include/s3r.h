@@ -324,6 +324,31 @@ s3r_status s3r_spec_sample(const float* target_logits, const float* draft_logits
                            hipStream_t stream);
 
 /*
+ * s3r_spec_sample_noalloc - s3r_spec_sample for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): no workspace argument, and no allocation in the
+ * call. Same arguments, kernels and results (bit for bit) as s3r_spec_sample.
+ *
+ * Its scratch is a fixed array of S3R_SAMPLE_SCRATCH_BYTES in the library's
+ * own device memory: each GPU the library runs on holds one copy until the
+ * process ends; its device address is looked up on the first call on that
+ * GPU (the GPU that runs `stream`). Every call on one GPU uses that GPU's
+ * copy: calls that overlap in time on one GPU (different streams, or host
+ * threads without ordering between them) race and give undefined results;
+ * calls ordered on one stream are safe. Nothing in it needs clearing between
+ * calls.
+ * S3R_ERR_WORKSPACE when s3r_spec_sample_workspace_bytes(B, k, V) exceeds
+ * S3R_SAMPLE_SCRATCH_BYTES (about 6700 sequences at k = 6, 5400 at k = 15);
+ * S3R_ERR_HIP also when the array's device address cannot be obtained;
+ * otherwise the statuses of s3r_spec_sample.
+ */
+#define S3R_SAMPLE_SCRATCH_BYTES ((size_t)8 << 20)
+s3r_status s3r_spec_sample_noalloc(const float* target_logits, const float* draft_logits,
+                                   const int32_t* draft_tokens, const float* uniforms, int32_t B, int32_t k,
+                                   int32_t V, float temperature, int32_t* tokens, int32_t* n_out,
+                                   int8_t* accepted, hipStream_t stream);
+
+/*
  * Multi-round driving: the two calls that join rounds on the device, so that
  * rounds follow each other without a host synchronisation (and can be
  * captured in a HIP graph together with the four calls above).

@@ -8,6 +8,7 @@ call does, and raises if it has not been built.
 
 from .s3r import (  # noqa: F401
     EXPORTED,
+    SAMPLE_SCRATCH_BYTES,
     PagedKV,
     S3RError,
     Workspace,
@@ -23,6 +24,7 @@ from .s3r import (  # noqa: F401
     sparse_decode_attn,
     sparse_decode_workspace_bytes,
     spec_sample,
+    spec_sample_noalloc,
     spec_sample_workspace_bytes,
     status_string,
     verify_attn,

@@ -223,6 +223,22 @@ s3r_status s3r_spec_sample(const float* target_logits, const float* draft_logits
                                           V, temperature, tokens, n_out, accepted, ws, stream));
 }
 
+s3r_status s3r_spec_sample_noalloc(const float* target_logits, const float* draft_logits,
+                                   const int32_t* draft_tokens, const float* uniforms, int32_t B, int32_t k,
+                                   int32_t V, float temperature, int32_t* tokens, int32_t* n_out,
+                                   int8_t* accepted, hipStream_t stream) {
+  if (!target_logits || !uniforms || !tokens || !n_out) return S3R_ERR_INVALID_ARG;
+  if (B < 1 || B > 65535 || V < 1 || k < 0 || k > kMaxK) return S3R_ERR_INVALID_ARG;
+  if (k > 0 && (!draft_logits || !draft_tokens)) return S3R_ERR_INVALID_ARG;
+  if (!(temperature >= 0.f) || !isfinite(temperature)) return S3R_ERR_INVALID_ARG;
+  if (s3r::sample_workspace_bytes(B, k, V) > s3r::kSampleScratchBytes) return S3R_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const hipError_t e = s3r::sample_scratch(stream, &ws);
+  if (e != hipSuccess) return S3R_ERR_HIP;
+  return from_hip(s3r::launch_spec_sample(target_logits, draft_logits, draft_tokens, uniforms, B, k, V,
+                                          temperature, tokens, n_out, accepted, ws, stream));
+}
+
 s3r_status s3r_kv_append(const void* k_rows, const void* v_rows, const s3r_paged_kv* kv,
                          const int32_t* pos, int32_t B, int32_t n, int32_t max_pos, hipStream_t stream) {
   if (!k_rows || !v_rows || !pos || !kv_ok(kv)) return S3R_ERR_INVALID_ARG;

@@ -86,6 +86,10 @@ hipError_t launch_verify_scores(int dtype, int D, const int* seq_len, int B, int
                                 hipStream_t stream);
 
 size_t sample_workspace_bytes(int B, int k, int V);
+// Device address, on the device that runs `stream`, of the sampling step's
+// library-owned scratch (kSampleScratchBytes per GPU); looked up once per device.
+constexpr size_t kSampleScratchBytes = (size_t)8 << 20;
+hipError_t sample_scratch(hipStream_t stream, void** ptr);
 hipError_t launch_spec_sample(const float* zt, const float* zd, const int* dtok, const float* u,
                               int B, int k, int V, float temperature, int* tokens, int* n_out,
                               int8_t* accepted, void* ws, hipStream_t stream);

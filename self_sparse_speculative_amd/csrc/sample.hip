@@ -26,6 +26,8 @@
 //      consecutive tokens, a block scan gives its starting cumulative weight,
 //      and the first token whose cumulative weight exceeds u * Z is taken.
 
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -484,6 +486,51 @@ hipError_t launch_spec_sample(const float* zt, const float* zd, const int* dtok,
   hipLaunchKernelGGL(final_draw_kernel, dim3(B), dim3(kSmpThreads), 0, stream, zt, zd, u, k, V, invT,
                      w.smax, w.ssum, w.desc, w.csum, tokens);
   return hipGetLastError();
+}
+
+}  // namespace s3r
+
+namespace s3r {
+
+// Scratch of the no-allocation entry point: the workspace of the kernels above
+// in the library's own device memory, a fixed array that every GPU the library
+// runs on holds until the process ends. In host code `scratch` is a host-side
+// stand-in, not a device address: its address on a device comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address reaches the kernels. Calls on one GPU share the array.
+static __device__ __align__(256) char scratch[kSampleScratchBytes];
+
+constexpr int kScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kScratchDevices] = {};
+
+hipError_t sample_scratch(hipStream_t stream, void** ptr) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t d = 0;
+    e = hipStreamGetDevice(stream, &d);
+    if (e != hipSuccess) return e;
+    dev = (int)d;
+  }
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace s3r

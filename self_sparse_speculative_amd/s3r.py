@@ -31,8 +31,9 @@ EXPORTED = (
     "s3r_sparse_decode_workspace_bytes", "s3r_sparse_decode_attn",
     "s3r_verify_workspace_bytes", "s3r_verify_attn", "s3r_verify_attn_deferred", "s3r_verify_scores",
     "s3r_spec_sample_workspace_bytes", "s3r_spec_sample", "s3r_kv_append", "s3r_commit",
-    "s3r_length_order",
+    "s3r_length_order", "s3r_spec_sample_noalloc",
 )
+SAMPLE_SCRATCH_BYTES = 8 << 20  # S3R_SAMPLE_SCRATCH_BYTES
 
 
 class PagedKVStruct(ctypes.Structure):
@@ -108,6 +109,8 @@ def load():
         L.s3r_spec_sample_workspace_bytes.argtypes = [i32, i32, i32]
         L.s3r_spec_sample.restype = ctypes.c_int
         L.s3r_spec_sample.argtypes = [vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
+        L.s3r_spec_sample_noalloc.restype = ctypes.c_int
+        L.s3r_spec_sample_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp]
         L.s3r_kv_append.restype = ctypes.c_int
         L.s3r_kv_append.argtypes = [vp, vp, ctypes.POINTER(PagedKVStruct), vp, i32, i32, i32, vp]
         L.s3r_commit.restype = ctypes.c_int
@@ -363,6 +366,20 @@ def spec_sample(target_logits, draft_logits, draft_tokens, uniforms, temperature
                              _ptr(draft_tokens) if k > 0 else None, _ptr(uniforms), B, k, V,
                              float(temperature), _ptr(tokens), _ptr(n_out), _ptr(accepted), _ptr(buf),
                              buf.numel(), _stream(stream)), "s3r_spec_sample")
+    return tokens, n_out, accepted
+
+
+def spec_sample_noalloc(target_logits, draft_logits, draft_tokens, uniforms, temperature, tokens, n_out,
+                        accepted=None, stream=None):
+    """s3r_spec_sample_noalloc: as spec_sample with caller-given outputs and the library's own scratch
+    (nothing is allocated, here or in the library)."""
+    L = load()
+    B, kp1, V = target_logits.shape
+    k = kp1 - 1
+    _check(L.s3r_spec_sample_noalloc(_ptr(target_logits), _ptr(draft_logits) if k > 0 else None,
+                                     _ptr(draft_tokens) if k > 0 else None, _ptr(uniforms), B, k, V,
+                                     float(temperature), _ptr(tokens), _ptr(n_out), _ptr(accepted),
+                                     _stream(stream)), "s3r_spec_sample_noalloc")
     return tokens, n_out, accepted
 
 

@@ -189,6 +189,24 @@ def test_sample_validation(lib):
     assert f(*args(k=0, zd=None, ws_b=0)) == WORKSPACE
 
 
+def test_sample_noalloc_validation(lib):
+    # every check before the scratch lookup: nothing here reaches a device
+    f = lib.s3r_spec_sample_noalloc
+    args = lambda B=4, k=6, V=1000, T=1.0, zd=FAKE, zt=FAKE: (zt, zd, FAKE, FAKE, B, k, V, T, FAKE, FAKE, None, None)
+    assert f(*args(k=16)) == INVALID
+    assert f(*args(V=0)) == INVALID
+    assert f(*args(B=0)) == INVALID
+    assert f(*args(T=float("nan"))) == INVALID
+    assert f(*args(zd=None)) == INVALID
+    assert f(*args(zt=None)) == INVALID
+    # a batch whose workspace exceeds the library's fixed scratch is refused
+    B = 1
+    while lib.s3r_spec_sample_workspace_bytes(B, 15, 1000) <= s3r.SAMPLE_SCRATCH_BYTES:
+        B += 256
+    assert f(*args(B=B, k=15)) == WORKSPACE
+    assert lib.s3r_spec_sample_workspace_bytes(5000, 15, 1000) <= s3r.SAMPLE_SCRATCH_BYTES  # the stated capacity
+
+
 def test_kv_append_validation(lib):
     f = lib.s3r_kv_append
     args = lambda kvs, n=7, B=4, mp=160, pos=FAKE, kr=FAKE: (kr, FAKE, ctypes.byref(kvs), pos, B, n, mp, None)
