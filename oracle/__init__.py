@@ -32,8 +32,8 @@ function is "parity unpinned".
 
 from .budget import budget  # noqa: F401
 from .select import select  # noqa: F401
-from .attention import attend, gather, sparse_decode, verify, dense_decode  # noqa: F401
+from .attention import attend, gather, sparse_decode, verify, dense_decode, page_scores  # noqa: F401
 from .sampling import softmax_t, invcdf, spec_decide, spec_sample, decide_margins, spec_margins  # noqa: F401
 from .round import commit  # noqa: F401
 from .cache import kv_append  # noqa: F401
-from .select_variants import grouped_count, select_grouped  # noqa: F401
+from .select_variants import grouped_count, select_grouped, select_by_page_scores  # noqa: F401

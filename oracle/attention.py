@@ -23,11 +23,18 @@ Conventions (readings, since the pages give no positions or head maps):
   nothing). The sum (not a max) over heads and rows is the reading adopted.
 * logits are scale * q.k with scale passed in by the caller (1/sqrt(D)).
 
+* page scores (the selector variant that keeps whole pages): the score of
+  page p of a KV head is the sum of the position scores of its positions
+  [16p, 16p + 16) that lie in the cache (the last page may be partial).
+
 Pins: explicit-loop brute force on tiny inputs; torch's fp64 scaled dot
 product attention (with the causal block mask and repeated KV heads) as a
 library special case; budget = L equals dense decode; k = 0 verification
 equals single-token decode; a single kept position returns that V row;
-constant keys return the mean of V; scores of each KV head sum to G(k+1).
+constant keys return the mean of V; scores of each KV head sum to G(k+1);
+page scores: an explicit loop over positions, the same G(k+1) total, unit 1
+returns the position scores, and a page's score moves only with the
+probabilities of its own positions.
 """
 
 import numpy as np
@@ -121,3 +128,14 @@ def verify(q, k_pages, v_pages, bt_row, seq_len: int, k: int, scale: float):
                 o[i, h], lse[i, h], p = attend(q[i, h], K[:last + 1], V[:last + 1], scale)
                 scores[kv, :last + 1] += p
     return o, lse, scores
+
+
+def page_scores(scores: np.ndarray, seq_len: int, unit: int = 16) -> np.ndarray:
+    """[Hkv][ceil(seq_len / unit)] float64: the sum of each page's position scores (positions
+    at and past seq_len are not in the cache and add nothing)."""
+    scores = np.asarray(scores, dtype=np.float64)
+    npg = -(-int(seq_len) // unit)
+    out = np.zeros((scores.shape[0], npg))
+    for p in range(npg):
+        out[:, p] = scores[:, p * unit:min((p + 1) * unit, int(seq_len))].sum(axis=1)
+    return out

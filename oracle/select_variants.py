@@ -25,6 +25,9 @@ Readings (the pages name the variants, not their rules):
 * the sums are float32 accumulated in the stated order, since the kernel
   takes its integer decisions on the same sums.
 
+select_by_page_scores takes the page keys as given (the verification's page
+scores) instead of forming them from position scores.
+
 Pins: with integer-valued scores (exact sums) the head sum equals an int64
 sum and the page choice equals a brute-force sort of int64 page sums; one
 KV head at unit 1 is the plain selection; the kept set is whole pages plus
@@ -76,9 +79,31 @@ def page_plan(L: int, s_num: int, s_den: int, window: int, unit: int = 16):
 def select_pages(key, L: int, s_num: int, s_den: int, window: int, unit: int = 16) -> np.ndarray:
     """Ascending kept positions when the older part of the cache is kept in whole pages (one key row)."""
     L = int(L)
+    f, _, _ = page_plan(L, s_num, s_den, window, unit)
+    return _keep_pages(page_sum(key, f * unit, unit), L, s_num, s_den, window, unit)
+
+
+def select_by_page_scores(page_rows, L: int, s_num: int, s_den: int, window: int, all_heads: bool,
+                          unit: int = 16):
+    """Kept positions of every KV head from scores given per page (page p covers positions
+    [unit p, unit p + unit)), by the whole-page rule above; with all_heads the page keys are the
+    float32 sum of the KV heads' page scores (ascending heads) and one set serves every head."""
+    L = int(L)
+    Hkv = len(page_rows)
+    f, _, _ = page_plan(L, s_num, s_den, window, unit)
+    for h in range(Hkv):
+        if any(math.isnan(float(v)) for v in np.asarray(page_rows[h][:f])):
+            raise ValueError("NaN score")
+    keys = [head_sum(page_rows, f)] if all_heads else [np.asarray(page_rows[h][:f], np.float32) for h in range(Hkv)]
+    sel = [_keep_pages(k_, L, s_num, s_den, window, unit) for k_ in keys]
+    return [sel[0]] * Hkv if all_heads else sel
+
+
+def _keep_pages(sums, L: int, s_num: int, s_den: int, window: int, unit: int) -> np.ndarray:
+    """The whole-page rule on the f candidate pages' keys `sums`: the n_top largest (ties to the
+    lower page) plus the window pages, as ascending positions."""
     f, wc, n_top = page_plan(L, s_num, s_den, window, unit)
-    sums = page_sum(key, f * unit, unit)  # the f full candidate pages
-    vals = [float(v) for v in sums]
+    vals = [float(v) for v in np.asarray(sums, dtype=np.float32)[:f]]
     order = sorted(range(f), key=lambda p: (-vals[p], p))
     kept = sorted(order[:n_top])
     pos = [j for p in kept for j in range(p * unit, (p + 1) * unit)] + list(range(f * unit, L))

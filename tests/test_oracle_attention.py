@@ -176,3 +176,27 @@ def test_bf16_widening_is_exact():
     assert np.signbit(vals[3])
     assert vals[4] == np.float32(3.3895314e38)
     assert vals[5] == np.float32(2.0 ** -133)
+
+
+def test_page_scores_are_sums_of_position_scores():
+    from s3r_inputs import get_config, make_batch
+    cfg = get_config(1, B=2, Hq=4, Hkv=2, D=16, k=3, lengths=("uniform", 40, 90))
+    bt = make_batch(cfg, parts=("kv", "q"))
+    for b in range(cfg.B):
+        S = int(bt.seq_len[b])
+        _, _, sc = oracle.verify(bt.q_verify[b], bt.k_pages, bt.v_pages, bt.block_table[b], S, cfg.k, float(bt.scale))
+        pg = oracle.page_scores(sc, S)
+        assert pg.shape == (cfg.Hkv, -(-S // 16))
+        # an explicit loop over the positions
+        ref = np.zeros_like(pg)
+        for h in range(cfg.Hkv):
+            for j in range(S):
+                ref[h, j // 16] += sc[h, j]
+        np.testing.assert_allclose(pg, ref, rtol=1e-14, atol=1e-16)
+        np.testing.assert_allclose(pg.sum(axis=1), cfg.G * (cfg.k + 1), rtol=1e-12)
+        assert np.array_equal(oracle.page_scores(sc, S, unit=1), sc[:, :S])
+        # a page moves only with its own positions
+        sc2 = sc.copy()
+        sc2[:, 17] += 1.0
+        d = oracle.page_scores(sc2, S) - pg
+        assert np.allclose(d[:, 1], 1.0) and np.abs(np.delete(d, 1, axis=1)).max() == 0

@@ -143,6 +143,40 @@ def _pin_commit(orc):
         return False
 
 
+def _pin_page_scores(orc):
+    from tests.test_oracle_attention import test_page_scores_are_sums_of_position_scores as pin
+    import tests.test_oracle_attention as ta
+    saved = ta.oracle
+    ta.oracle = orc
+    try:
+        pin()
+    except AssertionError:
+        return False
+    finally:
+        ta.oracle = saved
+    return True
+
+
+def _pin_page_select(orc):
+    from tests.test_oracle_select_variants import _brute_pages, _int_scores
+    rng = np.random.default_rng(4)
+    for all_heads in (False, True):
+        for L in (17, 300):
+            sc = _int_scores(rng, 3, L + 7, hi=6)
+            npg = -(-(L + 7) // 16)
+            pages = np.stack([[sc[h, 16 * p:16 * p + 16].astype(np.int64).sum() for p in range(npg)]
+                              for h in range(3)]).astype(np.float32)
+            try:
+                got = orc.select_by_page_scores(pages, L, 1, 5, 20, all_heads)
+            except IndexError:  # a slip that reads past the candidates fails the pin too
+                return False
+            for h in range(3):
+                key = sc.astype(np.int64).sum(axis=0) if all_heads else sc[h].astype(np.int64)
+                if got[h].tolist() != _brute_pages(key, L, 1, 5, 20):
+                    return False
+    return True
+
+
 MUTANTS = [
     ("budget.py", "frac = -((-s_num * L) // s_den)", "frac = (s_num * L) // s_den", _pin_budget),
     ("budget.py", "return min(L, max(newest, frac))", "return min(L, newest + frac)", _pin_budget),
@@ -164,6 +198,13 @@ MUTANTS = [
     ("sampling.py", "ratio = min(ratio, abs(float(u[i]) * q - p) / max(p, q))",
      "ratio = min(ratio, abs(float(u[i]) * q - p))", _pin_margins),
     ("sampling.py", "lo = c[y - 1] if y > 0 else 0.0", "lo = c[y - 1] if y > 1 else 0.0", _pin_margins),
+    ("attention.py", "out[:, p] = scores[:, p * unit:min((p + 1) * unit, int(seq_len))].sum(axis=1)",
+     "out[:, p] = scores[:, p * unit + 1:min((p + 1) * unit + 1, int(seq_len))].sum(axis=1)", _pin_page_scores),
+    ("attention.py", "npg = -(-int(seq_len) // unit)", "npg = int(seq_len) // unit", _pin_page_scores),
+    ("select_variants.py", "keys = [head_sum(page_rows, f)] if all_heads",
+     "keys = [np.asarray(page_rows[0][:f], np.float32)] if all_heads", _pin_page_select),
+    ("select_variants.py", "vals = [float(v) for v in np.asarray(sums, dtype=np.float32)[:f]]",
+     "vals = [float(v) for v in np.asarray(sums, dtype=np.float32)[1:f + 1]]", _pin_page_select),
     ("round.py", "L1 = int(L) + n_out", "L1 = int(L) + n_out - 1", _pin_commit),
     ("round.py", "pending = int(np.asarray(tokens)[n_out - 1])", "pending = int(np.asarray(tokens)[n_out - 2])",
      _pin_commit),
@@ -182,7 +223,7 @@ def test_unmutated_oracle_passes_pins():
     import oracle
     assert _pin_budget(oracle) and _pin_select(oracle) and _pin_verify(oracle) and _pin_decode(oracle)
     assert _pin_append(oracle) and _pin_pages(oracle) and _pin_all_heads(oracle)
-    assert _pin_margins(oracle) and _pin_commit(oracle)
+    assert _pin_margins(oracle) and _pin_commit(oracle) and _pin_page_scores(oracle) and _pin_page_select(oracle)
 
 
 @pytest.mark.parametrize("case", range(len(MUTANTS)))

@@ -90,3 +90,34 @@ def test_page_plan_at_the_24k_workload():
     # 24576 positions, s = 1/20 (1229 positions), window 64: 4 window pages plus 73 pages
     assert SV.page_plan(24576, 1, 20, 64) == (1532, 64, 73)
     assert oracle.grouped_count(24576, 1, 20, 64, 16) == 64 + 73 * 16
+
+
+@pytest.mark.parametrize("all_heads", [False, True])
+def test_selection_from_given_page_scores_on_exact_sums(all_heads):
+    # page scores that are the exact (integer) sums of integer position scores select what the
+    # whole-page rule selects from the position scores, and what brute force selects
+    rng = np.random.default_rng(5)
+    for L in (1, 16, 17, 250, 1500):
+        for (sn, sd, W) in ((1, 20, 64), (1, 5, 1), (1, 2, 30), (1, 20, 0)):
+            sc = _int_scores(rng, 3, L + 7, hi=6)
+            npg = -(-(L + 7) // 16)
+            pages = np.stack([[sc[h, 16 * p:16 * p + 16].astype(np.int64).sum() for p in range(npg)]
+                              for h in range(3)]).astype(np.float32)
+            got = oracle.select_by_page_scores(pages, L, sn, sd, W, all_heads)
+            ref = oracle.select_grouped(sc, L, sn, sd, W, 16, all_heads)
+            for h in range(3):
+                key = sc.astype(np.int64).sum(axis=0) if all_heads else sc[h].astype(np.int64)
+                assert got[h].tolist() == ref[h].tolist() == _brute_pages(key, L, sn, sd, W), (L, sn, sd, W, h)
+
+
+def test_selection_from_page_scores_ignores_pages_past_the_candidates():
+    # only the full pages older than the window are candidates: the window's pages and the pages
+    # of the block past L (which the verification scored) never change the choice
+    rng = np.random.default_rng(6)
+    L = 1000
+    pages = rng.random((2, 70)).astype(np.float32)
+    ref = oracle.select_by_page_scores(pages, L, 1, 20, 64, False)
+    f = (L - 64) // 16
+    pages[:, f:] = 1e30
+    got = oracle.select_by_page_scores(pages, L, 1, 20, 64, False)
+    assert all(np.array_equal(a, b) for a, b in zip(ref, got))
