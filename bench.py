@@ -57,6 +57,9 @@ def parse():
                          "growing lengths), eager and replayed from one captured HIP graph")
     ap.add_argument("--select-unit", type=int, default=1, choices=(1, 16),
                     help="selection granularity: single positions (1) or whole pages (16)")
+    ap.add_argument("--page-scores", action="store_true",
+                    help="the verification emits one score per page of 16 positions (s3r_verify_attn_pages) and the "
+                         "selection keeps whole pages ranked on them (s3r_select_pages); implies --select-unit 16")
     ap.add_argument("--select-all-heads", action="store_true",
                     help="one kept set per sequence from the summed scores of its KV heads")
     ap.add_argument("--adaptive-k", action="store_true",
@@ -157,9 +160,10 @@ def measure_round(args, cfg, batch, t, s3r, torch):
     B, k, Hq, Hkv, D = cfg.B, cfg.k, cfg.Hq, cfg.Hkv, cfg.D
     max_ctx = int(batch.ctx_len.max())
     max_seq = int(batch.seq_len.max())
-    plain_select = args.select_unit == 1 and not args.select_all_heads
+    pages = args.page_scores
+    plain_select = args.select_unit == 1 and not args.select_all_heads and not pages
     cap = s3r.budget(max_ctx, cfg.s_num, cfg.s_den, cfg.window) if plain_select else \
-        s3r.select_grouped_capacity(max_ctx, cfg.s_num, cfg.s_den, cfg.window, args.select_unit)
+        s3r.select_grouped_capacity(max_ctx, cfg.s_num, cfg.s_den, cfg.window, 16 if pages else args.select_unit)
     max_attend = cap + k
     scale = float(batch.scale)
     T = float(batch.temperature)
@@ -173,6 +177,8 @@ def measure_round(args, cfg, batch, t, s3r, torch):
     vout = torch.empty((B, k + 1, Hq, D), dtype=torch.float32, device="cuda")
     vlse = torch.empty((B, k + 1, Hq), dtype=torch.float32, device="cuda")
     scores = t["scores"]  # verification rewrites it for the next round's selection
+    if pages:  # one score per page; the first round's are the generator's U[0, 1) draws
+        scores = t["scores"][:, :, :(max_seq + 15) // 16].contiguous()
     tokens = torch.empty((B, k + 1), dtype=torch.int32, device="cuda")
     n_out = torch.empty((B,), dtype=torch.int32, device="cuda")
     accepted = torch.empty((B, k), dtype=torch.int8, device="cuda")
@@ -187,7 +193,10 @@ def measure_round(args, cfg, batch, t, s3r, torch):
     def step(ev=None, sev=None):
         if ev is not None:
             ev[0].record()
-        if plain_select:
+        if pages:
+            s3r.select_pages(scores, t["ctx_len"], max_ctx, cfg.s_num, cfg.s_den, cfg.window,
+                             all_heads=args.select_all_heads, idx=idx, n_sel=n_sel, ws=ws, order=order)
+        elif plain_select:
             s3r.select(scores, t["ctx_len"], max_ctx, cfg.s_num, cfg.s_den, cfg.window, idx=idx, n_sel=n_sel,
                        order=order)
         else:
@@ -201,7 +210,12 @@ def measure_round(args, cfg, batch, t, s3r, torch):
                                    out=dout, lse=dlse, ws=ws, order=order)
         if ev is not None:
             ev[2].record()
-        if not args.overlap_scores:
+        if pages:
+            s3r.verify_attn_pages(t["q_verify"], t["kv"], t["seq_len"], k, scale, max_seq, out=vout, lse=vlse,
+                                  page_scores=scores, ws=ws)
+            if ev is not None:
+                ev[3].record()
+        elif not args.overlap_scores:
             s3r.verify_attn(t["q_verify"], t["kv"], t["seq_len"], k, scale, max_seq, out=vout, lse=vlse,
                             scores=scores, ws=ws)
             if ev is not None:
@@ -257,11 +271,16 @@ def measure_round(args, cfg, batch, t, s3r, torch):
     kv_row = 2 * D * e  # one K row + one V row
     # the verify call on the launch stream: K and V rows, q, output rows and lse; in
     # the one-call form also the scores it writes
-    ver_bytes = int(Hkv * S.sum() * (kv_row + (0 if args.overlap_scores else 4)) + B * (k + 1) * Hq * (D * e + D * 4 + 4))
+    io_bytes = B * (k + 1) * Hq * (D * e + D * 4 + 4)
+    if pages:  # one score word per page written
+        ver_bytes = int(Hkv * S.sum() * kv_row + Hkv * ((S + 15) // 16).sum() * 4 + io_bytes)
+    else:
+        ver_bytes = int(Hkv * S.sum() * (kv_row + (0 if args.overlap_scores else 4)) + io_bytes)
     score_bytes = int(Hkv * S.sum() * 4)
     draft_bytes = int(sum(Hkv * (nsel_np.astype(np.int64) + j).sum() * (kv_row + 4) for j in range(1, k + 1))
                       + k * B * Hq * (D * e + D * 4 + 4))
-    sel_bytes = int(Hkv * L.sum() * 4 + Hkv * nsel_np.astype(np.int64).sum() * 4)
+    sel_read = ((L + 15) // 16).sum() if pages else L.sum()  # score words the selection reads
+    sel_bytes = int(Hkv * sel_read * 4 + Hkv * nsel_np.astype(np.int64).sum() * 4)
     smp_bytes = int(B * (2 * k + 1) * cfg.V * 4)
     kv_bytes = ver_bytes + draft_bytes
     kv_ms = t_ver + t_draft
@@ -578,10 +597,14 @@ def run_rounds(args, cfg, torch, s3r):
 
     def fresh():
         kv = s3r.PagedKV(st(b.k_pages), st(b.v_pages), torch.from_numpy(b.block_table).cuda())
-        drv = RoundDriver(kv, torch.from_numpy(L0.astype(np.int32)).cuda(), torch.from_numpy(b.scores).cuda(), k=k,
+        sc0 = torch.from_numpy(b.scores).cuda()
+        if args.page_scores:  # one first-round score per page: the generator's U[0, 1) draws
+            sc0 = sc0[:, :, :(max_len + 15) // 16].contiguous()
+        drv = RoundDriver(kv, torch.from_numpy(L0.astype(np.int32)).cuda(), sc0, k=k,
                           Hq=cfg.Hq, V=cfg.V, s_num=cfg.s_num, s_den=cfg.s_den, window=cfg.window,
                           scale=float(b.scale), temperature=float(b.temperature), max_len=max_len,
-                          select_unit=args.select_unit, select_all_heads=args.select_all_heads)
+                          select_unit=args.select_unit, select_all_heads=args.select_all_heads,
+                          page_scores=args.page_scores)
         drv.set_inputs(st(ri.q_draft), st(ri.k_draft), st(ri.v_draft), st(ri.q_verify), st(ri.k_block),
                        st(ri.v_block), st(ri.zt), st(ri.zd), st(ri.d), st(ri.u))
         drv.prepare()
@@ -785,6 +808,10 @@ def main():
     import self_sparse_speculative_amd as s3r
     from s3r_inputs import get_config, make_batch
 
+    if args.page_scores and args.overlap_scores:
+        print("bench.py: --page-scores and --overlap-scores do not combine (the deferred form keeps position "
+              "partials)", file=sys.stderr)
+        sys.exit(2)
     torch.cuda.set_device(0)
     if args.sweep:
         run_sweep(args, torch, s3r)
@@ -824,7 +851,7 @@ def main():
         return
     r = measure_round(args, cfg, batch, t, s3r, torch)
     traffic = load_traffic(os.path.join(ROOT, "self_sparse_speculative_amd", "csrc", "verify.hip"),
-                           "rows" if args.overlap_scores else "one_call")
+                           "pages" if args.page_scores else ("rows" if args.overlap_scores else "one_call"))
     copy_gbs, read_gbs = reference_rates(args, torch)
     cpu = None
     if not args.no_cpu:
@@ -851,15 +878,18 @@ def main():
             "workload": f"{cfg.name}: one attention layer, B={B}, Hq={Hq}, Hkv={Hkv}, head_dim={D}, {cfg.dtype} paged KV "
                         f"(page 16), context {cfg.lengths}, s={cfg.s_num}/{cfg.s_den}, window {cfg.window}, k={k}, "
                         f"V={cfg.V}, target N(0,{cfg.target_std}), draft noise {cfg.noise_std}, T={cfg.temperature}"
-                        + ("" if args.select_unit == 1 and not args.select_all_heads else
-                           f", selection of {'whole pages' if args.select_unit == 16 else 'positions'}"
+                        + ("" if args.select_unit == 1 and not args.select_all_heads and not args.page_scores else
+                           f", selection of {'whole pages' if args.select_unit == 16 or args.page_scores else 'positions'}"
+                           f"{' on scores per page from the verification' if args.page_scores else ''}"
                            f"{', one set per sequence from all KV heads' if args.select_all_heads else ''}"),
             "global_batch": B,
             "seq_len": r["max_seq"],
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": ("s3r_verify_attn: verify_mfma_kernel (split pass) + verify_finalize_kernel (merge, scores)"
+            "kernel": ("s3r_verify_attn_pages: verify_mfma_kernel (split pass, page masses) + verify_finalize_kernel "
+                       "(merge, page scores)" if args.page_scores else
+                       "s3r_verify_attn: verify_mfma_kernel (split pass) + verify_finalize_kernel (merge, scores)"
                        if not args.overlap_scores else
                        "s3r_verify_attn_deferred: verify_mfma_kernel (split pass) + verify_finalize_kernel (output merge)"),
             "bound": "hbm",

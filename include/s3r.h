@@ -177,6 +177,27 @@ s3r_status s3r_select_grouped(const float* scores, int32_t score_stride, const i
                               int32_t* order, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * s3r_select_pages - the whole-page selection of s3r_select_grouped (unit 16)
+ * from scores given per page, as s3r_verify_attn_pages writes them: the key of
+ * candidate page p is page_scores[b][kv][p] (all_heads: the float32 sum over
+ * the KV heads in ascending order) instead of the float32 sum of its 16
+ * position scores. The window pages, the count of kept pages, the tie rule
+ * and the output are those of s3r_select_grouped with unit 16.
+ *
+ *   page_scores device f32 [B][Hkv][page_stride]: only the candidate pages
+ *             p < floor((L_b - min(window, L_b)) / 16) are read;
+ *   page_stride >= ceil(max_ctx_len / 16);
+ *   nsel_cap  >= s3r_select_grouped_capacity(max_ctx_len, s_num, s_den, window, 16);
+ *   ws        s3r_select_grouped_workspace_bytes(B, Hkv, max_ctx_len, s_num,
+ *             s_den, window, 16, all_heads) bytes.
+ * Other arguments as for s3r_select_grouped.
+ */
+s3r_status s3r_select_pages(const float* page_scores, int32_t page_stride, const int32_t* ctx_len, int32_t B,
+                            int32_t Hkv, int32_t max_ctx_len, int32_t s_num, int32_t s_den, int32_t window,
+                            int32_t all_heads, int32_t* idx, int32_t nsel_cap, int32_t* n_sel, int32_t* order,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * s3r_sparse_decode_attn - one sparse draft step. [news], Interpretation:
  * drafting uses the policy's own weights and attends to the selected KV
  * entries; [explainer], mechanism paragraph: k quick draft steps over the
@@ -263,6 +284,33 @@ s3r_status s3r_verify_attn(const void* q, const s3r_paged_kv* kv, const int32_t*
                            int32_t B, int32_t k, int32_t Hq, float scale, int32_t max_seq_len,
                            float* out, float* lse, float* scores, int32_t score_stride, void* ws,
                            size_t ws_bytes, hipStream_t stream);
+
+/*
+ * s3r_verify_attn_pages - the verification with scores per page instead of
+ * per position, for selection in whole pages (s3r_select_pages). [explainer],
+ * mechanism paragraph: the drafter's set is described as the recent pages
+ * plus the pages the previous verification weighted most.
+ *
+ * out and lse exactly as s3r_verify_attn (the same arithmetic). The score of
+ * page p (positions [16 p, 16 p + 16) that lie below seq_len[b]) is the sum of
+ * the position scores of s3r_verify_attn over those positions:
+ *   page_scores[b][kv][p] = sum_{j in page p, j < seq_len[b]} scores[b][kv][j],
+ * for p < ceil(seq_len[b] / 16); later entries are not written. The split
+ * pass keeps one value per (page, query row) instead of one per (position,
+ * query row), so the pass writes 16x fewer partial bytes.
+ *
+ *   page_scores device f32 [B][Hkv][page_stride], required;
+ *   page_stride >= ceil(max_seq_len / 16);
+ *   ws        workspace of s3r_verify_pages_workspace_bytes(...) bytes (same
+ *             arguments as s3r_verify_workspace_bytes).
+ * Other arguments, statuses and UNSUPPORTED cases as for s3r_verify_attn.
+ */
+size_t s3r_verify_pages_workspace_bytes(int32_t B, int32_t k, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                        int32_t dtype, int32_t max_seq_len);
+s3r_status s3r_verify_attn_pages(const void* q, const s3r_paged_kv* kv, const int32_t* seq_len, int32_t B,
+                                 int32_t k, int32_t Hq, float scale, int32_t max_seq_len, float* out, float* lse,
+                                 float* page_scores, int32_t page_stride, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
 
 /*
  * The same verification in two calls, so that the scores, which only the

@@ -21,6 +21,7 @@ from .s3r import (  # noqa: F401
     select,
     select_grouped,
     select_grouped_capacity,
+    select_pages,
     sparse_decode_attn,
     sparse_decode_workspace_bytes,
     spec_sample,
@@ -29,6 +30,8 @@ from .s3r import (  # noqa: F401
     status_string,
     verify_attn,
     verify_attn_deferred,
+    verify_attn_pages,
+    verify_pages_workspace_bytes,
     verify_scores,
     verify_workspace_bytes,
 )

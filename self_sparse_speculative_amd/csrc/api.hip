@@ -109,6 +109,27 @@ s3r_status s3r_select_grouped(const float* scores, int32_t score_stride, const i
                                              window, unit, all_heads ? 1 : 0, idx, nsel_cap, n_sel, ws, stream));
 }
 
+s3r_status s3r_select_pages(const float* page_scores, int32_t page_stride, const int32_t* ctx_len, int32_t B,
+                            int32_t Hkv, int32_t max_ctx_len, int32_t s_num, int32_t s_den, int32_t window,
+                            int32_t all_heads, int32_t* idx, int32_t nsel_cap, int32_t* n_sel, int32_t* order,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!page_scores || !ctx_len || !idx || !n_sel) return S3R_ERR_INVALID_ARG;
+  if (B < 1 || Hkv < 1 || max_ctx_len < 1 || B > 65535 || Hkv > 65535) return S3R_ERR_INVALID_ARG;
+  if (s_den <= 0 || s_num < 0 || s_num > s_den || window < 0) return S3R_ERR_INVALID_ARG;
+  if (page_stride < (max_ctx_len + 15) / 16) return S3R_ERR_INVALID_ARG;
+  if (nsel_cap < 1 || nsel_cap < s3r::grouped_select_capacity(max_ctx_len, s_num, s_den, window, 16))
+    return S3R_ERR_INVALID_ARG;
+  const size_t need = s3r::grouped_select_plan(B, Hkv, max_ctx_len, s_num, s_den, window, 16,
+                                               all_heads ? 1 : 0).bytes;
+  if (ws_bytes < need || ws == nullptr) return S3R_ERR_WORKSPACE;
+  if (order != nullptr) {
+    const hipError_t e = s3r::launch_length_order(ctx_len, B, order, stream);
+    if (e != hipSuccess) return from_hip(e);
+  }
+  return from_hip(s3r::launch_select_pages(page_scores, page_stride, ctx_len, B, Hkv, max_ctx_len, s_num, s_den,
+                                           window, all_heads ? 1 : 0, idx, nsel_cap, n_sel, ws, stream));
+}
+
 size_t s3r_sparse_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head_dim, int32_t max_attend) {
   if (B < 1 || Hq < 1 || head_dim < 1 || max_attend < 1) return 0;
   return s3r::decode_workspace_bytes(B, Hq, head_dim, max_attend);
@@ -146,23 +167,33 @@ size_t s3r_verify_workspace_bytes(int32_t B, int32_t k, int32_t Hq, int32_t Hkv,
   if (B < 1 || k < 0 || k > kMaxK || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || head_dim < 1 ||
       max_seq_len < 1)
     return 0;
-  return s3r::verify_plan(B, k, Hq, Hkv, head_dim, dtype, max_seq_len).bytes;
+  return s3r::verify_plan(B, k, Hq, Hkv, head_dim, dtype, max_seq_len, false).bytes;
 }
 
-// Shared argument checks of the verification entry points.
+size_t s3r_verify_pages_workspace_bytes(int32_t B, int32_t k, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                        int32_t dtype, int32_t max_seq_len) {
+  if (B < 1 || k < 0 || k > kMaxK || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || head_dim < 1 ||
+      max_seq_len < 1)
+    return 0;
+  return s3r::verify_plan(B, k, Hq, Hkv, head_dim, dtype, max_seq_len, true).bytes;
+}
+
+// Shared argument checks of the verification entry points (pages: the
+// page-score form, whose scores hold one entry per page of 16 positions).
 static s3r_status verify_check(const s3r_paged_kv* kv, const int32_t* seq_len, int32_t B, int32_t k,
                                int32_t Hq, int32_t max_seq_len, float* scores, int32_t score_stride,
-                               void* ws, size_t ws_bytes) {
+                               void* ws, size_t ws_bytes, bool pages = false) {
   if (!kv_ok(kv) || !seq_len) return S3R_ERR_INVALID_ARG;
   if (B < 1 || B > 65535 || Hq < 1 || k < 0 || k > kMaxK || max_seq_len < k + 1) return S3R_ERR_INVALID_ARG;
   const int Hkv = kv->num_kv_heads;
   if (Hq % Hkv != 0 || Hkv > 65535) return S3R_ERR_INVALID_ARG;
   if ((long long)kv->max_pages_per_seq * kv->page_size < max_seq_len) return S3R_ERR_INVALID_ARG;
-  if (scores != nullptr && score_stride < max_seq_len) return S3R_ERR_INVALID_ARG;
+  const int need_stride = pages ? (max_seq_len + 15) / 16 : max_seq_len;
+  if (scores != nullptr && score_stride < need_stride) return S3R_ERR_INVALID_ARG;
   s3r_status st = kv_supported(kv);
   if (st != S3R_OK) return st;
   if ((k + 1) * (Hq / Hkv) > kMaxRows) return S3R_ERR_UNSUPPORTED;
-  const size_t need = s3r::verify_plan(B, k, Hq, Hkv, kv->head_dim, kv->dtype, max_seq_len).bytes;
+  const size_t need = s3r::verify_plan(B, k, Hq, Hkv, kv->head_dim, kv->dtype, max_seq_len, pages).bytes;
   if (ws_bytes < need || ws == nullptr) return S3R_ERR_WORKSPACE;
   return S3R_OK;
 }
@@ -177,7 +208,21 @@ s3r_status s3r_verify_attn(const void* q, const s3r_paged_kv* kv, const int32_t*
   return from_hip(s3r::launch_verify(kv->dtype, kv->head_dim, q, kv->k_pages, kv->v_pages,
                                      kv->block_table, kv->max_pages_per_seq, kv->num_kv_heads, seq_len,
                                      B, k, Hq, scale, max_seq_len, out, lse, scores, score_stride, false,
-                                     ws, stream));
+                                     false, ws, stream));
+}
+
+s3r_status s3r_verify_attn_pages(const void* q, const s3r_paged_kv* kv, const int32_t* seq_len, int32_t B,
+                                 int32_t k, int32_t Hq, float scale, int32_t max_seq_len, float* out, float* lse,
+                                 float* page_scores, int32_t page_stride, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  if (!q || !out || !page_scores || !isfinite(scale)) return S3R_ERR_INVALID_ARG;
+  const s3r_status st =
+      verify_check(kv, seq_len, B, k, Hq, max_seq_len, page_scores, page_stride, ws, ws_bytes, true);
+  if (st != S3R_OK) return st;
+  return from_hip(s3r::launch_verify(kv->dtype, kv->head_dim, q, kv->k_pages, kv->v_pages,
+                                     kv->block_table, kv->max_pages_per_seq, kv->num_kv_heads, seq_len,
+                                     B, k, Hq, scale, max_seq_len, out, lse, page_scores, page_stride, true,
+                                     false, ws, stream));
 }
 
 s3r_status s3r_verify_attn_deferred(const void* q, const s3r_paged_kv* kv, const int32_t* seq_len,
@@ -188,7 +233,7 @@ s3r_status s3r_verify_attn_deferred(const void* q, const s3r_paged_kv* kv, const
   if (st != S3R_OK) return st;
   return from_hip(s3r::launch_verify(kv->dtype, kv->head_dim, q, kv->k_pages, kv->v_pages,
                                      kv->block_table, kv->max_pages_per_seq, kv->num_kv_heads, seq_len,
-                                     B, k, Hq, scale, max_seq_len, out, lse, nullptr, 0, true, ws,
+                                     B, k, Hq, scale, max_seq_len, out, lse, nullptr, 0, false, true, ws,
                                      stream));
 }
 

@@ -69,17 +69,19 @@ hipError_t launch_length_order(const int* len, int B, int* order, hipStream_t st
 
 struct VerifyPlan {
   int G, R, NT, RP, chunk, nsplit, ntile_cap;
-  bool mfma;
-  size_t off_part_o, off_part_ml, off_sc_max, off_sc_val, bytes;
+  bool mfma, pages;
+  size_t off_part_o, off_part_ml, off_sc_max, off_sc_val, off_tmp, bytes;
 };
-VerifyPlan verify_plan(int B, int k, int Hq, int Hkv, int D, int dtype, int max_seq_len);
+// pages: the workspace of the page-score form (s3r_verify_attn_pages).
+VerifyPlan verify_plan(int B, int k, int Hq, int Hkv, int D, int dtype, int max_seq_len, bool pages);
 // Split pass + merge of the output rows. With scores != nullptr the scores
-// are written too; with defer_scores the score partials stay in ws for a
-// later launch_verify_scores (scores must then be nullptr).
+// are written too (pages: one per page of 16 positions); with defer_scores
+// the position-score partials stay in ws for a later launch_verify_scores
+// (scores must then be nullptr and pages false).
 hipError_t launch_verify(int dtype, int D, const void* q, const void* kp, const void* vp,
                          const int* bt, int max_pages, int Hkv, const int* seq_len, int B, int k,
                          int Hq, float scale, int max_seq_len, float* out, float* lse,
-                         float* scores, int score_stride, bool defer_scores, void* ws,
+                         float* scores, int score_stride, bool pages, bool defer_scores, void* ws,
                          hipStream_t stream);
 hipError_t launch_verify_scores(int dtype, int D, const int* seq_len, int B, int k, int Hq, int Hkv,
                                 int max_seq_len, float* scores, int score_stride, const void* ws,
@@ -101,6 +103,10 @@ struct GroupedSelectPlan {
 GroupedSelectPlan grouped_select_plan(int B, int Hkv, int max_ctx_len, int s_num, int s_den, int window,
                                       int unit, int all_heads);
 int grouped_select_capacity(int max_ctx_len, int s_num, int s_den, int window, int unit);
+// Whole-page selection from scores given per page (stride >= max_ctx_len / 16).
+hipError_t launch_select_pages(const float* page_scores, int stride, const int* ctx_len, int B, int Hkv,
+                               int max_ctx_len, int s_num, int s_den, int window, int all_heads, int* idx,
+                               int nsel_cap, int* n_sel, void* ws, hipStream_t stream);
 hipError_t launch_select_grouped(const float* scores, int stride, const int* ctx_len, int B, int Hkv,
                                  int max_ctx_len, int s_num, int s_den, int window, int unit, int all_heads,
                                  int* idx, int nsel_cap, int* n_sel, void* ws, hipStream_t stream);

@@ -598,6 +598,34 @@ __global__ __launch_bounds__(256) void group_keys_kernel(
   keys[((size_t)b * gridDim.z + g) * kstride + u] = v;
 }
 
+// Keys of the candidate pages from scores given per page (the page-score form
+// of the verification): one lane per page; the sum over the KV heads in
+// ascending order for one set per sequence. Also each sequence's plan.
+template <bool ALL>
+__global__ __launch_bounds__(256) void page_keys_kernel(
+    const float* __restrict__ page_scores, int stride, const int* __restrict__ ctx_len, int Hkv, int s_num,
+    int s_den, int window, float* __restrict__ keys, int kstride, int* __restrict__ units,
+    int* __restrict__ top, int* __restrict__ wcount) {
+  const int b = blockIdx.y, g = blockIdx.z;
+  const int u = blockIdx.x * 256 + threadIdx.x;
+  const PagePlan pp = page_plan(ctx_len[b], s_num, s_den, window);
+  if (u == 0 && g == 0) {
+    units[b] = pp.f;
+    top[b] = pp.ntop;
+    wcount[b] = pp.wc;
+  }
+  if (u >= pp.f) return;
+  const float* row = page_scores + (size_t)b * Hkv * stride;
+  float v;
+  if (ALL) {
+    v = 0.f;
+    for (int h = 0; h < Hkv; ++h) v += row[(size_t)h * stride + u];
+  } else {
+    v = row[(size_t)g * stride + u];
+  }
+  keys[((size_t)b * gridDim.z + g) * kstride + u] = v;
+}
+
 template <bool PAGES>
 __global__ __launch_bounds__(256) void expand_kernel(
     const int* __restrict__ sel_u, int cap_u, int G, const int* __restrict__ n_u, const int* __restrict__ units,
@@ -651,6 +679,33 @@ int grouped_select_capacity(int max_ctx_len, int s_num, int s_den, int window, i
   // at most window + 15 positions of window pages, and whole older pages
   // rounding the rest of the budget up by at most 15 positions
   return (int)min((long long)max_ctx_len, max(w + kPage - 1, n_max) + kPage - 1);
+}
+
+hipError_t launch_select_pages(const float* page_scores, int stride, const int* ctx_len, int B, int Hkv,
+                               int max_ctx_len, int s_num, int s_den, int window, int all_heads, int* idx,
+                               int nsel_cap, int* n_sel, void* ws, hipStream_t stream) {
+  const GroupedSelectPlan p = grouped_select_plan(B, Hkv, max_ctx_len, s_num, s_den, window, kPage, all_heads);
+  char* w = static_cast<char*>(ws);
+  float* keys = reinterpret_cast<float*>(w + p.off_keys);
+  int* units = reinterpret_cast<int*>(w + p.off_units);
+  int* top = reinterpret_cast<int*>(w + p.off_top);
+  int* wc = reinterpret_cast<int*>(w + p.off_wc);
+  int* sel = reinterpret_cast<int*>(w + p.off_sel);
+  int* nsel_u = reinterpret_cast<int*>(w + p.off_nsel);
+  const dim3 kgrid(ceil_div(p.kstride, 256), B, p.G);
+  if (all_heads)
+    hipLaunchKernelGGL(page_keys_kernel<true>, kgrid, dim3(256), 0, stream, page_scores, stride, ctx_len, Hkv,
+                       s_num, s_den, window, keys, p.kstride, units, top, wc);
+  else
+    hipLaunchKernelGGL(page_keys_kernel<false>, kgrid, dim3(256), 0, stream, page_scores, stride, ctx_len, Hkv,
+                       s_num, s_den, window, keys, p.kstride, units, top, wc);
+  const int cap = sampled_list_cap(p.kstride, p.cap_u);
+  hipLaunchKernelGGL(select_stream_kernel, dim3(p.G, B), dim3(kFsThreads), select_lds_bytes(cap), stream, keys,
+                     p.kstride, units, p.G, s_num, s_den, 0, sel, p.cap_u, nsel_u, (const int*)top, cap,
+                     (int*)nullptr);
+  hipLaunchKernelGGL(expand_kernel<true>, dim3(Hkv, B), dim3(256), 0, stream, sel, p.cap_u, p.G, nsel_u, units, wc,
+                     Hkv, idx, nsel_cap, n_sel);
+  return hipGetLastError();
 }
 
 hipError_t launch_select_grouped(const float* scores, int stride, const int* ctx_len, int B, int Hkv,

@@ -41,6 +41,8 @@
 // arrive, or by splits that exchange row statistics and keep their
 // probabilities on chip) measured slower on this part.
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -53,6 +55,9 @@ constexpr int kVerThreads = 256;
 constexpr int kVerWaves = kVerThreads / kWave;
 constexpr int kSub = 32;         // positions per subtile (two pages)
 constexpr int kVtStride = 40;    // LDS row stride (uint16) of a transposed V subtile: 32 slots + pad
+// The running reference maximum of a row is raised only when a logit exceeds
+// it by more than this (log2 units): probabilities stay below 2^8.
+constexpr float kLazyRescale = 8.f;
 
 // Floats per tile in the row-maxima record. Rounded up to whole 128 B lines
 // when that adds at most 12 floats, so no two tiles share a line and every
@@ -72,13 +77,18 @@ __device__ __forceinline__ uint32_t u4_word(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-template <int NT, bool QL>
+// Score partials the split kernel writes (SM): none; per position (fp16
+// probabilities relative to the row's reference maximum, plus that maximum per
+// tile); or per page (the log2 of the page's probability mass in the row).
+constexpr int kScoresNone = 0, kScoresPositions = 1, kScoresPages = 2;
+
+template <int NT, bool QL, int SM>
 __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
     const int* __restrict__ bt, int max_pages, int npairs, int Hkv, int G,
     const int* __restrict__ seq_len, int k, float scale_log2, int chunk, int nsplit, int ntile_cap,
-    int with_scores, float* __restrict__ part_o, float* __restrict__ part_ml,
-    _Float16* __restrict__ sc_val, float* __restrict__ sc_max) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, void* __restrict__ sc_val,
+    float* __restrict__ sc_max) {
   constexpr int D = 128;
   constexpr int RP = 16 * NT;
   __shared__ __attribute__((aligned(16))) uint16_t vt[kVerWaves][D * kVtStride];
@@ -189,7 +199,13 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
 
   Sub cur;
   if (wave < nsub) load_sub(wave, cur);
-  for (int st = wave; st < nsub; st += kVerWaves) {
+  // One subtile. EDGE: some position of it lies past some row's last one (the
+  // block's causal triangle, the end of the sequence), so the logits are
+  // masked; every row sees all positions of the earlier subtiles. (Rows past R
+  // then see logits 0 of their zero queries: they are never read.) The two
+  // forms are separate code, so the common one carries no mask arithmetic.
+  auto subtile = [&](int st, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     const int pos0 = c0 + st * kSub;
     const auto& kf = cur.kf;
     const auto& vraw = cur.vraw;
@@ -219,18 +235,28 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
       for (int pt = 0; pt < 2; ++pt) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int p = pos0 + pt * 16 + 4 * g4 + v;
           float x = s[pt][nt][v] * scale_log2;
-          x = p > row_last[nt] ? kNegInf : x;
+          if constexpr (EDGE) x = pos0 + pt * 16 + 4 * g4 + v > row_last[nt] ? kNegInf : x;
           s[pt][nt][v] = x;
           mx = fmaxf(mx, x);
         }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float mn = fmaxf(m_run[nt], mx);
-      const float base = mn == kNegInf ? 0.f : mn;
-      const float alpha = exp2f_fast(m_run[nt] - base);
+      // The probabilities are relative to a reference maximum m_run that is
+      // raised only when a row's logit exceeds it by more than kLazyRescale
+      // (log2 units), so they stay below 2^kLazyRescale and the rescale of the
+      // accumulators is skipped in nearly every subtile (a wave-uniform test).
+      // Rows without a finite logit so far keep -inf (their sums are 0).
+      if (__any(mx > m_run[nt] + kLazyRescale)) {
+        const float mn = mx > m_run[nt] + kLazyRescale ? mx : m_run[nt];
+        const float alpha = m_run[nt] == kNegInf ? 0.f : exp2f_fast(m_run[nt] - mn);
+        l_run[nt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) oacc[nt][dt] *= alpha;
+        m_run[nt] = mn;
+      }
+      const float base = m_run[nt] == kNegInf ? 0.f : m_run[nt];
       float pv[2][4];
       float psum = 0.f;
 #pragma unroll
@@ -241,28 +267,37 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
           psum += pv[pt][v];
         }
       }
-      l_run[nt] = l_run[nt] * alpha + psum;
-      m_run[nt] = mn;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) oacc[nt][dt] *= alpha;
+      l_run[nt] += psum;
       // B fragment of P^T: slots 0..3 -> first page, 4..7 -> second page
-      uint32_t w0 = pack_bf16x2(pv[0][0], pv[0][1]);
-      uint32_t w1 = pack_bf16x2(pv[0][2], pv[0][3]);
-      uint32_t w2 = pack_bf16x2(pv[1][0], pv[1][1]);
-      uint32_t w3 = pack_bf16x2(pv[1][2], pv[1][3]);
-      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-      u32x4_t pw = {w0, w1, w2, w3};
-      pf[nt] = __builtin_bit_cast(bf16x8_t, pw);
+      // (bf16, round to nearest even)
+      pf[nt] = bf16x8_t{(__bf16)pv[0][0], (__bf16)pv[0][1], (__bf16)pv[0][2], (__bf16)pv[0][3],
+                        (__bf16)pv[1][0], (__bf16)pv[1][1], (__bf16)pv[1][2], (__bf16)pv[1][3]};
 
       const int r = nt * 16 + n16;
-      if (with_scores && r < R) {
-        _Float16* dst = sc_val + ((bkv * ntile_cap + tile) * R + r) * kSub;
-        typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-        f16x4_t h0 = {(_Float16)pv[0][0], (_Float16)pv[0][1], (_Float16)pv[0][2], (_Float16)pv[0][3]};
-        f16x4_t h1 = {(_Float16)pv[1][0], (_Float16)pv[1][1], (_Float16)pv[1][2], (_Float16)pv[1][3]};
-        *reinterpret_cast<f16x4_t*>(dst + 4 * g4) = h0;
-        *reinterpret_cast<f16x4_t*>(dst + 16 + 4 * g4) = h1;
-        if (g4 == 0) sc_max[(bkv * ntile_cap + tile) * max_stride(R) + r] = base;
+      if constexpr (SM == kScoresPositions) {
+        if (r < R) {
+          _Float16* dst = static_cast<_Float16*>(sc_val) + ((bkv * ntile_cap + tile) * R + r) * kSub;
+          typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+          f16x4_t h0 = {(_Float16)pv[0][0], (_Float16)pv[0][1], (_Float16)pv[0][2], (_Float16)pv[0][3]};
+          f16x4_t h1 = {(_Float16)pv[1][0], (_Float16)pv[1][1], (_Float16)pv[1][2], (_Float16)pv[1][3]};
+          *reinterpret_cast<f16x4_t*>(dst + 4 * g4) = h0;
+          *reinterpret_cast<f16x4_t*>(dst + 16 + 4 * g4) = h1;
+          if (g4 == 0) sc_max[(bkv * ntile_cap + tile) * max_stride(R) + r] = base;
+        }
+      } else if constexpr (SM == kScoresPages) {
+        // Each of the subtile's two pages: the row's probability mass on it (the
+        // four lane groups' sums in a fixed order), kept as base + log2(mass)
+        // (-inf for none). Lanes of groups 0 and 1 write pages 2 tile and
+        // 2 tile + 1: one float per (page, row), every row of the tile.
+        float pa = (pv[0][0] + pv[0][1]) + (pv[0][2] + pv[0][3]);
+        float pb = (pv[1][0] + pv[1][1]) + (pv[1][2] + pv[1][3]);
+        pa += __shfl_xor(pa, 16, kWave);
+        pb += __shfl_xor(pb, 16, kWave);
+        pa += __shfl_xor(pa, 32, kWave);
+        pb += __shfl_xor(pb, 32, kWave);
+        const int page = 2 * tile + g4;
+        if (g4 < 2 && page * kPage < S)
+          static_cast<float*>(sc_val)[(bkv * 2 * ntile_cap + page) * RP + r] = base + __log2f(g4 == 0 ? pa : pb);
       }
     }
 
@@ -270,7 +305,7 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
     // pool holds there. Their probabilities are 0, but 0 * NaN or 0 * Inf is NaN
     // in the contraction below, so their V words are cleared. (Their K rows only
     // reach logits that the causal mask above replaces by -inf.)
-    if (pos0 + kSub > S) {
+    if (EDGE && pos0 + kSub > S) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int a = (lane + 64 * tt) & 7;
@@ -307,6 +342,12 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
         oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfrag, pf[nt], oacc[nt][dt], 0, 0, 0);
     }
     if (st + kVerWaves < nsub) load_sub(st + kVerWaves, cur);
+  };
+  for (int st = wave; st < nsub; st += kVerWaves) {
+    if (c0 + st * kSub + kSub - 1 > P0)
+      subtile(st, std::true_type{});
+    else
+      subtile(st, std::false_type{});
   }
 
   // Merge the waves: rows are lane % 16 (+16 nt); l is a per-lane partial.
@@ -475,25 +516,27 @@ __global__ __launch_bounds__(kVerThreads) void verify_generic_kernel(
 
 // Merge the splits of each (sequence, KV head) pair and normalise the score
 // partials. Blocks [0, nblk_o) each write 256 outputs of the merged rows;
-// the remaining blocks each normalise kFinTiles tiles of score partials.
-// Every block first merges the per-split (max, sum) of all rows, in split
-// order, so every value is computed the same way by every block.
+// the remaining blocks each normalise kFinTiles tiles of position partials
+// (PAGES: kVerThreads pages of page masses, one page per thread). Every
+// block first merges the per-split (max, sum) of all rows, in split order,
+// so every value is computed the same way by every block.
 constexpr int kFinTiles = kVerThreads / (kSub / 4);  // score tiles per finalize block (4 positions per thread)
 
-template <typename VT, int D>
+template <typename VT, int D, bool PAGES>
 __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, const VT* __restrict__ sc_val,
     const float* __restrict__ sc_max, const int* __restrict__ seq_len, int k, int Hkv, int G, int chunk,
     int nsplit, int ntile_cap, int RP, int nblk_o, int x0, float* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ scores, int score_stride) {
   __shared__ float mrow[64], lrow[64], l2row[64];
-  __shared__ float wt[kFinTiles][64];
+  __shared__ float wt[PAGES ? 1 : kFinTiles][64];
   const int pair = blockIdx.y, tid = threadIdx.x;
   const int b = pair / Hkv, kv = pair % Hkv;
   const int S = seq_len[b];
   const int x = x0 + (int)blockIdx.x;
   const int tile_beg = (x - nblk_o) * kFinTiles;
-  if (x >= nblk_o && tile_beg * kSub >= S) return;
+  const int page_beg = (x - nblk_o) * kVerThreads;
+  if (x >= nblk_o && (PAGES ? page_beg * kPage : tile_beg * kSub) >= S) return;
   const int used = min(nsplit, ceil_div(S, chunk));
   const int R = (k + 1) * G, Hq = Hkv * G;
   const size_t bkv = (size_t)pair;
@@ -538,6 +581,24 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
     }
     return;
   }
+  if constexpr (PAGES) {
+    // page score = sum over the rows of exp2(mass - log2 of the row's normaliser)
+    const int page = page_beg + tid;
+    if (page * kPage < S) {
+      const float4* m4 = reinterpret_cast<const float4*>(sc_val + (bkv * 2 * ntile_cap + page) * RP);
+      float acc = 0.f;
+      for (int r4 = 0; r4 < RP / 4; ++r4) {
+        const float4 m = m4[r4];
+        const int r = 4 * r4;
+        if (r < R) acc += exp2f_fast(m.x - l2row[r]);
+        if (r + 1 < R) acc += exp2f_fast(m.y - l2row[r + 1]);
+        if (r + 2 < R) acc += exp2f_fast(m.z - l2row[r + 2]);
+        if (r + 3 < R) acc += exp2f_fast(m.w - l2row[r + 3]);
+      }
+      scores[bkv * score_stride + page] = acc;
+    }
+    return;
+  }
   const int ntiles = ceil_div(S, kSub);
   const int tile_end = min(ntiles, tile_beg + kFinTiles);
   // weights of every (tile, row) of this block, then 4 positions per thread
@@ -571,11 +632,27 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-VerifyPlan verify_plan(int B, int k, int Hq, int Hkv, int D, int dtype, int max_seq_len) {
+// Page scores of the generic path: the position scores (staged in the
+// workspace, row stride `stride`) summed over each page in slot order.
+__global__ __launch_bounds__(256) void page_sum_kernel(const float* __restrict__ pos_scores, int stride,
+                                                       const int* __restrict__ seq_len, int Hkv,
+                                                       float* __restrict__ page_scores, int page_stride) {
+  const int pair = blockIdx.y;
+  const int S = seq_len[pair / Hkv];
+  const int page = blockIdx.x * 256 + threadIdx.x;
+  if (page * kPage >= S) return;
+  const float* row = pos_scores + (size_t)pair * stride;
+  float acc = 0.f;
+  for (int j = page * kPage; j < min(S, page * kPage + kPage); ++j) acc += row[j];
+  page_scores[(size_t)pair * page_stride + page] = acc;
+}
+
+VerifyPlan verify_plan(int B, int k, int Hq, int Hkv, int D, int dtype, int max_seq_len, bool pages) {
   VerifyPlan p;
   p.G = Hq / Hkv;
   p.R = (k + 1) * p.G;
   p.mfma = (dtype == 1 && D == 128);
+  p.pages = pages;
   p.NT = ceil_div(p.R, 16);
   p.RP = 16 * p.NT;
   // MFMA path: at most kVerChunkMfma positions per split; the kernel spreads
@@ -592,45 +669,70 @@ VerifyPlan verify_plan(int B, int k, int Hq, int Hkv, int D, int dtype, int max_
   off = align256(off + nbkv * p.nsplit * p.RP * D * sizeof(float));
   p.off_part_ml = off;
   off = align256(off + nbkv * p.nsplit * p.RP * 2 * sizeof(float));
-  p.off_sc_max = off;
-  off = align256(off + nbkv * p.ntile_cap * max_stride(p.R) * sizeof(float));
-  p.off_sc_val = off;
-  off = align256(off + nbkv * p.ntile_cap * p.R * kSub * (p.mfma ? sizeof(_Float16) : sizeof(float)));
+  p.off_tmp = 0;
+  if (pages && p.mfma) {
+    // one float per (page, row slot): 2 pages per subtile
+    p.off_sc_max = off;
+    p.off_sc_val = off;
+    off = align256(off + nbkv * 2 * p.ntile_cap * p.RP * sizeof(float));
+  } else {
+    p.off_sc_max = off;
+    off = align256(off + nbkv * p.ntile_cap * max_stride(p.R) * sizeof(float));
+    p.off_sc_val = off;
+    off = align256(off + nbkv * p.ntile_cap * p.R * kSub * (p.mfma ? sizeof(_Float16) : sizeof(float)));
+    if (pages) {  // generic path: position scores staged for the page sums
+      p.off_tmp = off;
+      off = align256(off + nbkv * (size_t)max_seq_len * sizeof(float));
+    }
+  }
   p.bytes = off;
   return p;
 }
 
-template <int NT>
-static void launch_mfma(const VerifyPlan& p, const void* q, const void* kp, const void* vp,
-                        const int* bt, int max_pages, int Hkv, const int* seq_len, int npairs, int k,
-                        float sl2, int with_scores, char* ws, hipStream_t stream) {
+template <int NT, int SM>
+static void launch_mfma_sm(const VerifyPlan& p, const void* q, const void* kp, const void* vp, const int* bt,
+                           int max_pages, int Hkv, const int* seq_len, int npairs, int k, float sl2, char* ws,
+                           hipStream_t stream) {
   const int nblocks = ceil_div(npairs, 8) * 8 * p.nsplit;
-  hipLaunchKernelGGL((verify_mfma_kernel<NT, kVerQLds && NT == 3>), dim3(nblocks), dim3(kVerThreads), 0, stream,
-                     (const bf16_t*)q, (const bf16_t*)kp, (const bf16_t*)vp, bt, max_pages, npairs, Hkv,
-                     p.G, seq_len, k, sl2, p.chunk, p.nsplit, p.ntile_cap, with_scores,
-                     (float*)(ws + p.off_part_o), (float*)(ws + p.off_part_ml),
-                     (_Float16*)(ws + p.off_sc_val), (float*)(ws + p.off_sc_max));
+  hipLaunchKernelGGL((verify_mfma_kernel<NT, kVerQLds && NT == 3, SM>), dim3(nblocks), dim3(kVerThreads), 0,
+                     stream, (const bf16_t*)q, (const bf16_t*)kp, (const bf16_t*)vp, bt, max_pages, npairs, Hkv,
+                     p.G, seq_len, k, sl2, p.chunk, p.nsplit, p.ntile_cap, (float*)(ws + p.off_part_o),
+                     (float*)(ws + p.off_part_ml), (void*)(ws + p.off_sc_val), (float*)(ws + p.off_sc_max));
 }
 
-// Finalize blocks [x0, x0 + nx) of the (output rows | score tiles) range.
+template <int NT>
+static void launch_mfma(const VerifyPlan& p, const void* q, const void* kp, const void* vp, const int* bt,
+                        int max_pages, int Hkv, const int* seq_len, int npairs, int k, float sl2, int sm, char* ws,
+                        hipStream_t stream) {
+  if (sm == kScoresPositions)
+    launch_mfma_sm<NT, kScoresPositions>(p, q, kp, vp, bt, max_pages, Hkv, seq_len, npairs, k, sl2, ws, stream);
+  else if (sm == kScoresPages)
+    launch_mfma_sm<NT, kScoresPages>(p, q, kp, vp, bt, max_pages, Hkv, seq_len, npairs, k, sl2, ws, stream);
+  else
+    launch_mfma_sm<NT, kScoresNone>(p, q, kp, vp, bt, max_pages, Hkv, seq_len, npairs, k, sl2, ws, stream);
+}
+
+// Finalize blocks [x0, x0 + nx) of the (output rows | score tiles or pages) range.
 static hipError_t launch_finalize(const VerifyPlan& p, int D, const int* seq_len, int npairs, int k,
                                   int Hkv, int x0, int nx, float* out, float* lse, float* scores,
                                   int score_stride, const char* ws, hipStream_t stream) {
   if (nx <= 0) return hipSuccess;
   const int nblk_o = ceil_div(p.R * D, kVerThreads);
   const dim3 grid(nx, npairs);
-#define S3R_FIN(VT, DD)                                                                              \
-  hipLaunchKernelGGL((verify_finalize_kernel<VT, DD>), grid, dim3(kVerThreads), 0, stream,          \
+#define S3R_FIN(VT, DD, PG)                                                                          \
+  hipLaunchKernelGGL((verify_finalize_kernel<VT, DD, PG>), grid, dim3(kVerThreads), 0, stream,      \
                      (const float*)(ws + p.off_part_o), (const float*)(ws + p.off_part_ml),          \
                      (const VT*)(ws + p.off_sc_val), (const float*)(ws + p.off_sc_max), seq_len, k,  \
                      Hkv, p.G, p.chunk, p.nsplit, p.ntile_cap, p.RP, nblk_o, x0, out, lse, scores,   \
                      score_stride)
-  if (p.mfma) {
-    S3R_FIN(_Float16, 128);
+  if (p.mfma && p.pages) {
+    S3R_FIN(float, 128, true);
+  } else if (p.mfma) {
+    S3R_FIN(_Float16, 128, false);
   } else if (D == 128) {
-    S3R_FIN(float, 128);
+    S3R_FIN(float, 128, false);
   } else {
-    S3R_FIN(float, 64);
+    S3R_FIN(float, 64, false);
   }
 #undef S3R_FIN
   return hipGetLastError();
@@ -639,16 +741,17 @@ static hipError_t launch_finalize(const VerifyPlan& p, int D, const int* seq_len
 hipError_t launch_verify(int dtype, int D, const void* q, const void* kp, const void* vp,
                          const int* bt, int max_pages, int Hkv, const int* seq_len, int B, int k,
                          int Hq, float scale, int max_seq_len, float* out, float* lse,
-                         float* scores, int score_stride, bool defer_scores, void* ws_v,
+                         float* scores, int score_stride, bool pages, bool defer_scores, void* ws_v,
                          hipStream_t stream) {
-  const VerifyPlan p = verify_plan(B, k, Hq, Hkv, D, dtype, max_seq_len);
+  const VerifyPlan p = verify_plan(B, k, Hq, Hkv, D, dtype, max_seq_len, pages);
   char* ws = (char*)ws_v;
   const float sl2 = scale * kLog2e;
   const int with_scores = (scores != nullptr || defer_scores) ? 1 : 0;
   const int npairs = B * Hkv;
   if (p.mfma) {
+    const int sm = !with_scores ? kScoresNone : (pages ? kScoresPages : kScoresPositions);
 #define S3R_MFMA(NTV) \
-  launch_mfma<NTV>(p, q, kp, vp, bt, max_pages, Hkv, seq_len, npairs, k, sl2, with_scores, ws, stream)
+  launch_mfma<NTV>(p, q, kp, vp, bt, max_pages, Hkv, seq_len, npairs, k, sl2, sm, ws, stream)
     switch (p.NT) {
       case 1: S3R_MFMA(1); break;
       case 2: S3R_MFMA(2); break;
@@ -674,15 +777,26 @@ hipError_t launch_verify(int dtype, int D, const void* q, const void* kp, const 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nblk_o = ceil_div(p.R * D, kVerThreads);
-  const int nblk_s = (scores != nullptr && !defer_scores) ? ceil_div(p.ntile_cap, kFinTiles) : 0;
-  return launch_finalize(p, D, seq_len, npairs, k, Hkv, 0, nblk_o + nblk_s, out, lse,
-                         defer_scores ? nullptr : scores, score_stride, ws, stream);
+  const bool now = scores != nullptr && !defer_scores;
+  if (pages && !p.mfma && now) {
+    // generic path: position scores into the workspace, then their page sums
+    float* pos = (float*)(ws + p.off_tmp);
+    e = launch_finalize(p, D, seq_len, npairs, k, Hkv, 0, nblk_o + ceil_div(p.ntile_cap, kFinTiles), out, lse, pos,
+                        max_seq_len, ws, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(page_sum_kernel, dim3(ceil_div(ceil_div(max_seq_len, kPage), 256), npairs), dim3(256), 0,
+                       stream, pos, max_seq_len, seq_len, Hkv, scores, score_stride);
+    return hipGetLastError();
+  }
+  const int nblk_s = !now ? 0 : (pages ? ceil_div(2 * p.ntile_cap, kVerThreads) : ceil_div(p.ntile_cap, kFinTiles));
+  return launch_finalize(p, D, seq_len, npairs, k, Hkv, 0, nblk_o + nblk_s, out, lse, now ? scores : nullptr,
+                         score_stride, ws, stream);
 }
 
 hipError_t launch_verify_scores(int dtype, int D, const int* seq_len, int B, int k, int Hq, int Hkv,
                                 int max_seq_len, float* scores, int score_stride, const void* ws,
                                 hipStream_t stream) {
-  const VerifyPlan p = verify_plan(B, k, Hq, Hkv, D, dtype, max_seq_len);
+  const VerifyPlan p = verify_plan(B, k, Hq, Hkv, D, dtype, max_seq_len, false);
   const int nblk_o = ceil_div(p.R * D, kVerThreads);
   return launch_finalize(p, D, seq_len, B * Hkv, k, Hkv, nblk_o, ceil_div(p.ntile_cap, kFinTiles), nullptr,
                          nullptr, scores, score_stride, (const char*)ws, stream);

@@ -39,18 +39,25 @@ class RoundDriver:
               (the pages are written by s3r_kv_append);
     ctx_len   int32 [B] device: committed lengths at the start (updated in place);
     scores    float32 [B][Hkv][stride >= max_len] device: first-round scores
-              (rewritten by every verification);
+              (rewritten by every verification); with page_scores, one score
+              per page of 16 positions ([B][Hkv][stride >= ceil(max_len / 16)]),
+              written by s3r_verify_attn_pages and read by s3r_select_pages;
     max_len   host bound on any sequence's cache length during the run
               (initial length + rounds * (k + 1)).
     """
 
     def __init__(self, kv: s3r.PagedKV, ctx_len: torch.Tensor, scores: torch.Tensor, *, k: int, Hq: int, V: int,
                  s_num: int, s_den: int, window: int, scale: float, temperature: float, max_len: int,
-                 select_unit: int = 1, select_all_heads: bool = False):
+                 select_unit: int = 1, select_all_heads: bool = False, page_scores: bool = False):
         dev = ctx_len.device
         B = ctx_len.shape[0]
         Hkv, D = kv.num_kv_heads, kv.head_dim
-        if scores.shape[0] != B or scores.shape[1] != Hkv or scores.shape[2] < max_len:
+        self.page_scores = bool(page_scores)
+        if self.page_scores:
+            select_unit = 16  # scores per page select whole pages
+            if scores.shape[0] != B or scores.shape[1] != Hkv or scores.shape[2] < (max_len + 15) // 16:
+                raise ValueError("page scores must be [B][Hkv][stride >= ceil(max_len / 16)]")
+        elif scores.shape[0] != B or scores.shape[1] != Hkv or scores.shape[2] < max_len:
             raise ValueError("scores must be [B][Hkv][stride >= max_len]")
         if kv.block_table.shape[1] * 16 < max_len:
             raise ValueError("the block table must cover max_len positions")
@@ -111,7 +118,11 @@ class RoundDriver:
     def step(self):
         """Enqueue one round on the current stream."""
         k, ml = self.k, self.max_len
-        if self.plain_select:
+        if self.page_scores:
+            s3r.select_pages(self.scores, self.ctx_len, ml, self.s_num, self.s_den, self.window,
+                             all_heads=self.select_all_heads, idx=self.idx, n_sel=self.n_sel, ws=self.ws,
+                             order=self.order)
+        elif self.plain_select:
             s3r.select(self.scores, self.ctx_len, ml, self.s_num, self.s_den, self.window, idx=self.idx,
                        n_sel=self.n_sel, order=self.order)
         else:
@@ -125,8 +136,12 @@ class RoundDriver:
                                    self.cur_len[j - 1], self.scale, self.max_attend, out=self.draft_out[j - 1],
                                    lse=self.draft_lse[j - 1], ws=self.ws, order=self.order)
         s3r.kv_append(self.k_block, self.v_block, self.kv, self.ctx_len, ml)
-        s3r.verify_attn(self.q_verify, self.kv, self.seq_len, k, self.scale, ml, out=self.ver_out,
-                        lse=self.ver_lse, scores=self.scores, ws=self.ws)
+        if self.page_scores:
+            s3r.verify_attn_pages(self.q_verify, self.kv, self.seq_len, k, self.scale, ml, out=self.ver_out,
+                                  lse=self.ver_lse, page_scores=self.scores, ws=self.ws)
+        else:
+            s3r.verify_attn(self.q_verify, self.kv, self.seq_len, k, self.scale, ml, out=self.ver_out,
+                            lse=self.ver_lse, scores=self.scores, ws=self.ws)
         s3r.spec_sample(self.zt, self.zd, self.d, self.u, self.temperature, tokens=self.tokens, n_out=self.n_out,
                         accepted=self.accepted if k > 0 else None, want_accepted=k > 0, ws=self.ws)
         s3r.commit(self.n_out, self.tokens, self.ctx_len, pending=self.pending,
@@ -141,7 +156,8 @@ class RoundDriver:
                 B, self.Hkv, self.max_len, self.s_num, self.s_den, self.window, self.select_unit,
                 int(self.select_all_heads)))))
         self.ws.get("decode", s3r.sparse_decode_workspace_bytes(B, Hq, D, self.max_attend))
-        self.ws.get("verify", s3r.verify_workspace_bytes(B, k, Hq, self.Hkv, D, self.kv.dtype_code, self.max_len))
+        wsb = s3r.verify_pages_workspace_bytes if self.page_scores else s3r.verify_workspace_bytes
+        self.ws.get("verify", wsb(B, k, Hq, self.Hkv, D, self.kv.dtype_code, self.max_len))
         self.ws.get("sample", s3r.spec_sample_workspace_bytes(B, k, self.V))
 
     def capture(self):

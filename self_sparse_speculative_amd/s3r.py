@@ -31,7 +31,8 @@ EXPORTED = (
     "s3r_sparse_decode_workspace_bytes", "s3r_sparse_decode_attn",
     "s3r_verify_workspace_bytes", "s3r_verify_attn", "s3r_verify_attn_deferred", "s3r_verify_scores",
     "s3r_spec_sample_workspace_bytes", "s3r_spec_sample", "s3r_kv_append", "s3r_commit",
-    "s3r_length_order", "s3r_spec_sample_noalloc",
+    "s3r_length_order", "s3r_spec_sample_noalloc", "s3r_verify_pages_workspace_bytes", "s3r_verify_attn_pages",
+    "s3r_select_pages",
 )
 SAMPLE_SCRATCH_BYTES = 8 << 20  # S3R_SAMPLE_SCRATCH_BYTES
 
@@ -99,6 +100,13 @@ def load():
         L.s3r_verify_attn.restype = ctypes.c_int
         L.s3r_verify_attn.argtypes = [vp, ctypes.POINTER(PagedKVStruct), vp, i32, i32, i32, f32, i32, vp,
                                       vp, vp, i32, vp, sz, vp]
+        L.s3r_verify_pages_workspace_bytes.restype = sz
+        L.s3r_verify_pages_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.s3r_verify_attn_pages.restype = ctypes.c_int
+        L.s3r_verify_attn_pages.argtypes = [vp, ctypes.POINTER(PagedKVStruct), vp, i32, i32, i32, f32, i32, vp,
+                                            vp, vp, i32, vp, sz, vp]
+        L.s3r_select_pages.restype = ctypes.c_int
+        L.s3r_select_pages.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, vp, i32, vp, vp, vp, sz, vp]
         L.s3r_verify_attn_deferred.restype = ctypes.c_int
         L.s3r_verify_attn_deferred.argtypes = [vp, ctypes.POINTER(PagedKVStruct), vp, i32, i32, i32, f32, i32,
                                                vp, vp, vp, sz, vp]
@@ -248,6 +256,28 @@ def select_grouped(scores, ctx_len, max_ctx_len, s_num, s_den, window, unit=16, 
     return idx, n_sel
 
 
+def select_pages(page_scores, ctx_len, max_ctx_len, s_num, s_den, window, all_heads=False, idx=None, n_sel=None,
+                 nsel_cap=None, ws=None, stream=None, order=None):
+    """s3r_select_pages: whole pages chosen on scores given per page (page_scores [B][Hkv][page_stride]).
+    Returns (idx [B][Hkv][cap], n_sel [B])."""
+    L = load()
+    B, Hkv, stride = page_scores.shape
+    if nsel_cap is None:
+        nsel_cap = idx.shape[2] if idx is not None else max(1, select_grouped_capacity(max_ctx_len, s_num, s_den,
+                                                                                        window, 16))
+    if idx is None:
+        idx = torch.empty((B, Hkv, nsel_cap), dtype=torch.int32, device=page_scores.device)
+    if n_sel is None:
+        n_sel = torch.empty((B,), dtype=torch.int32, device=page_scores.device)
+    nb = int(L.s3r_select_grouped_workspace_bytes(B, Hkv, int(max_ctx_len), int(s_num), int(s_den), int(window), 16,
+                                                  int(bool(all_heads))))
+    buf = _ws(ws, page_scores.device).get("select", max(nb, 1))
+    _check(L.s3r_select_pages(_ptr(page_scores), stride, _ptr(ctx_len), B, Hkv, int(max_ctx_len), int(s_num),
+                              int(s_den), int(window), int(bool(all_heads)), _ptr(idx), int(nsel_cap), _ptr(n_sel),
+                              _ptr(order), _ptr(buf), buf.numel(), _stream(stream)), "s3r_select_pages")
+    return idx, n_sel
+
+
 def sparse_decode_workspace_bytes(B, Hq, head_dim, max_attend) -> int:
     return int(load().s3r_sparse_decode_workspace_bytes(B, Hq, head_dim, max_attend))
 
@@ -306,6 +336,32 @@ def verify_attn(q, kv: PagedKV, seq_len, k, scale, max_seq_len, out=None, lse=No
                              int(max_seq_len), _ptr(out), _ptr(lse), _ptr(scores), stride, _ptr(buf),
                              buf.numel(), _stream(stream)), "s3r_verify_attn")
     return out, lse, scores
+
+
+def verify_pages_workspace_bytes(B, k, Hq, Hkv, D, dtype_code, max_seq_len) -> int:
+    return int(load().s3r_verify_pages_workspace_bytes(B, k, Hq, Hkv, D, dtype_code, max_seq_len))
+
+
+def verify_attn_pages(q, kv: PagedKV, seq_len, k, scale, max_seq_len, out=None, lse=None, page_scores=None,
+                      want_lse=True, page_stride=None, ws=None, stream=None):
+    """s3r_verify_attn_pages. q [B][k+1][Hq][D]. Returns (out, lse, page_scores [B][Hkv][page_stride])."""
+    L = load()
+    B, kp1, Hq, D = q.shape
+    assert kp1 == k + 1
+    Hkv = kv.num_kv_heads
+    if out is None:
+        out = torch.empty((B, k + 1, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, k + 1, Hq), dtype=torch.float32, device=q.device)
+    if page_scores is None:
+        stride = (int(max_seq_len) + 15) // 16 if page_stride is None else int(page_stride)
+        page_scores = torch.empty((B, Hkv, stride), dtype=torch.float32, device=q.device)
+    nb = verify_pages_workspace_bytes(B, k, Hq, Hkv, D, kv.dtype_code, int(max_seq_len))
+    buf = _ws(ws, q.device).get("verify", nb)
+    _check(L.s3r_verify_attn_pages(_ptr(q), ctypes.byref(kv.struct), _ptr(seq_len), B, int(k), Hq, float(scale),
+                                   int(max_seq_len), _ptr(out), _ptr(lse), _ptr(page_scores), page_scores.shape[2],
+                                   _ptr(buf), buf.numel(), _stream(stream)), "s3r_verify_attn_pages")
+    return out, lse, page_scores
 
 
 def verify_attn_deferred(q, kv: PagedKV, seq_len, k, scale, max_seq_len, out=None, lse=None, want_lse=True,

@@ -189,6 +189,28 @@ def test_sample_validation(lib):
     assert f(*args(k=0, zd=None, ws_b=0)) == WORKSPACE
 
 
+def test_verify_pages_and_select_pages_validation(lib):
+    kv = _kv()
+    ws = lib.s3r_verify_pages_workspace_bytes(4, 6, 32, 8, 128, 1, 160)
+    assert 0 < ws < lib.s3r_verify_workspace_bytes(4, 6, 32, 8, 128, 1, 160)
+    f = lib.s3r_verify_attn_pages
+    args = lambda stride=10, ws_b=ws, pg=FAKE, kvp=kv, ms=160: (FAKE, ctypes.byref(kvp), FAKE, 4, 6, 32,
+                                                              0.088, ms, FAKE, None, pg, stride, FAKE, ws_b, None)
+    assert f(*args(pg=None)) == INVALID               # page scores are required
+    assert f(*args(stride=9)) == INVALID              # ceil(160 / 16) = 10 pages
+    assert f(*args(ws_b=ws - 1)) == WORKSPACE
+    assert f(*args(kvp=_kv(page=8), ms=80, stride=5)) == UNSUPPORTED
+    g = lib.s3r_select_pages
+    sw = lib.s3r_select_grouped_workspace_bytes(4, 8, 160, 1, 20, 64, 16, 0)
+    cap = lib.s3r_select_grouped_capacity(160, 1, 20, 64, 16)
+    gargs = lambda stride=10, cap_=cap, ws_b=sw, sn=1: (FAKE, stride, FAKE, 4, 8, 160, sn, 20, 64, 0, FAKE, cap_,
+                                                        FAKE, None, FAKE, ws_b, None)
+    assert g(*gargs(stride=9)) == INVALID
+    assert g(*gargs(cap_=cap - 1)) == INVALID
+    assert g(*gargs(sn=21)) == INVALID
+    assert g(*gargs(ws_b=sw - 1)) == WORKSPACE
+
+
 def test_sample_noalloc_validation(lib):
     # every check before the scratch lookup: nothing here reaches a device
     f = lib.s3r_spec_sample_noalloc
