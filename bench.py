@@ -68,6 +68,10 @@ def parse():
     ap.add_argument("--cost-model", action="store_true",
                     help="round cost against dense decoding: dense single-token attention step, draft step and "
                          "verification timed on the workload, break-even tokens and acceptance, attention speedup")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="read ceiling of the attention kernels on the workload: the verification's and a draft "
+                         "step's read patterns with no arithmetic (s3r_read_*_pattern), beside the verification "
+                         "without scores, with page scores and with position scores, and the draft step")
     ap.add_argument("--copy-gib", type=float, default=2.0,
                     help="size of the device-to-device copy timed as the HBM reference (0 to skip)")
     return ap.parse_args()
@@ -302,6 +306,9 @@ def measure_round(args, cfg, batch, t, s3r, torch):
                     "verify": round(ver_gbs, 1),
                     "spec_sample": round(smp_bytes / (t_smp * 1e-3) / 1e9, 1),
                     "verify_scores_side_stream": None if t_scores is None else round(score_bytes / (t_scores * 1e-3) / 1e9, 1)},
+            "draft_kv_read_fraction": round(float(sum((nsel_np.astype(np.int64) + j).sum() for j in range(1, k + 1))
+                                                  / (k * (L + 1).sum())), 6) if k > 0 else None,
+            "accepted_prefix_fraction": round((verified / B - 1.0) / k, 6) if k > 0 else None,
             "draft_plus_verify_kv_GBs": round(kv_bytes / (kv_ms * 1e-3) / 1e9, 1),
             "draft_plus_verify_frac_of_hbm_peak": round(kv_bytes / (kv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "round_algorithmic_bytes": round_bytes,
@@ -345,12 +352,19 @@ def run_sweep(args, torch, s3r):
 
     from s3r_inputs import make_batch
     from s3r_inputs.configs import CONFIGS, SWEEP_K, SWEEP_S, SWEEP_SIGMA
+    from self_sparse_speculative_amd import cost_model as cm
+
     base = CONFIGS[5]
+    points = []
+    t_dense = None
     for k in SWEEP_K:
         cfg_k = replace(base, k=k)
         batch = make_batch(cfg_k, seed=args.seed)
         t = to_dev(batch, s3r, torch)
         scores0 = t["scores"].clone()
+        if t_dense is None:  # every point shares the 24576-position cache: one dense step for all
+            t_dense = time_dense_step(args, cfg_k, batch, t, torch, s3r)
+            print(json.dumps({"sweep": "qwen3-8b-24k", "dense_step_ms": round(t_dense, 4)}), flush=True)
         for sig in SWEEP_SIGMA:
             lb = make_batch(replace(cfg_k, noise_std=sig), seed=args.seed, parts=("logits",))
             for name in ("zt", "zd", "d", "u"):
@@ -360,11 +374,40 @@ def run_sweep(args, torch, s3r):
                 cfg = replace(cfg_k, s_num=s_num, s_den=s_den, noise_std=sig)
                 t["scores"].copy_(scores0)  # every point starts from the same first-round scores
                 r = measure_round(args, cfg, batch, t, s3r, torch)
+                br = r["breakdown"]
+                sp = br["tokens_per_sequence"] * t_dense / r["ms_step"]
+                points.append({"s": (s_num, s_den), "k": k, "sigma": sig, "a": br["accepted_prefix_fraction"],
+                               "rho": br["draft_kv_read_fraction"], "speedup": sp, "ms_per_step": r["ms_step"]})
                 print(json.dumps({"sweep": "qwen3-8b-24k", "s": f"{s_num}/{s_den}", "k": k, "sigma": sig,
                                   "value": round(r["value"], 1), "unit": "verified tokens/s",
-                                  "ms_per_step": round(r["ms_step"], 4), **r["breakdown"]}), flush=True)
+                                  "ms_per_step": round(r["ms_step"], 4), "speedup_over_dense": round(sp, 4),
+                                  **br}), flush=True)
         del t, batch
         torch.cuda.empty_cache()
+    # calibrated speedup model: the constant correction fitted on the extreme budgets, judged on the
+    # middle two (held out)
+    calib_s, held_s = {(1, 50), (1, 5)}, {(1, 20), (1, 10)}
+    tup = lambda p: (p["a"], p["rho"], p["k"], p["speedup"])
+    cal = [tup(p) for p in points if p["s"] in calib_s]
+    held = [tup(p) for p in points if p["s"] in held_s]
+    c = cm.fit_constant_correction(cal)
+    print(json.dumps({"sweep": "qwen3-8b-24k", "calibration": {
+        "model": "speedup = (1 + a k) / (k rho + 1 + c)", "fitted_on_budgets": ["1/50", "1/5"],
+        "held_out_budgets": ["1/20", "1/10"], "c": round(c, 4),
+        "mape_held_out_uncorrected_pct": round(cm.mape(held, 0.0), 2),
+        "mape_held_out_corrected_pct": round(cm.mape(held, c), 2),
+        "mape_calibration_corrected_pct": round(cm.mape(cal, c), 2)}}), flush=True)
+    # adaptive budget at k = 6, draft noise 0.3: the measured round times per budget and the
+    # acceptance-versus-budget curve through the listing's two points (synthetic logits make the
+    # measured acceptance independent of the budget)
+    curve = cm.acceptance_curve([(0.05, 0.804), (0.50, 0.967)])
+    t_round = {n / d: p["ms_per_step"] for p in points if p["k"] == 6 and p["sigma"] == 0.3 for n, d in [p["s"]]}
+    best, gains = cm.choose_budget(curve, t_round, t_dense, 6)
+    print(json.dumps({"sweep": "qwen3-8b-24k", "adaptive_budget": {
+        "k": 6, "acceptance_curve": "log-linear through (0.05, 0.804), (0.50, 0.967)",
+        "acceptance": {f"{s_:.2f}": round(curve(s_), 4) for s_ in sorted(t_round)},
+        "modelled_speedup": {f"{s_:.2f}": round(v, 4) for s_, v in sorted(gains.items())},
+        "chosen_s": best}}), flush=True)
 
 
 def rollout_unique_positions(seq_len, idx, n_sel, prefix, group, k):
@@ -422,12 +465,16 @@ def run_rollout(args, cfg, torch, s3r):
         layers.append({"kv": s3r.PagedKV(kp, vp, torch.from_numpy(b.block_table).cuda()),
                        "q_draft": bf16(b.q_draft), "q_verify": bf16(b.q_verify),
                        "scores": torch.from_numpy(b.scores).cuda(), "num_pages": b.num_pages})
+        if args.page_scores:  # one first-round score per page: the generator's U[0, 1) draws
+            layers[-1]["scores"] = layers[-1]["scores"][:, :, :(b.scores.shape[2] + 15) // 16].contiguous()
         del b
         print(f"[bench] layer {l + 1}/{L_layers} resident ({time.time() - t0:.0f} s, "
               f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB)", file=sys.stderr, flush=True)
 
     max_ctx, max_seq = int(ctx_np.max()), int(seq_np.max())
-    cap = s3r.budget(max_ctx, cfg.s_num, cfg.s_den, cfg.window)
+    pages = args.page_scores
+    cap = s3r.select_grouped_capacity(max_ctx, cfg.s_num, cfg.s_den, cfg.window, 16) if pages else \
+        s3r.budget(max_ctx, cfg.s_num, cfg.s_den, cfg.window)
     max_attend = cap + k
     ws = s3r.Workspace()
     idx = [torch.empty((B, Hkv, cap), dtype=torch.int32, device="cuda") for _ in range(L_layers)]
@@ -446,8 +493,12 @@ def run_rollout(args, cfg, torch, s3r):
         rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
         rec(0)
         for l, ly in enumerate(layers):
-            s3r.select(ly["scores"], ctx_len, max_ctx, cfg.s_num, cfg.s_den, cfg.window, idx=idx[l], n_sel=n_sel[l],
-                       order=order if l == 0 else None)
+            if pages:
+                s3r.select_pages(ly["scores"], ctx_len, max_ctx, cfg.s_num, cfg.s_den, cfg.window, idx=idx[l],
+                                 n_sel=n_sel[l], ws=ws, order=order if l == 0 else None)
+            else:
+                s3r.select(ly["scores"], ctx_len, max_ctx, cfg.s_num, cfg.s_den, cfg.window, idx=idx[l],
+                           n_sel=n_sel[l], order=order if l == 0 else None)
         rec(1)
         for j in range(k):
             for l, ly in enumerate(layers):
@@ -455,8 +506,12 @@ def run_rollout(args, cfg, torch, s3r):
                                        max_attend, out=dout, lse=dlse, ws=ws, order=order)
         rec(2)
         for ly in layers:
-            s3r.verify_attn(ly["q_verify"], ly["kv"], seq_len, k, scale, max_seq, out=vout, lse=vlse,
-                            scores=ly["scores"], ws=ws)
+            if pages:
+                s3r.verify_attn_pages(ly["q_verify"], ly["kv"], seq_len, k, scale, max_seq, out=vout, lse=vlse,
+                                      page_scores=ly["scores"], ws=ws)
+            else:
+                s3r.verify_attn(ly["q_verify"], ly["kv"], seq_len, k, scale, max_seq, out=vout, lse=vlse,
+                                scores=ly["scores"], ws=ws)
         rec(3)
         s3r.spec_sample(zt, zd, dtok, u, T, tokens=tokens, n_out=n_out, accepted=accepted, ws=ws)
         rec(4)
@@ -495,12 +550,13 @@ def run_rollout(args, cfg, torch, s3r):
     for l in range(L_layers):
         ix, ns = idx[l].cpu().numpy(), n_sel[l].cpu().numpy()
         vu, du = rollout_unique_positions(seq_np, ix, ns, prefix, group, k)
-        ver_log += Hkv * int(S.sum()) * (kv_row + 4) + ver_io
-        ver_uni += vu * kv_row + Hkv * int(S.sum()) * 4 + ver_io
+        score_words = Hkv * int(((S + 15) // 16).sum()) if pages else Hkv * int(S.sum())
+        ver_log += Hkv * int(S.sum()) * kv_row + score_words * 4 + ver_io
+        ver_uni += vu * kv_row + score_words * 4 + ver_io
         nsel = ns.astype(np.int64)
         draft_log += sum(Hkv * int((nsel + j).sum()) * (kv_row + 4) for j in range(1, k + 1)) + draft_io
         draft_uni += sum(d * kv_row + Hkv * int((nsel + j).sum()) * 4 for j, d in zip(range(1, k + 1), du)) + draft_io
-        sel_bytes += Hkv * int(L.sum()) * 4 + Hkv * int(nsel.sum()) * 4
+        sel_bytes += Hkv * int(((L + 15) // 16).sum() if pages else L.sum()) * 4 + Hkv * int(nsel.sum()) * 4
     smp_bytes = B * (2 * k + 1) * cfg.V * 4
     gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
     t_ver_launch = float(t_ver) / L_layers
@@ -548,7 +604,8 @@ def run_rollout(args, cfg, torch, s3r):
         "config": {
             "workload": f"{cfg.name}: {L_layers} stacked attention layers, B={B} ({B // group} prompts x {group} "
                         f"responses sharing a {prefix}-token prefix, page-aliased), Hq={Hq}, Hkv={Hkv}, head_dim={D}, "
-                        f"{cfg.dtype} paged KV (page {P}), responses lognormal(median {cfg.lengths[2]}, "
+                        f"{cfg.dtype} paged KV (page {P}), "
+                        f"{'scores and selection in whole pages, ' if pages else ''}responses lognormal(median {cfg.lengths[2]}, "
                         f"sigma {cfg.lengths[3]}) clipped to {cfg.lengths[4]}, s={cfg.s_num}/{cfg.s_den}, window "
                         f"{cfg.window}, k={k}, V={cfg.V}, one sampling step per round",
             "global_batch": B,
@@ -556,8 +613,10 @@ def run_rollout(args, cfg, torch, s3r):
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "s3r_verify_attn: verify_mfma_kernel (split pass) + verify_finalize_kernel (merge, scores), "
-                      "per layer; unique bytes (shared prefix once per group)",
+            "kernel": ("s3r_verify_attn_pages: verify_mfma_kernel (split pass with the last-split merge, page scores)"
+                       if pages else
+                       "s3r_verify_attn: verify_mfma_kernel (split pass) + verify_finalize_kernel (merge, scores)")
+                      + ", per layer; unique bytes (shared prefix once per group)",
             "bound": "hbm",
             "achieved": round(gbs(ver_uni_launch, t_ver_launch), 1),
             "peak": HBM_PEAK_GBS,
@@ -663,22 +722,14 @@ def run_rounds(args, cfg, torch, s3r):
     }
 
 
-def run_cost_model(args, cfg, batch, t, torch, s3r):
-    """The round's attention cost in dense decoding steps on this GPU (break-even and speedup)."""
-    from self_sparse_speculative_amd import cost_model as cm
-
-    r = measure_round(args, cfg, batch, t, s3r, torch)
-    k, B = cfg.k, cfg.B
-    ms = r["breakdown"]["ms"]
-    t_draft = ms["draft_k_steps"] / k
-    t_verify = ms["verify"]
-    # one dense decoding step of attention: the pending token's query over the whole cache
-    # (a block of one row, no scores)
+def time_dense_step(args, cfg, batch, t, torch, s3r):
+    """One dense decoding step of attention on the workload's cache: the pending token's query over
+    the whole cache (a verification of one row, no scores). Returns ms per step."""
     q1 = t["q_verify"][:, :1].contiguous()
     seq1 = (t["ctx_len"] + 1).to(torch.int32)
     max1 = int(batch.ctx_len.max()) + 1
     ws = s3r.Workspace()
-    out = torch.empty((B, 1, cfg.Hq, cfg.D), dtype=torch.float32, device="cuda")
+    out = torch.empty((cfg.B, 1, cfg.Hq, cfg.D), dtype=torch.float32, device="cuda")
     dense = lambda: s3r.verify_attn(q1, t["kv"], seq1, 0, float(batch.scale), max1, out=out, want_scores=False,
                                     want_lse=False, ws=ws)
     for _ in range(3):
@@ -690,7 +741,19 @@ def run_cost_model(args, cfg, batch, t, torch, s3r):
         dense()
     e1.record()
     torch.cuda.synchronize()
-    t_dense = e0.elapsed_time(e1) / args.steps
+    return e0.elapsed_time(e1) / args.steps
+
+
+def run_cost_model(args, cfg, batch, t, torch, s3r):
+    """The round's attention cost in dense decoding steps on this GPU (break-even and speedup)."""
+    from self_sparse_speculative_amd import cost_model as cm
+
+    r = measure_round(args, cfg, batch, t, s3r, torch)
+    k, B = cfg.k, cfg.B
+    ms = r["breakdown"]["ms"]
+    t_draft = ms["draft_k_steps"] / k
+    t_verify = ms["verify"]
+    t_dense = time_dense_step(args, cfg, batch, t, torch, s3r)
     tau = r["verified"] / B
     e = 2 if cfg.dtype == "bf16" else 4
     dense_bytes = int(cfg.Hkv * (batch.ctx_len.astype(np.int64) + 1).sum() * 2 * cfg.D * e)
@@ -707,6 +770,67 @@ def run_cost_model(args, cfg, batch, t, torch, s3r):
         "alpha_be": round(cm.break_even_acceptance(t_dense, k, t_draft, t_verify), 4),
         "attention_speedup": round(cm.speedup(tau, t_dense, k, t_draft, t_verify), 4),
         "attention_speedup_full_acceptance": round(cm.speedup(k + 1, t_dense, k, t_draft, t_verify), 4),
+    }
+
+
+def run_read_ceiling(args, cfg, batch, t, torch, s3r):
+    """Time the attention kernels against reads of the same bytes in the same launch shape."""
+    k, B, Hkv, D = cfg.k, cfg.B, cfg.Hkv, cfg.D
+    max_ctx, max_seq = int(batch.ctx_len.max()), int(batch.seq_len.max())
+    scale = float(batch.scale)
+    ws = s3r.Workspace()
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    S = batch.seq_len.astype(np.int64)
+    row = 2 * D * 2
+    ver_read = Hkv * int(((S + 31) // 32 * 32).sum()) * row  # whole subtiles, as the kernel reads them
+    ver_alg = Hkv * int(S.sum()) * row
+    idx, n_sel = s3r.select(t["scores"], t["ctx_len"], max_ctx, cfg.s_num, cfg.s_den, cfg.window)
+    cap = idx.shape[2]
+    cur1 = t["ctx_len"] + 1
+    torch.cuda.synchronize()
+    draft_rows = Hkv * int((n_sel.cpu().numpy().astype(np.int64) + 1).sum())
+    out = torch.empty((B, k + 1, cfg.Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, k + 1, cfg.Hq), dtype=torch.float32, device="cuda")
+    sc = torch.empty((B, Hkv, max_seq), dtype=torch.float32, device="cuda")
+    pg = torch.empty((B, Hkv, (max_seq + 15) // 16), dtype=torch.float32, device="cuda")
+    dout = torch.empty((B, cfg.Hq, D), dtype=torch.float32, device="cuda")
+    res = {
+        "verify_read_pattern": timed(lambda: s3r.read_verify_pattern(t["kv"], t["seq_len"], max_seq)),
+        "verify_no_scores": timed(lambda: s3r.verify_attn(t["q_verify"], t["kv"], t["seq_len"], k, scale, max_seq,
+                                                          out=out, lse=lse, want_scores=False, ws=ws)),
+        "verify_page_scores": timed(lambda: s3r.verify_attn_pages(t["q_verify"], t["kv"], t["seq_len"], k, scale,
+                                                                  max_seq, out=out, lse=lse, page_scores=pg, ws=ws)),
+        "verify_position_scores": timed(lambda: s3r.verify_attn(t["q_verify"], t["kv"], t["seq_len"], k, scale,
+                                                                max_seq, out=out, lse=lse, scores=sc, ws=ws)),
+        "draft_read_pattern": timed(lambda: s3r.read_draft_pattern(t["kv"], idx, n_sel, t["ctx_len"], cur1, cap + 1)),
+        "draft_step": timed(lambda: s3r.sparse_decode_attn(t["q_draft"][0], t["kv"], idx, n_sel, t["ctx_len"], cur1,
+                                                           scale, cap + k, out=dout, ws=ws)),
+    }
+    tbps = lambda nbytes, ms: round(nbytes / (ms * 1e-3) / 1e12, 3)
+    return {
+        "read_ceiling": cfg.name, "B": B, "k": k, "context": list(cfg.lengths),
+        "ms": {n: round(v, 4) for n, v in res.items()},
+        "TBps_on_kv_rows": {
+            "verify_read_pattern": tbps(ver_read, res["verify_read_pattern"]),
+            "verify_no_scores": tbps(ver_alg, res["verify_no_scores"]),
+            "verify_page_scores": tbps(ver_alg, res["verify_page_scores"]),
+            "verify_position_scores": tbps(ver_alg, res["verify_position_scores"]),
+            "draft_read_pattern": tbps(draft_rows * row, res["draft_read_pattern"]),
+            "draft_step": tbps(draft_rows * row, res["draft_step"]),
+        },
+        "bytes": {"verify_kv_rows": ver_alg, "verify_read_pattern": ver_read, "draft_kv_rows": draft_rows * row},
     }
 
 
@@ -848,6 +972,9 @@ def main():
 
     if args.cost_model:
         print(json.dumps(run_cost_model(args, cfg, batch, t, torch, s3r)))
+        return
+    if args.read_ceiling:
+        print(json.dumps(run_read_ceiling(args, cfg, batch, t, torch, s3r)))
         return
     r = measure_round(args, cfg, batch, t, s3r, torch)
     traffic = load_traffic(os.path.join(ROOT, "self_sparse_speculative_amd", "csrc", "verify.hip"),

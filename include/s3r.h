@@ -452,6 +452,30 @@ s3r_status s3r_commit(const int32_t* n_out, const int32_t* tokens, int32_t B, in
                       int32_t* pending, int32_t* cur_len, int32_t* seq_len, int64_t* verified,
                       hipStream_t stream);
 
+/*
+ * Measurement helpers (not part of the method): the HBM read patterns of the
+ * verification and of one draft step, for the read ceiling the attention
+ * kernels are measured against. Each reads exactly the K and V bytes the
+ * bf16 / head_dim 128 kernel of that call reads (whole 32-position subtiles
+ * of every sequence's cache; the kept rows plus [sel_len, cur_len)), in the
+ * same launch shape, performs no arithmetic on them, and writes one 32-bit
+ * checksum (an xor of the loaded words) per workgroup to sink so no load is
+ * dropped. The checksums carry no meaning beyond that.
+ *
+ *   s3r_read_verify_pattern: kv and seq_len as for s3r_verify_attn;
+ *   s3r_read_draft_pattern: kv, idx, nsel_cap, n_sel, sel_len, cur_len, B and
+ *             max_attend as for s3r_sparse_decode_attn (no order);
+ *   sink      device u32 of at least s3r_read_pattern_sink_words(B, Hkv,
+ *             max_seq_len or max_attend, draft = 0 or 1) words.
+ * UNSUPPORTED unless bf16, head_dim 128, page_size 16.
+ */
+size_t s3r_read_pattern_sink_words(int32_t B, int32_t Hkv, int32_t max_len, int32_t draft);
+s3r_status s3r_read_verify_pattern(const s3r_paged_kv* kv, const int32_t* seq_len, int32_t B, int32_t max_seq_len,
+                                   uint32_t* sink, size_t sink_words, hipStream_t stream);
+s3r_status s3r_read_draft_pattern(const s3r_paged_kv* kv, const int32_t* idx, int32_t nsel_cap,
+                                  const int32_t* n_sel, const int32_t* sel_len, const int32_t* cur_len, int32_t B,
+                                  int32_t max_attend, uint32_t* sink, size_t sink_words, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,6 +18,8 @@ from .s3r import (  # noqa: F401
     length_order,
     lib_path,
     load,
+    read_draft_pattern,
+    read_verify_pattern,
     select,
     select_grouped,
     select_grouped_capacity,

@@ -28,9 +28,36 @@ accepted, from the decisions of recent rounds, and pick the k that maximises
 the speedup above; a round of k drafts then outputs on average
 sum_{i=0..k} prod_{m<i} alpha_m tokens.
 
+Calibrated speedup ([digest], the section on the limits of the speedup
+claim; [listing], Figures 12 and 13 captions, Eq. 24 there, which the pages
+do not print): the speedup is modelled from the accepted-prefix fraction a
+(the share of the k drafts a round keeps on average, so a round outputs
+1 + a k tokens) and the effective draft KV-read fraction rho (the positions a
+draft step reads over the positions a dense step reads), with one constant
+correction fitted to profiled rounds. Reading adopted, in dense-step units:
+a round costs k rho for its draft steps plus one verification worth one
+dense step, plus the constant c that absorbs everything else (the
+verification's extra rows, selection, sampling, launch gaps):
+  speedup(a, rho; c) = (1 + a k) / (k rho + 1 + c),
+c = 0 being the uncorrected model. c is fitted by least squares on the
+calibration points' measured round costs (1 + a k) / speedup - (k rho + 1),
+and the model is judged by its mean absolute percentage error on held-out
+points, as the digest reports it (84.61 % -> 0.80 % for Qwen3-1.7B, 63.03 %
+-> 0.68 % for Qwen3-8B on the pages' hardware).
+
+Adaptive budget ([news], Perspective: adaptive sparse budgets named as a next
+step; [listing], Abstract and Figure 6: acceptance rises with the budget,
+80.4 % at s = 0.05 and 96.7 % at s = 0.50, while the speedup falls from
+1.370x to 1.058x): choose_budget picks, among budgets with measured round
+times, the one whose modelled speedup is largest, given an acceptance-
+versus-budget curve supplied by the caller (synthetic logits make acceptance
+independent of the budget, so the curve is an input, not a measurement).
+
 Host arithmetic on measured or printed times only; nothing here runs on the
 device.
 """
+
+import math
 
 
 def round_cost(k: int, t_draft_step: float, t_verify: float) -> float:
@@ -110,3 +137,53 @@ class AcceptanceTracker:
             self.alpha[m] = rate if not self.seen[m] else self.decay * self.alpha[m] + (1 - self.decay) * rate
             self.seen[m] = True
         return list(self.alpha)
+
+
+def calibrated_speedup(a: float, rho: float, k: int, c: float = 0.0) -> float:
+    """Speedup of a round over dense decoding from the accepted-prefix fraction a, the draft
+    KV-read fraction rho and the constant correction c (dense-step units)."""
+    return (1.0 + a * k) / (k * rho + 1.0 + c)
+
+
+def fit_constant_correction(points, k_of=None) -> float:
+    """Least-squares c over calibration points (a, rho, k, measured speedup): the mean of
+    (1 + a k) / speedup - (k rho + 1), which minimises the squared error of the modelled
+    round cost."""
+    res = [(1.0 + a * k) / sp - (k * rho + 1.0) for a, rho, k, sp in points]
+    return sum(res) / len(res)
+
+
+def mape(points, c: float) -> float:
+    """Mean absolute percentage error (%) of calibrated_speedup against measured speedups."""
+    errs = [abs(calibrated_speedup(a, rho, k, c) - sp) / sp for a, rho, k, sp in points]
+    return 100.0 * sum(errs) / len(errs)
+
+
+def acceptance_curve(points):
+    """Acceptance as a function of the budget s, through (s, alpha) points: linear in log s
+    between neighbouring points, the end segments extended, clamped to [0, 1]."""
+    pts = sorted((float(s_), float(a_)) for s_, a_ in points)
+    if len(pts) < 2:
+        raise ValueError("two points at least")
+
+    def alpha(s_: float) -> float:
+        x = math.log(float(s_))
+        i = 0
+        while i < len(pts) - 2 and x > math.log(pts[i + 1][0]):
+            i += 1
+        (s0, a0), (s1, a1) = pts[i], pts[i + 1]
+        t = (x - math.log(s0)) / (math.log(s1) - math.log(s0))
+        return min(1.0, max(0.0, a0 + t * (a1 - a0)))
+
+    return alpha
+
+
+def choose_budget(alpha_of_s, t_round_of_s, t_dense_step: float, k: int):
+    """The budget with the largest modelled speedup (ties to the smaller budget).
+
+    alpha_of_s: per-draft acceptance at budget s (callable); t_round_of_s: measured round time
+    at each candidate budget (mapping s -> time, same unit as t_dense_step). A round at budget s
+    outputs expected_tokens(alpha(s), k) tokens on average. Returns (s, {s: speedup})."""
+    gains = {s_: expected_tokens(alpha_of_s(s_), k) * t_dense_step / t for s_, t in t_round_of_s.items()}
+    best = max(gains, key=lambda s_: (gains[s_], -s_))
+    return best, gains

@@ -284,6 +284,34 @@ s3r_status s3r_spec_sample_noalloc(const float* target_logits, const float* draf
                                           temperature, tokens, n_out, accepted, ws, stream));
 }
 
+size_t s3r_read_pattern_sink_words(int32_t B, int32_t Hkv, int32_t max_len, int32_t draft) {
+  if (B < 1 || Hkv < 1 || max_len < 1) return 0;
+  return draft ? s3r::read_draft_pattern_words(B, Hkv, max_len) : s3r::read_verify_pattern_words(B, Hkv, max_len);
+}
+
+s3r_status s3r_read_verify_pattern(const s3r_paged_kv* kv, const int32_t* seq_len, int32_t B, int32_t max_seq_len,
+                                   uint32_t* sink, size_t sink_words, hipStream_t stream) {
+  if (!kv_ok(kv) || !seq_len || !sink) return S3R_ERR_INVALID_ARG;
+  if (B < 1 || B > 65535 || max_seq_len < 1 || kv->num_kv_heads > 65535) return S3R_ERR_INVALID_ARG;
+  if ((long long)kv->max_pages_per_seq * kv->page_size < max_seq_len) return S3R_ERR_INVALID_ARG;
+  if (kv->page_size != 16 || kv->head_dim != 128 || kv->dtype != S3R_BF16) return S3R_ERR_UNSUPPORTED;
+  if (sink_words < s3r::read_verify_pattern_words(B, kv->num_kv_heads, max_seq_len)) return S3R_ERR_WORKSPACE;
+  return from_hip(s3r::launch_read_verify_pattern(kv->k_pages, kv->v_pages, kv->block_table, kv->max_pages_per_seq,
+                                                  kv->num_kv_heads, seq_len, B, max_seq_len, sink, stream));
+}
+
+s3r_status s3r_read_draft_pattern(const s3r_paged_kv* kv, const int32_t* idx, int32_t nsel_cap,
+                                  const int32_t* n_sel, const int32_t* sel_len, const int32_t* cur_len, int32_t B,
+                                  int32_t max_attend, uint32_t* sink, size_t sink_words, hipStream_t stream) {
+  if (!kv_ok(kv) || !idx || !n_sel || !sel_len || !cur_len || !sink) return S3R_ERR_INVALID_ARG;
+  if (B < 1 || B > 65535 || nsel_cap < 1 || max_attend < 1 || kv->num_kv_heads > 65535) return S3R_ERR_INVALID_ARG;
+  if (kv->page_size != 16 || kv->head_dim != 128 || kv->dtype != S3R_BF16) return S3R_ERR_UNSUPPORTED;
+  if (sink_words < s3r::read_draft_pattern_words(B, kv->num_kv_heads, max_attend)) return S3R_ERR_WORKSPACE;
+  return from_hip(s3r::launch_read_draft_pattern(kv->k_pages, kv->v_pages, kv->block_table, kv->max_pages_per_seq,
+                                                 kv->num_kv_heads, idx, nsel_cap, n_sel, sel_len, cur_len, B,
+                                                 max_attend, sink, stream));
+}
+
 s3r_status s3r_kv_append(const void* k_rows, const void* v_rows, const s3r_paged_kv* kv,
                          const int32_t* pos, int32_t B, int32_t n, int32_t max_pos, hipStream_t stream) {
   if (!k_rows || !v_rows || !pos || !kv_ok(kv)) return S3R_ERR_INVALID_ARG;

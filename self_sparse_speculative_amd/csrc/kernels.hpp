@@ -47,6 +47,25 @@ constexpr bool kVerBalance = S3R_VERIFY_BALANCE != 0;  // equal-size verify spli
 // workgroups share a CU instead of one (36 rows at 24K: 3.90 -> 3.64 ms).
 // At two row tiles the same change spills and is slower (3.39 -> 3.48 ms).
 constexpr bool kVerQLds = S3R_VERIFY_Q_LDS != 0;
+#ifndef S3R_VERIFY_EARLY_LOADS
+#define S3R_VERIFY_EARLY_LOADS 1
+#endif
+// Verify: a wave issues its next subtile's K loads right after its S MFMAs and
+// its V loads right after the V transpose, instead of both at the end.
+constexpr bool kVerEarlyLoads = S3R_VERIFY_EARLY_LOADS != 0;
+#ifndef S3R_VERIFY_SPLIT_EDGE
+#define S3R_VERIFY_SPLIT_EDGE 1
+#endif
+// Verify: separate code for the subtiles that need the causal mask and those
+// that do not (0: one masked form for all).
+constexpr bool kVerSplitEdge = S3R_VERIFY_SPLIT_EDGE != 0;
+#ifndef S3R_VERIFY_PAGE_BURST
+#define S3R_VERIFY_PAGE_BURST 1
+#endif
+// Verify, page scores, up to two row tiles: a split's page records gathered in
+// LDS and written in one burst at its end.
+constexpr bool kVerPageBurst = S3R_VERIFY_PAGE_BURST != 0;
+
 #ifndef S3R_SELECT_SAMPLED
 #define S3R_SELECT_SAMPLED 1
 #endif
@@ -110,6 +129,17 @@ hipError_t launch_select_pages(const float* page_scores, int stride, const int* 
 hipError_t launch_select_grouped(const float* scores, int stride, const int* ctx_len, int B, int Hkv,
                                  int max_ctx_len, int s_num, int s_den, int window, int unit, int all_heads,
                                  int* idx, int nsel_cap, int* n_sel, void* ws, hipStream_t stream);
+
+// Measurement: the read patterns of the verification and of a draft step.
+size_t read_verify_pattern_words(int B, int Hkv, int max_seq_len);
+size_t read_draft_pattern_words(int B, int Hkv, int max_attend);
+hipError_t launch_read_verify_pattern(const void* kp, const void* vp, const int* bt, int max_pages, int Hkv,
+                                      const int* seq_len, int B, int max_seq_len, uint32_t* sink,
+                                      hipStream_t stream);
+hipError_t launch_read_draft_pattern(const void* kp, const void* vp, const int* bt, int max_pages, int Hkv,
+                                     const int* idx, int nsel_cap, const int* n_sel, const int* sel_len,
+                                     const int* cur_len, int B, int max_attend, uint32_t* sink,
+                                     hipStream_t stream);
 
 hipError_t launch_kv_append(const void* k_rows, const void* v_rows, void* k_pages, void* v_pages,
                             const int* bt, int max_pages, const int* pos, int B, int n, int Hkv,

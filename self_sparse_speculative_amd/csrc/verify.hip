@@ -97,6 +97,11 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
   // QL: Q rows as B fragments, slot (nt, kk, lane) = row nt*16 + lane%16,
   // elements kk*32 + 8*(lane/16) .. +8 (zero rows past R)
   __shared__ uint4 q_sh[QL ? NT * 4 * 64 : 1];
+  // Page scores with at most two row tiles: the split's page records are
+  // gathered here and written out in one contiguous burst at the end of the
+  // split (scattered 256 B writes during the stream cost far more).
+  constexpr bool PB = SM == kScoresPages && NT <= 2 && kVerPageBurst;
+  __shared__ __attribute__((aligned(16))) float pbuf[PB ? (kVerChunkMfma / kPage) * RP : 1];
 
   // Workgroups are dispatched round-robin over the XCDs; consecutive splits of
   // one (sequence, KV head) pair go to the same XCD. Draft step j of a round
@@ -176,16 +181,23 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
     bf16x8_t kf[2][4];  // K rows as A fragments: lane (n16 = position in the 16-row tile, g4 = k group)
     uint4 vraw[2][4];   // V rows for the LDS transpose: task = (4 positions a, 8-wide d chunk c)
   };
-  auto load_sub = [&](int st, Sub& d) {
-    const int pos0 = c0 + st * kSub;
-    const int page_a = pages_sh[2 * st];
-    const int page_b = (pos0 + 16 < S) ? pages_sh[2 * st + 1] : page_a;
+  auto sub_pages = [&](int st, int& page_a, int& page_b) {
+    page_a = pages_sh[2 * st];
+    page_b = (c0 + st * kSub + 16 < S) ? pages_sh[2 * st + 1] : page_a;
+  };
+  auto load_k = [&](int st, Sub& d) {
+    int page_a, page_b;
+    sub_pages(st, page_a, page_b);
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
       const bf16_t* kb = kp + (((size_t)(pt ? page_b : page_a) * Hkv + kv) * kPage + n16) * D + g4 * 8;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) d.kf[pt][kk] = *reinterpret_cast<const bf16x8_t*>(kb + kk * 32);
     }
+  };
+  auto load_v = [&](int st, Sub& d) {
+    int page_a, page_b;
+    sub_pages(st, page_a, page_b);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int task = lane + 64 * tt;
@@ -198,7 +210,10 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
   };
 
   Sub cur;
-  if (wave < nsub) load_sub(wave, cur);
+  if (wave < nsub) {
+    load_k(wave, cur);
+    load_v(wave, cur);
+  }
   // One subtile. EDGE: some position of it lies past some row's last one (the
   // block's causal triangle, the end of the sequence), so the logits are
   // masked; every row sees all positions of the earlier subtiles. (Rows past R
@@ -225,9 +240,20 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
         s[pt][nt] = acc;
       }
     }
+    // The K fragments are consumed: the wave's next subtile's K loads go out
+    // now, so they are in flight during the rest of this subtile. (The last
+    // subtile of a wave reloads itself from the cache instead, so every path
+    // through the loop issues the same loads and the wait at the top of the
+    // next subtile covers only its K loads.)
+    const int st_next = st + kVerWaves < nsub ? st + kVerWaves : st;
+    if (kVerEarlyLoads) {
+      load_k(st_next, cur);
+      pin_issued_loads();
+    }
 
     const int tile = pos0 / kSub;
     bf16x8_t pf[NT];
+    float pmass[NT];  // page masses of this lane's rows (page scores)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float mx = kNegInf;
@@ -287,17 +313,38 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
       } else if constexpr (SM == kScoresPages) {
         // Each of the subtile's two pages: the row's probability mass on it (the
         // four lane groups' sums in a fixed order), kept as base + log2(mass)
-        // (-inf for none). Lanes of groups 0 and 1 write pages 2 tile and
-        // 2 tile + 1: one float per (page, row), every row of the tile.
+        // (-inf for none); lanes of group 0 keep page 2 tile, group 1 page
+        // 2 tile + 1.
         float pa = (pv[0][0] + pv[0][1]) + (pv[0][2] + pv[0][3]);
         float pb = (pv[1][0] + pv[1][1]) + (pv[1][2] + pv[1][3]);
         pa += __shfl_xor(pa, 16, kWave);
         pb += __shfl_xor(pb, 16, kWave);
         pa += __shfl_xor(pa, 32, kWave);
         pb += __shfl_xor(pb, 32, kWave);
-        const int page = 2 * tile + g4;
-        if (g4 < 2 && page * kPage < S)
-          static_cast<float*>(sc_val)[(bkv * 2 * ntile_cap + page) * RP + r] = base + __log2f(g4 == 0 ? pa : pb);
+        pmass[nt] = base + __log2f(g4 == 0 ? pa : pb);
+      }
+    }
+    if constexpr (SM == kScoresPages) {
+      // One store per subtile: a page's record holds row nt * 16 + n at float
+      // n * NT + nt, so each lane writes its NT rows as one vector and the two
+      // pages' records (RP floats each, adjacent) are written as whole lines.
+      const int page = 2 * tile + g4;
+      if (PB && g4 < 2) {
+        float* dst = pbuf + (2 * st + g4) * RP + n16 * NT;
+        if constexpr (NT == 1) dst[0] = pmass[0];
+        else *reinterpret_cast<float2*>(dst) = make_float2(pmass[0], pmass[NT - 1]);
+      } else if (!PB && g4 < 2 && page * kPage < S) {
+        float* dst = static_cast<float*>(sc_val) + (bkv * 2 * ntile_cap + page) * RP + n16 * NT;
+        if constexpr (NT == 1) {
+          dst[0] = pmass[0];
+        } else if constexpr (NT == 2) {
+          *reinterpret_cast<float2*>(dst) = make_float2(pmass[0], pmass[1]);
+        } else if constexpr (NT == 3) {
+          typedef float f32x3_t __attribute__((ext_vector_type(3)));
+          *reinterpret_cast<f32x3_t*>(dst) = f32x3_t{pmass[0], pmass[1], pmass[2]};
+        } else {
+          *reinterpret_cast<float4*>(dst) = make_float4(pmass[0], pmass[1], pmass[2], pmass[3]);
+        }
       }
     }
 
@@ -332,6 +379,11 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
         *reinterpret_cast<uint2*>(my_vt + (c * 8 + e) * kVtStride + slot) = make_uint2(lo, hi);
       }
     }
+    // The V words are in LDS: the next subtile's V loads go out now.
+    if (kVerEarlyLoads) {
+      load_v(st_next, cur);
+      pin_issued_loads();
+    }
     wave_lds_sync();  // each lane reads rows written by other lanes
     // O^T += V^T P^T
 #pragma unroll
@@ -341,13 +393,25 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
       for (int nt = 0; nt < NT; ++nt)
         oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfrag, pf[nt], oacc[nt][dt], 0, 0, 0);
     }
-    if (st + kVerWaves < nsub) load_sub(st + kVerWaves, cur);
+    if (!kVerEarlyLoads && st + kVerWaves < nsub) {
+      load_k(st + kVerWaves, cur);
+      load_v(st + kVerWaves, cur);
+    }
   };
   for (int st = wave; st < nsub; st += kVerWaves) {
-    if (c0 + st * kSub + kSub - 1 > P0)
+    if (!kVerSplitEdge || c0 + st * kSub + kSub - 1 > P0)
       subtile(st, std::true_type{});
     else
       subtile(st, std::false_type{});
+  }
+
+  if constexpr (PB) {
+    // the split's page records, [c0 / 16, ceil(c1 / 16)), as one run of float4
+    __syncthreads();
+    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(sc_val) + (bkv * 2 * ntile_cap + c0 / kPage) * RP);
+    const float4* src = reinterpret_cast<const float4*>(pbuf);
+    const int n4 = ceil_div(c1 - c0, kPage) * RP / 4;
+    for (int t = tid; t < n4; t += kVerThreads) dst[t] = src[t];
   }
 
   // Merge the waves: rows are lane % 16 (+16 nt); l is a per-lane partial.
@@ -405,7 +469,6 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
     part_ml[(rec + tid) * 2] = base;
     part_ml[(rec + tid) * 2 + 1] = Ls;
   }
-
 }
 
 // Generic path: one row at a time, two passes over the chunk (max, then
@@ -526,7 +589,7 @@ template <typename VT, int D, bool PAGES>
 __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, const VT* __restrict__ sc_val,
     const float* __restrict__ sc_max, const int* __restrict__ seq_len, int k, int Hkv, int G, int chunk,
-    int nsplit, int ntile_cap, int RP, int nblk_o, int x0, float* __restrict__ out,
+    int nsplit, int ntile_cap, int RP, int nblk_o, int x0, int balanced, float* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ scores, int score_stride) {
   __shared__ float mrow[64], lrow[64], l2row[64];
   __shared__ float wt[PAGES ? 1 : kFinTiles][64];
@@ -537,7 +600,10 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
   const int tile_beg = (x - nblk_o) * kFinTiles;
   const int page_beg = (x - nblk_o) * kVerThreads;
   if (x >= nblk_o && (PAGES ? page_beg * kPage : tile_beg * kSub) >= S) return;
-  const int used = min(nsplit, ceil_div(S, chunk));
+  // the splits the split pass wrote: balanced splits (MFMA path) may leave the
+  // last of ceil(S / chunk) empty once a sequence has hundreds of them
+  const int used = balanced ? ceil_div(S, ceil_div(ceil_div(S, ceil_div(S, chunk)), kSub) * kSub)
+                            : min(nsplit, ceil_div(S, chunk));
   const int R = (k + 1) * G, Hq = Hkv * G;
   const size_t bkv = (size_t)pair;
   // Row statistics: 4 lanes per row, each over every 4th split, then a fixed
@@ -567,8 +633,9 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
   }
   __syncthreads();
   if (x < nblk_o) {
-    const int t = x * kVerThreads + tid;
-    if (t < R * D) {
+    const int t0 = x * kVerThreads + tid;
+    const int t1 = min(R * D, (x + 1) * kVerThreads);
+    for (int t = t0; t < t1; t += kVerThreads) {
       const int r = t / D, d = t % D;
       float A = 0.f;
       for (int c = 0; c < used; ++c) {
@@ -583,18 +650,14 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
   }
   if constexpr (PAGES) {
     // page score = sum over the rows of exp2(mass - log2 of the row's normaliser)
+    // record slot i holds row (i % NT) * 16 + i / NT (NT = RP / 16 row tiles);
+    // the rows are summed in ascending order
+    const int NT = RP / 16;
     const int page = page_beg + tid;
     if (page * kPage < S) {
-      const float4* m4 = reinterpret_cast<const float4*>(sc_val + (bkv * 2 * ntile_cap + page) * RP);
+      const float* m = sc_val + (bkv * 2 * ntile_cap + page) * RP;
       float acc = 0.f;
-      for (int r4 = 0; r4 < RP / 4; ++r4) {
-        const float4 m = m4[r4];
-        const int r = 4 * r4;
-        if (r < R) acc += exp2f_fast(m.x - l2row[r]);
-        if (r + 1 < R) acc += exp2f_fast(m.y - l2row[r + 1]);
-        if (r + 2 < R) acc += exp2f_fast(m.z - l2row[r + 2]);
-        if (r + 3 < R) acc += exp2f_fast(m.w - l2row[r + 3]);
-      }
+      for (int r = 0; r < R; ++r) acc += exp2f_fast(m[(r & 15) * NT + (r >> 4)] - l2row[r]);
       scores[bkv * score_stride + page] = acc;
     }
     return;
@@ -723,8 +786,8 @@ static hipError_t launch_finalize(const VerifyPlan& p, int D, const int* seq_len
   hipLaunchKernelGGL((verify_finalize_kernel<VT, DD, PG>), grid, dim3(kVerThreads), 0, stream,      \
                      (const float*)(ws + p.off_part_o), (const float*)(ws + p.off_part_ml),          \
                      (const VT*)(ws + p.off_sc_val), (const float*)(ws + p.off_sc_max), seq_len, k,  \
-                     Hkv, p.G, p.chunk, p.nsplit, p.ntile_cap, p.RP, nblk_o, x0, out, lse, scores,   \
-                     score_stride)
+                     Hkv, p.G, p.chunk, p.nsplit, p.ntile_cap, p.RP, nblk_o, x0,                     \
+                     (p.mfma && kVerBalance) ? 1 : 0, out, lse, scores, score_stride)
   if (p.mfma && p.pages) {
     S3R_FIN(float, 128, true);
   } else if (p.mfma) {

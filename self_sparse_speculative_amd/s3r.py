@@ -32,7 +32,7 @@ EXPORTED = (
     "s3r_verify_workspace_bytes", "s3r_verify_attn", "s3r_verify_attn_deferred", "s3r_verify_scores",
     "s3r_spec_sample_workspace_bytes", "s3r_spec_sample", "s3r_kv_append", "s3r_commit",
     "s3r_length_order", "s3r_spec_sample_noalloc", "s3r_verify_pages_workspace_bytes", "s3r_verify_attn_pages",
-    "s3r_select_pages",
+    "s3r_select_pages", "s3r_read_pattern_sink_words", "s3r_read_verify_pattern", "s3r_read_draft_pattern",
 )
 SAMPLE_SCRATCH_BYTES = 8 << 20  # S3R_SAMPLE_SCRATCH_BYTES
 
@@ -119,6 +119,13 @@ def load():
         L.s3r_spec_sample.argtypes = [vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
         L.s3r_spec_sample_noalloc.restype = ctypes.c_int
         L.s3r_spec_sample_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp]
+        L.s3r_read_pattern_sink_words.restype = sz
+        L.s3r_read_pattern_sink_words.argtypes = [i32, i32, i32, i32]
+        L.s3r_read_verify_pattern.restype = ctypes.c_int
+        L.s3r_read_verify_pattern.argtypes = [ctypes.POINTER(PagedKVStruct), vp, i32, i32, vp, sz, vp]
+        L.s3r_read_draft_pattern.restype = ctypes.c_int
+        L.s3r_read_draft_pattern.argtypes = [ctypes.POINTER(PagedKVStruct), vp, i32, vp, vp, vp, i32, i32, vp, sz,
+                                             vp]
         L.s3r_kv_append.restype = ctypes.c_int
         L.s3r_kv_append.argtypes = [vp, vp, ctypes.POINTER(PagedKVStruct), vp, i32, i32, i32, vp]
         L.s3r_commit.restype = ctypes.c_int
@@ -437,6 +444,31 @@ def spec_sample_noalloc(target_logits, draft_logits, draft_tokens, uniforms, tem
                                      float(temperature), _ptr(tokens), _ptr(n_out), _ptr(accepted),
                                      _stream(stream)), "s3r_spec_sample_noalloc")
     return tokens, n_out, accepted
+
+
+def read_verify_pattern(kv: PagedKV, seq_len, max_seq_len, sink=None, stream=None):
+    """s3r_read_verify_pattern (measurement): returns the checksum words."""
+    L = load()
+    B = seq_len.shape[0]
+    n = int(L.s3r_read_pattern_sink_words(B, kv.num_kv_heads, int(max_seq_len), 0))
+    if sink is None:
+        sink = torch.empty((n,), dtype=torch.int32, device=seq_len.device)
+    _check(L.s3r_read_verify_pattern(ctypes.byref(kv.struct), _ptr(seq_len), B, int(max_seq_len), _ptr(sink),
+                                     sink.numel(), _stream(stream)), "s3r_read_verify_pattern")
+    return sink
+
+
+def read_draft_pattern(kv: PagedKV, idx, n_sel, sel_len, cur_len, max_attend, sink=None, stream=None):
+    """s3r_read_draft_pattern (measurement): returns the checksum words."""
+    L = load()
+    B, _, cap = idx.shape
+    n = int(L.s3r_read_pattern_sink_words(B, kv.num_kv_heads, int(max_attend), 1))
+    if sink is None:
+        sink = torch.empty((n,), dtype=torch.int32, device=idx.device)
+    _check(L.s3r_read_draft_pattern(ctypes.byref(kv.struct), _ptr(idx), cap, _ptr(n_sel), _ptr(sel_len),
+                                    _ptr(cur_len), B, int(max_attend), _ptr(sink), sink.numel(), _stream(stream)),
+           "s3r_read_draft_pattern")
+    return sink
 
 
 def kv_append(k_rows, v_rows, kv: PagedKV, pos, max_pos, stream=None):

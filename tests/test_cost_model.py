@@ -101,3 +101,61 @@ def test_acceptance_tracker_counts():
     assert est[:4] == [3 / 4, 2 / 3, 1 / 2, 1 / 1]
     est = tr.update(np.array([[0, -1, -1, -1]], dtype=np.int8))
     assert est[0] == 0.5 * 0.75 and est[1:] == [2 / 3, 1 / 2, 1.0]  # unreached positions keep their estimate
+
+
+def test_calibrated_speedup_limits():
+    k = 6
+    # a draft that reads the whole cache (rho = 1) and keeps every draft costs exactly the k + 1
+    # dense steps it replaces
+    assert abs(cm.calibrated_speedup(1.0, 1.0, k) - 1.0) < 1e-15
+    # full acceptance outputs k + 1 tokens: the numerator
+    assert abs(cm.calibrated_speedup(1.0, 0.05, k) * (k * 0.05 + 1.0) - (k + 1)) < 1e-12
+    # nothing accepted: one token for the round's cost
+    assert abs(cm.calibrated_speedup(0.0, 0.05, k, 0.2) - 1.0 / (k * 0.05 + 1.2)) < 1e-15
+    # the correction only lengthens (c > 0) or shortens the round
+    assert cm.calibrated_speedup(0.8, 0.05, k, 0.3) < cm.calibrated_speedup(0.8, 0.05, k, 0.0)
+    # the explainer's round in the same terms: 6 steps at 0.35 of a dense step and a verification
+    # of 1.4 dense steps are rho = 0.35 and c = 0.4; 5.5 tokens per round give 1.57x
+    assert round(cm.calibrated_speedup(4.5 / 6, 0.35, 6, 0.4), 2) == 1.57
+
+
+def test_constant_correction_fit_recovers_a_planted_constant():
+    rng = np.random.default_rng(0)
+    pts = []
+    for _ in range(24):
+        a, rho, k = rng.uniform(0.3, 0.95), rng.uniform(0.01, 0.3), int(rng.integers(2, 9))
+        pts.append((a, rho, k, cm.calibrated_speedup(a, rho, k, 0.37)))
+    c = cm.fit_constant_correction(pts[:12])
+    assert abs(c - 0.37) < 1e-12
+    assert cm.mape(pts[12:], c) < 1e-10
+    assert cm.mape(pts[12:], 0.0) > 5.0  # the uncorrected model is off
+    # the fit minimises the squared error of the modelled round cost: a brute-force scan agrees
+    noisy = [(a, rho, k, sp * (1 + 0.02 * rng.standard_normal())) for a, rho, k, sp in pts]
+    c_fit = cm.fit_constant_correction(noisy)
+    cost = lambda c: sum(((1 + a * k) / sp - (k * rho + 1 + c)) ** 2 for a, rho, k, sp in noisy)
+    grid = np.linspace(c_fit - 0.05, c_fit + 0.05, 2001)
+    assert abs(grid[int(np.argmin([cost(g) for g in grid]))] - c_fit) <= 0.05 / 1000
+
+
+def test_acceptance_curve_through_the_pages_points():
+    # the listing's abstract: 80.4 % acceptance at s = 0.05, 96.7 % at s = 0.50
+    f = cm.acceptance_curve([(0.05, 0.804), (0.50, 0.967)])
+    assert abs(f(0.05) - 0.804) < 1e-12 and abs(f(0.50) - 0.967) < 1e-12
+    assert abs(f(np.sqrt(0.05 * 0.5)) - (0.804 + 0.967) / 2) < 1e-12  # linear in log s
+    assert f(0.02) < f(0.05) < f(0.1) < f(0.2) < f(0.5) and f(10.0) == 1.0
+
+
+def test_budget_choice_is_the_brute_force_argmax():
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        k = int(rng.integers(2, 9))
+        budgets = sorted(rng.uniform(0.01, 0.5, size=5))
+        t_dense = 2.0
+        t_round = {s: t_dense * (1.2 + k * s * rng.uniform(0.8, 1.2)) for s in budgets}
+        a0, a1 = rng.uniform(0.5, 0.85), rng.uniform(0.86, 0.99)
+        f = cm.acceptance_curve([(0.05, a0), (0.5, a1)])
+        best, gains = cm.choose_budget(f, t_round, t_dense, k)
+        brute = max(budgets, key=lambda s: (sum(f(s) ** i for i in range(k + 1)) * t_dense / t_round[s], -s))
+        assert best == brute
+        assert all(abs(gains[s] - cm.speedup(cm.expected_tokens(f(s), k), t_dense, k, 0.0, t_round[s])) < 1e-12
+                   for s in budgets)

@@ -160,3 +160,24 @@ def test_rollout_benchmark_inputs_middle_layer():
         assert eo <= TOL_BF16 and es <= TOL_BF16, (b, eo, es)
         assert np.abs(vlse[b] - rl).max() <= 2e-3
     print(f"[rollout] {len(seqs)} sequences checked (groups 0, 16, 31)", flush=True)
+
+
+def test_read_pattern_kernels_run_in_bounds_and_deterministically():
+    # measurement kernels: the verification's and a draft step's reads, checksummed per workgroup
+    cfg = get_config(3, B=5, lengths=("uniform", 1, 9000))
+    batch = make_batch(cfg, lengths=np.array([1, 17, 4095, 4097, 9000], np.int32), parts=("kv", "scores"))
+    t = to_dev(batch)
+    ms = int(batch.seq_len.max())
+    # workgroups past a sequence's end write nothing: the sinks start at zero
+    nv = s3r.load().s3r_read_pattern_sink_words(cfg.B, cfg.Hkv, ms, 0)
+    a = s3r.read_verify_pattern(t["kv"], t["seq_len"], ms, sink=torch.zeros(nv, dtype=torch.int32, device="cuda"))
+    b = s3r.read_verify_pattern(t["kv"], t["seq_len"], ms, sink=torch.zeros(nv, dtype=torch.int32, device="cuda"))
+    idx, n_sel = run_select(cfg, batch, t)
+    cap = idx.shape[2]
+    nd = s3r.load().s3r_read_pattern_sink_words(cfg.B, cfg.Hkv, cap + 1, 1)
+    c = s3r.read_draft_pattern(t["kv"], idx, n_sel, t["ctx_len"], t["ctx_len"] + 1, cap + 1,
+                               sink=torch.zeros(nd, dtype=torch.int32, device="cuda"))
+    d = s3r.read_draft_pattern(t["kv"], idx, n_sel, t["ctx_len"], t["ctx_len"] + 1, cap + 1,
+                               sink=torch.zeros(nd, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(c, d)
