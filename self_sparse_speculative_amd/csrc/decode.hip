@@ -281,12 +281,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
   __shared__ int rows[kDecChunkMfma];
 
   // Workgroups take the sequences in `order` (when given: longest first keeps
-  // workgroups of similar length together). Draft steps alternate the
-  // direction (odd steps from the last), so a step starts on the rows the
-  // previous step read last, which the Infinity Cache may still hold.
+  // workgroups of similar length together).
   const int split = blockIdx.x, kv = blockIdx.y;
-  const int z = (kDecAlternate && ((cur_len[0] - sel_len[0]) & 1)) ? (int)gridDim.z - 1 - (int)blockIdx.z
-                                                                     : (int)blockIdx.z;
+  const int z = (int)blockIdx.z;
   const int b = order != nullptr ? order[z] : z;
   if ((unsigned)b >= gridDim.z) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

@@ -22,15 +22,6 @@ constexpr int kDecChunkMfma = S3R_DRAFT_CHUNK;  // most attended positions per d
 #define S3R_DRAFT_BALANCE 1
 #endif
 constexpr bool kDecBalance = S3R_DRAFT_BALANCE != 0;  // equal-size draft splits
-#ifndef S3R_DRAFT_ALTERNATE
-#define S3R_DRAFT_ALTERNATE 1
-#endif
-constexpr bool kDecAlternate = S3R_DRAFT_ALTERNATE != 0;  // odd draft steps visit the sequences backwards
-#ifndef S3R_VERIFY_FOLLOW_DRAFT
-#define S3R_VERIFY_FOLLOW_DRAFT 1
-#endif
-// the verification starts on the sequences the last draft step read last
-constexpr bool kVerFollowDraft = S3R_VERIFY_FOLLOW_DRAFT != 0;
 #ifndef S3R_VERIFY_CHUNK
 #define S3R_VERIFY_CHUNK 4096
 #endif
@@ -65,6 +56,12 @@ constexpr bool kVerSplitEdge = S3R_VERIFY_SPLIT_EDGE != 0;
 // Verify, page scores, up to two row tiles: a split's page records gathered in
 // LDS and written in one burst at its end.
 constexpr bool kVerPageBurst = S3R_VERIFY_PAGE_BURST != 0;
+#ifndef S3R_VERIFY_POS_BURST
+#define S3R_VERIFY_POS_BURST 1
+#endif
+// Verify, position scores, up to two row tiles: the partials of each group of
+// 16 subtiles gathered in LDS and written as one run.
+constexpr bool kVerPosBurst = S3R_VERIFY_POS_BURST != 0;
 
 #ifndef S3R_SELECT_SAMPLED
 #define S3R_SELECT_SAMPLED 1

@@ -102,17 +102,20 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
   // split (scattered 256 B writes during the stream cost far more).
   constexpr bool PB = SM == kScoresPages && NT <= 2 && kVerPageBurst;
   __shared__ __attribute__((aligned(16))) float pbuf[PB ? (kVerChunkMfma / kPage) * RP : 1];
+  // Position scores with at most two row tiles: the partials of a group of
+  // kPosGroup consecutive subtiles (fp16 probabilities and row maxima) are
+  // gathered here and written as one contiguous run once the group is done.
+  constexpr bool QB = SM == kScoresPositions && NT <= 2 && kVerPosBurst;
+  constexpr int kPosGroup = 16;
+  __shared__ __attribute__((aligned(16))) _Float16 qbuf[QB ? kPosGroup * RP * kSub : 1];
+  __shared__ __attribute__((aligned(16))) float qmax[QB ? kPosGroup * 32 : 1];
 
   // Workgroups are dispatched round-robin over the XCDs; consecutive splits of
-  // one (sequence, KV head) pair go to the same XCD. Draft step j of a round
-  // visits the sequences backwards when j is odd, so after k draft steps the
-  // last sequence was read last when k is even: the pairs are then taken from
-  // the last, and the first workgroups may find their pages in the Infinity
-  // Cache.
+  // one (sequence, KV head) pair go to the same XCD.
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
   const int pair0 = (local / nsplit) * 8 + xcd, split = local % nsplit;
   if (pair0 >= npairs) return;
-  const int pair = (kVerFollowDraft && !(k & 1)) ? npairs - 1 - pair0 : pair0;
+  const int pair = pair0;
   const int b = pair / Hkv, kv = pair % Hkv;
   const int S = seq_len[b];
   // `chunk` is the most positions a split holds; each sequence spreads its
@@ -300,7 +303,18 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
                         (__bf16)pv[1][0], (__bf16)pv[1][1], (__bf16)pv[1][2], (__bf16)pv[1][3]};
 
       const int r = nt * 16 + n16;
-      if constexpr (SM == kScoresPositions) {
+      if constexpr (SM == kScoresPositions && QB) {
+        // group slot st % kPosGroup: R rows of 32 fp16 probabilities, then the maxima
+        if (r < R) {
+          _Float16* dst = qbuf + ((st % kPosGroup) * R + r) * kSub;
+          typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+          f16x4_t h0 = {(_Float16)pv[0][0], (_Float16)pv[0][1], (_Float16)pv[0][2], (_Float16)pv[0][3]};
+          f16x4_t h1 = {(_Float16)pv[1][0], (_Float16)pv[1][1], (_Float16)pv[1][2], (_Float16)pv[1][3]};
+          *reinterpret_cast<f16x4_t*>(dst + 4 * g4) = h0;
+          *reinterpret_cast<f16x4_t*>(dst + 16 + 4 * g4) = h1;
+          if (g4 == 0) qmax[(st % kPosGroup) * 32 + r] = base;
+        }
+      } else if constexpr (SM == kScoresPositions) {
         if (r < R) {
           _Float16* dst = static_cast<_Float16*>(sc_val) + ((bkv * ntile_cap + tile) * R + r) * kSub;
           typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
@@ -398,11 +412,34 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
       load_v(st + kVerWaves, cur);
     }
   };
-  for (int st = wave; st < nsub; st += kVerWaves) {
+  auto run_subtile = [&](int st) {
     if (!kVerSplitEdge || c0 + st * kSub + kSub - 1 > P0)
       subtile(st, std::true_type{});
     else
       subtile(st, std::false_type{});
+  };
+  if constexpr (QB) {
+    // groups of kPosGroup subtiles; after each, the group's partials go out in
+    // one run (tiles are contiguous in the record array, R x 32 fp16 each, and
+    // their maxima records max_stride(R) floats each)
+    const int tile0 = c0 / kSub;
+    const int ms = max_stride(R);
+    for (int g0 = 0; g0 < nsub; g0 += kPosGroup) {
+      const int gn = min(kPosGroup, nsub - g0);
+      for (int st = g0 + wave; st < g0 + gn; st += kVerWaves) run_subtile(st);
+      __syncthreads();
+      const int n8 = gn * R * kSub / 8;  // 16 B chunks of probabilities
+      uint4* pd = reinterpret_cast<uint4*>(static_cast<_Float16*>(sc_val) + (bkv * ntile_cap + tile0 + g0) * R * kSub);
+      const uint4* ps = reinterpret_cast<const uint4*>(qbuf);
+      for (int t = tid; t < n8; t += kVerThreads) pd[t] = ps[t];
+      for (int t = tid; t < gn * R; t += kVerThreads) {
+        const int tl = t / R, r = t % R;
+        sc_max[(bkv * ntile_cap + tile0 + g0 + tl) * ms + r] = qmax[tl * 32 + r];
+      }
+      __syncthreads();
+    }
+  } else {
+    for (int st = wave; st < nsub; st += kVerWaves) run_subtile(st);
   }
 
   if constexpr (PB) {
