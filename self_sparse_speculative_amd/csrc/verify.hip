@@ -21,8 +21,9 @@
 //     (read from LDS for three row tiles, see kVerQLds);
 //   - keeps the online-softmax state per row in the lanes that hold that row
 //     (lane % 16), so row rescales are lane-local;
-//   - writes the probabilities (relative to the running row maximum, fp16)
-//     and that maximum as score partials;
+//   - writes the probabilities (relative to the running row maximum, as
+//     12-bit codes of the bf16 values that also weight V) and that maximum
+//     as score partials;
 //   - transposes its V subtile through LDS (ds_write_b64 of 4 positions,
 //     ds_read_b128 of 8 slots) and accumulates O^T += V^T P^T on MFMA, with P
 //     already in B-fragment layout (the position order inside the contraction
@@ -77,7 +78,49 @@ __device__ __forceinline__ uint32_t u4_word(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-// Score partials the split kernel writes (SM): none; per position (fp16
+// Position score partials are 12-bit codes of the bf16 probabilities that
+// weight V (so the scores carry the precision the output does): the bf16 bit
+// pattern less kCodeBias, i.e. a 5-bit exponent spanning 2^-23 .. 2^9 over
+// the 7 mantissa bits. The probabilities lie in [0, 2^kLazyRescale], so the
+// codes stay below 4096; anything at or below 2^-23 becomes code 0, which
+// stands for zero. A lane's eight probabilities of a subtile (four positions
+// on each of its pages) pack into three words, code i at bits 12 i.
+constexpr uint32_t kCodeBias = 0x3400u;  // bf16 pattern of 2^-23
+constexpr int kCodeWords = kSub * 12 / 32;  // words per (subtile, row) record
+// Records are grouped by 16 consecutive tiles: group, then row, then the 16
+// tiles' records side by side, so the finalize's wave (one group, lane =
+// (tile, lane group)) reads each row's 16 records as one contiguous run.
+constexpr int kCodeGroup = 16;
+__host__ __device__ __forceinline__ size_t code_record(size_t bkv, int ngrp, int R, int tile, int r) {
+  return ((bkv * ngrp + (tile >> 4)) * R + r) * (kCodeGroup * kCodeWords) + (tile & 15) * kCodeWords;
+}
+
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t codes_of_pair(uint32_t w) {
+  u16x2_t h = __builtin_bit_cast(u16x2_t, w);
+  h = __builtin_elementwise_sub_sat(h, u16x2_t{(unsigned short)kCodeBias, (unsigned short)kCodeBias});
+  h = __builtin_elementwise_min(h, u16x2_t{4095, 4095});
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ void pack_codes(const bf16x8_t& p, uint32_t& w0, uint32_t& w1, uint32_t& w2) {
+  const uint4 b = __builtin_bit_cast(uint4, p);
+  const uint32_t d0 = codes_of_pair(b.x), d1 = codes_of_pair(b.y);  // (c1, c0), (c3, c2)
+  const uint32_t d2 = codes_of_pair(b.z), d3 = codes_of_pair(b.w);  // (c5, c4), (c7, c6)
+  w0 = (d0 & 0xfffu) | ((d0 >> 4) & 0xfff000u) | (d1 << 24);
+  w1 = ((d1 >> 8) & 0xfu) | (d1 >> 12) | (d2 << 16 & 0xfff0000u) | (d2 >> 16 << 28);
+  w2 = (d2 >> 20) | ((d3 & 0xfffu) << 8) | ((d3 >> 16) << 20);
+}
+
+// Decoding: the code shifted to bits 16..27 is a float of the probability
+// times 2^-104 (exponent field 0x68 lower), so the finalize folds 2^104 into
+// its row weight and needs a mask per code. Codes below 128 (probabilities
+// under 2^-22 of the reference maximum) land in the denormal range and come
+// out within 2^-22 of their value; code 0 is 0.
+constexpr float kCodeScaleLog2 = 104.f;
+
+// Score partials the split kernel writes (SM): none; per position (coded
 // probabilities relative to the row's reference maximum, plus that maximum per
 // tile); or per page (the log2 of the page's probability mass in the row).
 constexpr int kScoresNone = 0, kScoresPositions = 1, kScoresPages = 2;
@@ -102,13 +145,15 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
   // split (scattered 256 B writes during the stream cost far more).
   constexpr bool PB = SM == kScoresPages && NT <= 2 && kVerPageBurst;
   __shared__ __attribute__((aligned(16))) float pbuf[PB ? (kVerChunkMfma / kPage) * RP : 1];
-  // Position scores with at most two row tiles: the partials of a group of
-  // kPosGroup consecutive subtiles (fp16 probabilities and row maxima) are
-  // gathered here and written as one contiguous run once the group is done.
-  constexpr bool QB = SM == kScoresPositions && NT <= 2 && kVerPosBurst;
-  constexpr int kPosGroup = 16;
-  __shared__ __attribute__((aligned(16))) _Float16 qbuf[QB ? kPosGroup * RP * kSub : 1];
-  __shared__ __attribute__((aligned(16))) float qmax[QB ? kPosGroup * 32 : 1];
+  // Position scores: the partials of a group of kPosGroup consecutive
+  // subtiles (probability codes and row maxima) are gathered here and written
+  // out once the group is done, each row's records as one run. (Eight
+  // subtiles with three row tiles, whose Q fragments also sit in LDS, so two
+  // workgroups still fit a CU.)
+  constexpr bool QB = SM == kScoresPositions && kVerPosBurst;
+  constexpr int kPosGroup = NT <= 2 ? 16 : 8;
+  __shared__ __attribute__((aligned(16))) uint32_t qbuf[QB ? RP * kPosGroup * kCodeWords : 1];  // [row][slot]
+  __shared__ __attribute__((aligned(16))) float qmax[QB ? kPosGroup * RP : 1];
 
   // Workgroups are dispatched round-robin over the XCDs; consecutive splits of
   // one (sequence, KV head) pair go to the same XCD.
@@ -130,6 +175,7 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
   const int R = (k + 1) * G;
   const int P0 = S - (k + 1);
   const size_t bkv = (size_t)pair;
+  const int ngrp = ceil_div(ntile_cap, kCodeGroup);
 
   bf16x8_t qf[QL ? 1 : NT][4];
   int row_last[NT];
@@ -303,26 +349,20 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
                         (__bf16)pv[1][0], (__bf16)pv[1][1], (__bf16)pv[1][2], (__bf16)pv[1][3]};
 
       const int r = nt * 16 + n16;
-      if constexpr (SM == kScoresPositions && QB) {
-        // group slot st % kPosGroup: R rows of 32 fp16 probabilities, then the maxima
+      if constexpr (SM == kScoresPositions) {
+        // record (tile, row): kCodeWords words, lane group g4 at word 3 g4
         if (r < R) {
-          _Float16* dst = qbuf + ((st % kPosGroup) * R + r) * kSub;
-          typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-          f16x4_t h0 = {(_Float16)pv[0][0], (_Float16)pv[0][1], (_Float16)pv[0][2], (_Float16)pv[0][3]};
-          f16x4_t h1 = {(_Float16)pv[1][0], (_Float16)pv[1][1], (_Float16)pv[1][2], (_Float16)pv[1][3]};
-          *reinterpret_cast<f16x4_t*>(dst + 4 * g4) = h0;
-          *reinterpret_cast<f16x4_t*>(dst + 16 + 4 * g4) = h1;
-          if (g4 == 0) qmax[(st % kPosGroup) * 32 + r] = base;
-        }
-      } else if constexpr (SM == kScoresPositions) {
-        if (r < R) {
-          _Float16* dst = static_cast<_Float16*>(sc_val) + ((bkv * ntile_cap + tile) * R + r) * kSub;
-          typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-          f16x4_t h0 = {(_Float16)pv[0][0], (_Float16)pv[0][1], (_Float16)pv[0][2], (_Float16)pv[0][3]};
-          f16x4_t h1 = {(_Float16)pv[1][0], (_Float16)pv[1][1], (_Float16)pv[1][2], (_Float16)pv[1][3]};
-          *reinterpret_cast<f16x4_t*>(dst + 4 * g4) = h0;
-          *reinterpret_cast<f16x4_t*>(dst + 16 + 4 * g4) = h1;
-          if (g4 == 0) sc_max[(bkv * ntile_cap + tile) * max_stride(R) + r] = base;
+          uint32_t w0, w1, w2;
+          pack_codes(pf[nt], w0, w1, w2);
+          uint32_t* dst = QB ? qbuf + (r * kPosGroup + st % kPosGroup) * kCodeWords + 3 * g4
+                             : static_cast<uint32_t*>(sc_val) + code_record(bkv, ngrp, R, tile, r) + 3 * g4;
+          dst[0] = w0;
+          dst[1] = w1;
+          dst[2] = w2;
+          if (g4 == 0) {
+            if constexpr (QB) qmax[(st % kPosGroup) * RP + r] = base;
+            else sc_max[(bkv * ntile_cap + tile) * max_stride(R) + r] = base;
+          }
         }
       } else if constexpr (SM == kScoresPages) {
         // Each of the subtile's two pages: the row's probability mass on it (the
@@ -419,22 +459,27 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
       subtile(st, std::false_type{});
   };
   if constexpr (QB) {
-    // groups of kPosGroup subtiles; after each, the group's partials go out in
-    // one run (tiles are contiguous in the record array, R x 32 fp16 each, and
-    // their maxima records max_stride(R) floats each)
+    // groups of kPosGroup subtiles; after each, the group's partials go out
+    // (a row's records of consecutive tiles are contiguous within a group of
+    // kCodeGroup tiles; the maxima records are max_stride(R) floats per tile)
     const int tile0 = c0 / kSub;
     const int ms = max_stride(R);
     for (int g0 = 0; g0 < nsub; g0 += kPosGroup) {
       const int gn = min(kPosGroup, nsub - g0);
       for (int st = g0 + wave; st < g0 + gn; st += kVerWaves) run_subtile(st);
       __syncthreads();
-      const int n8 = gn * R * kSub / 8;  // 16 B chunks of probabilities
-      uint4* pd = reinterpret_cast<uint4*>(static_cast<_Float16*>(sc_val) + (bkv * ntile_cap + tile0 + g0) * R * kSub);
-      const uint4* ps = reinterpret_cast<const uint4*>(qbuf);
-      for (int t = tid; t < n8; t += kVerThreads) pd[t] = ps[t];
+      // 16 B chunks of codes, row-major over (row, tile) so neighbouring
+      // threads write neighbouring tiles of a row
+      uint32_t* pd = static_cast<uint32_t*>(sc_val);
+      constexpr int kChunks = kCodeWords / 4;
+      for (int t = tid; t < R * gn * kChunks; t += kVerThreads) {
+        const int part = t % kChunks, rt = t / kChunks, r = rt / gn, tl = rt % gn;
+        *reinterpret_cast<uint4*>(pd + code_record(bkv, ngrp, R, tile0 + g0 + tl, r) + 4 * part) =
+            *reinterpret_cast<const uint4*>(qbuf + (r * kPosGroup + tl) * kCodeWords + 4 * part);
+      }
       for (int t = tid; t < gn * R; t += kVerThreads) {
         const int tl = t / R, r = t % R;
-        sc_max[(bkv * ntile_cap + tile0 + g0 + tl) * ms + r] = qmax[tl * 32 + r];
+        sc_max[(bkv * ntile_cap + tile0 + g0 + tl) * ms + r] = qmax[tl * RP + r];
       }
       __syncthreads();
     }
@@ -616,11 +661,12 @@ __global__ __launch_bounds__(kVerThreads) void verify_generic_kernel(
 
 // Merge the splits of each (sequence, KV head) pair and normalise the score
 // partials. Blocks [0, nblk_o) each write 256 outputs of the merged rows;
-// the remaining blocks each normalise kFinTiles tiles of position partials
-// (PAGES: kVerThreads pages of page masses, one page per thread). Every
-// block first merges the per-split (max, sum) of all rows, in split order,
-// so every value is computed the same way by every block.
-constexpr int kFinTiles = kVerThreads / (kSub / 4);  // score tiles per finalize block (4 positions per thread)
+// the remaining blocks each normalise fin_tiles tiles of position partials
+// (float partials: 4 positions per thread; codes: a lane group's 8 per
+// thread) or, PAGES, kVerThreads pages of page masses, one page per thread.
+// Every block first merges the per-split (max, sum) of all rows, in split
+// order, so every value is computed the same way by every block.
+__host__ __device__ constexpr int fin_tiles(bool codes) { return codes ? kVerThreads / 4 : kVerThreads / (kSub / 4); }
 
 template <typename VT, int D, bool PAGES>
 __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
@@ -628,6 +674,8 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
     const float* __restrict__ sc_max, const int* __restrict__ seq_len, int k, int Hkv, int G, int chunk,
     int nsplit, int ntile_cap, int RP, int nblk_o, int x0, int balanced, float* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ scores, int score_stride) {
+  constexpr bool CODES = std::is_same<VT, uint32_t>::value && !PAGES;
+  constexpr int kFinTiles = fin_tiles(CODES);
   __shared__ float mrow[64], lrow[64], l2row[64];
   __shared__ float wt[PAGES ? 1 : kFinTiles][64];
   const int pair = blockIdx.y, tid = threadIdx.x;
@@ -702,29 +750,89 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
   const int ntiles = ceil_div(S, kSub);
   const int tile_end = min(ntiles, tile_beg + kFinTiles);
   // weights of every (tile, row) of this block, then 4 positions per thread
-  for (int e = tid; e < kFinTiles * R; e += kVerThreads) {
-    const int et = e / R, r = e % R, tile = tile_beg + et;
-    wt[et][r] = tile < tile_end ? exp2f_fast(sc_max[(bkv * ntile_cap + tile) * max_stride(R) + r] - l2row[r]) : 0.f;
+  // (the block's maxima records are one contiguous run: loads issued 4 at a time)
+  const float sh = CODES ? kCodeScaleLog2 : 0.f;
+  const int ms = max_stride(R);
+  for (int e0 = tid; e0 < kFinTiles * R; e0 += 4 * kVerThreads) {
+    float mv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + i * kVerThreads, et = e / R, r = e % R, tile = tile_beg + et;
+      mv[i] = (e < kFinTiles * R && tile < tile_end) ? sc_max[(bkv * ntile_cap + tile) * ms + r] : kNegInf;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + i * kVerThreads;
+      if (e < kFinTiles * R) wt[e / R][e % R] = mv[i] == kNegInf ? 0.f : exp2f_fast(mv[i] - l2row[e % R] + sh);
+    }
   }
   __syncthreads();
-  const int tl = tid / (kSub / 4), j4 = (tid % (kSub / 4)) * 4;
-  const int tile = tile_beg + tl, pos = tile * kSub + j4;
-  if (tile < tile_end && pos < S) {
-    const VT* vals = sc_val + (bkv * ntile_cap + tile) * R * kSub + j4;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int r = 0; r < R; ++r) {
-      const float w = wt[tl][r];
-      const VT* v = vals + r * kSub;
-      a0 = fmaf(w, (float)v[0], a0);
-      a1 = fmaf(w, (float)v[1], a1);
-      a2 = fmaf(w, (float)v[2], a2);
-      a3 = fmaf(w, (float)v[3], a3);
+  if constexpr (CODES) {
+    // wave = one group of kCodeGroup tiles, lane = (tile, lane group g4):
+    // positions 4 g4 .. +3 and 16 + 4 g4 .. +3 of the tile
+    const int tl = tid >> 2, g4 = tid & 3;
+    const int tile = tile_beg + tl, pos = tile * kSub + 4 * g4;
+    if (tile < tile_end && pos < S) {
+      const int ngrp = ceil_div(ntile_cap, kCodeGroup);
+      const uint32_t* rec = sc_val + code_record(bkv, ngrp, R, tile, 0) + 3 * g4;
+      float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      // rows in batches of kRowBatch, all loads of a batch issued first (rows
+      // past R re-read row R - 1 and carry weight 0)
+      constexpr int kRowBatch = 8;
+      for (int r0 = 0; r0 < R; r0 += kRowBatch) {
+        uint32_t wv[kRowBatch][3];
+#pragma unroll
+        for (int i = 0; i < kRowBatch; ++i) {
+          const uint32_t* v = rec + (size_t)min(r0 + i, R - 1) * kCodeGroup * kCodeWords;
+          wv[i][0] = v[0];
+          wv[i][1] = v[1];
+          wv[i][2] = v[2];
+        }
+#pragma unroll
+        for (int i = 0; i < kRowBatch; ++i) {
+          const float w = r0 + i < R ? wt[tl][r0 + i] : 0.f;  // includes 2^kCodeScaleLog2
+          const uint32_t w0 = wv[i][0], w1 = wv[i][1], w2 = wv[i][2];
+          constexpr uint32_t M = 0x0fff0000u;
+          const uint32_t f[8] = {(w0 << 16) & M, (w0 << 4) & M, __builtin_amdgcn_alignbit(w1, w0, 8) & M,
+                                 (w1 << 12) & M, w1 & M, __builtin_amdgcn_alignbit(w2, w1, 12) & M,
+                                 (w2 << 8) & M, (w2 >> 4) & M};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) a[j] = fmaf(w, __uint_as_float(f[j]), a[j]);
+        }
+      }
+      float* dst = scores + bkv * score_stride + tile * kSub + 4 * g4;
+      const bool vec = ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) && tile * kSub + kSub <= S;
+      if (vec) {
+        *reinterpret_cast<float4*>(dst) = make_float4(a[0], a[1], a[2], a[3]);
+        *reinterpret_cast<float4*>(dst + 16) = make_float4(a[4], a[5], a[6], a[7]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int pj = (j & 3) + 16 * (j >> 2);
+          if (pos + pj < S) dst[pj] = a[j];
+        }
+      }
     }
-    float* dst = scores + bkv * score_stride + pos;
-    dst[0] = a0;
-    if (pos + 1 < S) dst[1] = a1;
-    if (pos + 2 < S) dst[2] = a2;
-    if (pos + 3 < S) dst[3] = a3;
+  } else {
+    const int tl = tid / (kSub / 4), j4 = (tid % (kSub / 4)) * 4;
+    const int tile = tile_beg + tl, pos = tile * kSub + j4;
+    if (tile < tile_end && pos < S) {
+      const VT* vals = sc_val + (bkv * ntile_cap + tile) * R * kSub + j4;
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+      for (int r = 0; r < R; ++r) {
+        const float w = wt[tl][r];
+        const VT* v = vals + r * kSub;
+        a0 = fmaf(w, (float)v[0], a0);
+        a1 = fmaf(w, (float)v[1], a1);
+        a2 = fmaf(w, (float)v[2], a2);
+        a3 = fmaf(w, (float)v[3], a3);
+      }
+      float* dst = scores + bkv * score_stride + pos;
+      dst[0] = a0;
+      if (pos + 1 < S) dst[1] = a1;
+      if (pos + 2 < S) dst[2] = a2;
+      if (pos + 3 < S) dst[3] = a3;
+    }
   }
 }
 
@@ -779,7 +887,8 @@ VerifyPlan verify_plan(int B, int k, int Hq, int Hkv, int D, int dtype, int max_
     p.off_sc_max = off;
     off = align256(off + nbkv * p.ntile_cap * max_stride(p.R) * sizeof(float));
     p.off_sc_val = off;
-    off = align256(off + nbkv * p.ntile_cap * p.R * kSub * (p.mfma ? sizeof(_Float16) : sizeof(float)));
+    off = align256(off + (p.mfma ? nbkv * ceil_div(p.ntile_cap, kCodeGroup) * kCodeGroup * p.R * kCodeWords * sizeof(uint32_t)
+                                 : nbkv * p.ntile_cap * p.R * kSub * sizeof(float)));
     if (pages) {  // generic path: position scores staged for the page sums
       p.off_tmp = off;
       off = align256(off + nbkv * (size_t)max_seq_len * sizeof(float));
@@ -828,7 +937,7 @@ static hipError_t launch_finalize(const VerifyPlan& p, int D, const int* seq_len
   if (p.mfma && p.pages) {
     S3R_FIN(float, 128, true);
   } else if (p.mfma) {
-    S3R_FIN(_Float16, 128, false);
+    S3R_FIN(uint32_t, 128, false);
   } else if (D == 128) {
     S3R_FIN(float, 128, false);
   } else {
@@ -881,14 +990,14 @@ hipError_t launch_verify(int dtype, int D, const void* q, const void* kp, const 
   if (pages && !p.mfma && now) {
     // generic path: position scores into the workspace, then their page sums
     float* pos = (float*)(ws + p.off_tmp);
-    e = launch_finalize(p, D, seq_len, npairs, k, Hkv, 0, nblk_o + ceil_div(p.ntile_cap, kFinTiles), out, lse, pos,
+    e = launch_finalize(p, D, seq_len, npairs, k, Hkv, 0, nblk_o + ceil_div(p.ntile_cap, fin_tiles(false)), out, lse, pos,
                         max_seq_len, ws, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(page_sum_kernel, dim3(ceil_div(ceil_div(max_seq_len, kPage), 256), npairs), dim3(256), 0,
                        stream, pos, max_seq_len, seq_len, Hkv, scores, score_stride);
     return hipGetLastError();
   }
-  const int nblk_s = !now ? 0 : (pages ? ceil_div(2 * p.ntile_cap, kVerThreads) : ceil_div(p.ntile_cap, kFinTiles));
+  const int nblk_s = !now ? 0 : (pages ? ceil_div(2 * p.ntile_cap, kVerThreads) : ceil_div(p.ntile_cap, fin_tiles(p.mfma)));
   return launch_finalize(p, D, seq_len, npairs, k, Hkv, 0, nblk_o + nblk_s, out, lse, now ? scores : nullptr,
                          score_stride, ws, stream);
 }
@@ -898,7 +1007,7 @@ hipError_t launch_verify_scores(int dtype, int D, const int* seq_len, int B, int
                                 hipStream_t stream) {
   const VerifyPlan p = verify_plan(B, k, Hq, Hkv, D, dtype, max_seq_len, false);
   const int nblk_o = ceil_div(p.R * D, kVerThreads);
-  return launch_finalize(p, D, seq_len, B * Hkv, k, Hkv, nblk_o, ceil_div(p.ntile_cap, kFinTiles), nullptr,
+  return launch_finalize(p, D, seq_len, B * Hkv, k, Hkv, nblk_o, ceil_div(p.ntile_cap, fin_tiles(p.mfma)), nullptr,
                          nullptr, scores, score_stride, (const char*)ws, stream);
 }
 
