@@ -723,9 +723,18 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
     for (int t = t0; t < t1; t += kVerThreads) {
       const int r = t / D, d = t % D;
       float A = 0.f;
-      for (int c = 0; c < used; ++c) {
-        const size_t rc = (bkv * nsplit + c) * RP + r;
-        A += part_o[rc * D + d] * exp2f_fast(part_ml[rc * 2] - mrow[r]);
+      // splits in order, loads of 8 splits issued together
+      for (int c0 = 0; c0 < used; c0 += 8) {
+        float po[8], pm[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const size_t rc = (bkv * nsplit + min(c0 + i, used - 1)) * RP + r;
+          po[i] = part_o[rc * D + d];
+          pm[i] = part_ml[rc * 2];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (c0 + i < used) A += po[i] * exp2f_fast(pm[i] - mrow[r]);
       }
       const int i = r / G, h = kv * G + r % G;
       out[(((size_t)b * (k + 1) + i) * Hq + h) * D + d] = A / lrow[r];
@@ -736,13 +745,29 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
   if constexpr (PAGES) {
     // page score = sum over the rows of exp2(mass - log2 of the row's normaliser)
     // record slot i holds row (i % NT) * 16 + i / NT (NT = RP / 16 row tiles);
-    // the rows are summed in ascending order
+    // the rows are summed in slot order
     const int NT = RP / 16;
     const int page = page_beg + tid;
     if (page * kPage < S) {
-      const float* m = sc_val + (bkv * 2 * ntile_cap + page) * RP;
+      // the record (RP floats, 16 B aligned) loaded whole, 16 floats at a time
+      const float4* m4 = reinterpret_cast<const float4*>(sc_val + (bkv * 2 * ntile_cap + page) * RP);
       float acc = 0.f;
-      for (int r = 0; r < R; ++r) acc += exp2f_fast(m[(r & 15) * NT + (r >> 4)] - l2row[r]);
+      for (int i0 = 0; i0 < RP; i0 += 16) {
+        float m[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 v = m4[i0 / 4 + j];
+          m[4 * j] = v.x;
+          m[4 * j + 1] = v.y;
+          m[4 * j + 2] = v.z;
+          m[4 * j + 3] = v.w;
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int i = i0 + j, r = (i % NT) * 16 + i / NT;
+          if (r < R) acc += exp2f_fast(m[j] - l2row[r]);
+        }
+      }
       scores[bkv * score_stride + page] = acc;
     }
     return;
