@@ -120,6 +120,10 @@ __device__ __forceinline__ void pack_codes(const bf16x8_t& p, uint32_t& w0, uint
 // out within 2^-22 of their value; code 0 is 0.
 constexpr float kCodeScaleLog2 = 104.f;
 
+// Page records are gathered in LDS (and written as bf16) for up to two row
+// tiles; with more, the LDS holds the Q fragments and they go out as floats.
+__host__ __device__ constexpr bool page_records_bf16(int NT) { return NT <= 2 && kVerPageBurst; }
+
 // Score partials the split kernel writes (SM): none; per position (coded
 // probabilities relative to the row's reference maximum, plus that maximum per
 // tile); or per page (the log2 of the page's probability mass in the row).
@@ -140,10 +144,11 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
   // QL: Q rows as B fragments, slot (nt, kk, lane) = row nt*16 + lane%16,
   // elements kk*32 + 8*(lane/16) .. +8 (zero rows past R)
   __shared__ uint4 q_sh[QL ? NT * 4 * 64 : 1];
-  // Page scores with at most two row tiles: the split's page records are
-  // gathered here and written out in one contiguous burst at the end of the
-  // split (scattered 256 B writes during the stream cost far more).
-  constexpr bool PB = SM == kScoresPages && NT <= 2 && kVerPageBurst;
+  // Page scores with at most two row tiles: the split's page masses are
+  // gathered here and written out at the end of the split, in one contiguous
+  // burst and as bf16 relative to the split's row bases (scattered 256 B
+  // writes during the stream cost far more).
+  constexpr bool PB = SM == kScoresPages && page_records_bf16(NT);
   __shared__ __attribute__((aligned(16))) float pbuf[PB ? (kVerChunkMfma / kPage) * RP : 1];
   // Position scores: the partials of a group of kPosGroup consecutive
   // subtiles (probability codes and row maxima) are gathered here and written
@@ -487,15 +492,6 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
     for (int st = wave; st < nsub; st += kVerWaves) run_subtile(st);
   }
 
-  if constexpr (PB) {
-    // the split's page records, [c0 / 16, ceil(c1 / 16)), as one run of float4
-    __syncthreads();
-    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(sc_val) + (bkv * 2 * ntile_cap + c0 / kPage) * RP);
-    const float4* src = reinterpret_cast<const float4*>(pbuf);
-    const int n4 = ceil_div(c1 - c0, kPage) * RP / 4;
-    for (int t = tid; t < n4; t += kVerThreads) dst[t] = src[t];
-  }
-
   // Merge the waves: rows are lane % 16 (+16 nt); l is a per-lane partial.
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -511,6 +507,36 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
     }
   }
   __syncthreads();
+  if constexpr (PB) {
+    // The split's page records, pages [c0 / 16, ceil(c1 / 16)), written as one
+    // run once the split's row bases are known: per page RP bf16 slots in row
+    // order, each the page's probability mass relative to the base the split's
+    // (m, l) record carries (at most 2^12: 16 positions below 2^8 each), two
+    // rows a word. A thread keeps one pair of rows (kVerThreads is a multiple
+    // of RP / 2).
+    const int cw = tid % (RP / 2);
+    float bse[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 2 * cw + h;
+      float M = kNegInf;
+      for (int w = 0; w < kVerWaves; ++w) M = fmaxf(M, ml_sh[w][0][r]);
+      bse[h] = M == kNegInf ? 0.f : M;
+    }
+    uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(sc_val) + (bkv * 2 * ntile_cap + c0 / kPage) * RP);
+    const int nw = ceil_div(c1 - c0, kPage) * RP / 2;
+    for (int t = tid; t < nw; t += kVerThreads) {
+      const int pl = t / (RP / 2);
+      float v[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 2 * cw + h;
+        v[h] = r < R ? exp2f_fast(pbuf[pl * RP + (r & 15) * NT + (r >> 4)] - bse[h]) : 0.f;
+      }
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      dst[t] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)v[0], (__bf16)v[1]});
+    }
+  }
   float* obuf = reinterpret_cast<float*>(&vt[0][0]);  // RP x D floats (fits in the V buffers)
   float fac[NT];
 #pragma unroll
@@ -678,6 +704,7 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
   constexpr int kFinTiles = fin_tiles(CODES);
   __shared__ float mrow[64], lrow[64], l2row[64];
   __shared__ float wt[PAGES ? 1 : kFinTiles][64];
+  __shared__ float wsp[PAGES ? 4 : 1][64];  // page records in bf16: weights of the block's splits
   const int pair = blockIdx.y, tid = threadIdx.x;
   const int b = pair / Hkv, kv = pair % Hkv;
   const int S = seq_len[b];
@@ -742,7 +769,43 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
     }
     return;
   }
-  if constexpr (PAGES) {
+  if constexpr (PAGES && std::is_same<VT, uint16_t>::value) {
+    // bf16 page records (row order) relative to the base of the page's split:
+    // page score = sum over the rows, in order, of the split's weight
+    // exp2(base - log2 of the row's normaliser) times the record's mass. The
+    // block's 256 pages span at most 3 splits (a sequence cut into several
+    // splits has splits of at least 2048 positions); their weights go to LDS.
+    const int ch = balanced ? ceil_div(ceil_div(S, ceil_div(S, chunk)), kSub) * kSub : chunk;
+    const int npages = ceil_div(S, kPage);
+    const int s_lo = page_beg * kPage / ch;
+    const int s_hi = min(used - 1, (min(page_beg + kVerThreads, npages) - 1) * kPage / ch);
+    for (int e = tid; e < 4 * R; e += kVerThreads) {
+      const int i = e / R, r = e % R;
+      wsp[i][r] = s_lo + i <= s_hi ? exp2f_fast(part_ml[((bkv * nsplit + s_lo + i) * RP + r) * 2] - l2row[r]) : 0.f;
+    }
+    __syncthreads();
+    const int page = page_beg + tid;
+    if (page < npages) {
+      const int sp = page * kPage / ch, si = sp - s_lo;
+      const uint4* m4 = reinterpret_cast<const uint4*>(sc_val + (bkv * 2 * ntile_cap + page) * RP);
+      float acc = 0.f;
+      for (int i0 = 0; i0 < RP; i0 += 16) {
+        const uint4 ua = m4[i0 / 8], ub = m4[i0 / 8 + 1];
+        const uint32_t u[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int r = i0 + j;
+          if (r < R) {
+            const float w = si < 4 ? wsp[si][r]
+                                   : exp2f_fast(part_ml[((bkv * nsplit + sp) * RP + r) * 2] - l2row[r]);
+            acc = fmaf(w, __uint_as_float((j & 1) ? (u[j >> 1] & 0xffff0000u) : (u[j >> 1] << 16)), acc);
+          }
+        }
+      }
+      scores[bkv * score_stride + page] = acc;
+    }
+    return;
+  } else if constexpr (PAGES) {
     // page score = sum over the rows of exp2(mass - log2 of the row's normaliser)
     // record slot i holds row (i % NT) * 16 + i / NT (NT = RP / 16 row tiles);
     // the rows are summed in slot order
@@ -904,10 +967,11 @@ VerifyPlan verify_plan(int B, int k, int Hq, int Hkv, int D, int dtype, int max_
   off = align256(off + nbkv * p.nsplit * p.RP * 2 * sizeof(float));
   p.off_tmp = 0;
   if (pages && p.mfma) {
-    // one float per (page, row slot): 2 pages per subtile
+    // one value per (page, row slot): 2 pages per subtile; bf16 masses when
+    // the split kernel gathers them in LDS, float log2 masses otherwise
     p.off_sc_max = off;
     p.off_sc_val = off;
-    off = align256(off + nbkv * 2 * p.ntile_cap * p.RP * sizeof(float));
+    off = align256(off + nbkv * 2 * p.ntile_cap * p.RP * (page_records_bf16(p.NT) ? sizeof(uint16_t) : sizeof(float)));
   } else {
     p.off_sc_max = off;
     off = align256(off + nbkv * p.ntile_cap * max_stride(p.R) * sizeof(float));
@@ -959,7 +1023,9 @@ static hipError_t launch_finalize(const VerifyPlan& p, int D, const int* seq_len
                      (const VT*)(ws + p.off_sc_val), (const float*)(ws + p.off_sc_max), seq_len, k,  \
                      Hkv, p.G, p.chunk, p.nsplit, p.ntile_cap, p.RP, nblk_o, x0,                     \
                      (p.mfma && kVerBalance) ? 1 : 0, out, lse, scores, score_stride)
-  if (p.mfma && p.pages) {
+  if (p.mfma && p.pages && page_records_bf16(p.NT)) {
+    S3R_FIN(uint16_t, 128, true);
+  } else if (p.mfma && p.pages) {
     S3R_FIN(float, 128, true);
   } else if (p.mfma) {
     S3R_FIN(uint32_t, 128, false);
