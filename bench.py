@@ -616,8 +616,8 @@ def run_rollout(args, cfg, torch, s3r):
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": ("s3r_verify_attn_pages: verify_mfma_kernel (split pass with the last-split merge, page scores)"
-                       if pages else
+            "kernel": ("s3r_verify_attn_pages: verify_mfma_kernel (split pass, page masses) + verify_finalize_kernel "
+                       "(merge, page scores)" if pages else
                        "s3r_verify_attn: verify_mfma_kernel (split pass) + verify_finalize_kernel (merge, scores)")
                       + ", per layer; unique bytes (shared prefix once per group)",
             "bound": "hbm",
