@@ -687,12 +687,13 @@ __global__ __launch_bounds__(kVerThreads) void verify_generic_kernel(
 
 // Merge the splits of each (sequence, KV head) pair and normalise the score
 // partials. Blocks [0, nblk_o) each write 256 outputs of the merged rows;
-// the remaining blocks each normalise fin_tiles tiles of position partials
-// (float partials: 4 positions per thread; codes: a lane group's 8 per
-// thread) or, PAGES, kVerThreads pages of page masses, one page per thread.
+// the remaining blocks each normalise kFinTiles tiles of position partials
+// (4 positions per thread: float partials, or a lane group's codes on one
+// page of a subtile) or, PAGES, kVerThreads pages of page masses, one page
+// per thread.
 // Every block first merges the per-split (max, sum) of all rows, in split
 // order, so every value is computed the same way by every block.
-__host__ __device__ constexpr int fin_tiles(bool codes) { return codes ? kVerThreads / 4 : kVerThreads / (kSub / 4); }
+constexpr int kFinTiles = kVerThreads / (kSub / 4);  // score tiles per finalize block (8 threads per tile)
 
 template <typename VT, int D, bool PAGES>
 __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
@@ -701,9 +702,8 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
     int nsplit, int ntile_cap, int RP, int nblk_o, int x0, int balanced, float* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ scores, int score_stride) {
   constexpr bool CODES = std::is_same<VT, uint32_t>::value && !PAGES;
-  constexpr int kFinTiles = fin_tiles(CODES);
   __shared__ float mrow[64], lrow[64], l2row[64];
-  __shared__ float wt[PAGES ? 1 : kFinTiles][64];
+  __shared__ float wt[PAGES ? 1 : kFinTiles][65];  // padded: a wave's tiles read distinct banks
   __shared__ float wsp[PAGES ? 4 : 1][64];  // page records in bf16: weights of the block's splits
   const int pair = blockIdx.y, tid = threadIdx.x;
   const int b = pair / Hkv, kv = pair % Hkv;
@@ -857,48 +857,44 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
   __syncthreads();
   if constexpr (CODES) {
     // wave = one group of kCodeGroup tiles, lane = (tile, lane group g4):
-    // positions 4 g4 .. +3 and 16 + 4 g4 .. +3 of the tile
-    const int tl = tid >> 2, g4 = tid & 3;
-    const int tile = tile_beg + tl, pos = tile * kSub + 4 * g4;
+    // thread (tile, lane group g4, page h): positions 16 h + 4 g4 .. +3
+    const int tl = tid >> 3, g4 = (tid >> 1) & 3, h = tid & 1;
+    const int tile = tile_beg + tl, pos = tile * kSub + 16 * h + 4 * g4;
     if (tile < tile_end && pos < S) {
       const int ngrp = ceil_div(ntile_cap, kCodeGroup);
-      const uint32_t* rec = sc_val + code_record(bkv, ngrp, R, tile, 0) + 3 * g4;
-      float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      // rows in batches of kRowBatch, all loads of a batch issued first (rows
-      // past R re-read row R - 1 and carry weight 0)
+      const uint32_t* rec = sc_val + code_record(bkv, ngrp, R, tile, 0) + 3 * g4 + h;
+      float a[4] = {0.f, 0.f, 0.f, 0.f};
       constexpr int kRowBatch = 8;
       for (int r0 = 0; r0 < R; r0 += kRowBatch) {
-        uint32_t wv[kRowBatch][3];
+        uint32_t wv[kRowBatch][2];
 #pragma unroll
         for (int i = 0; i < kRowBatch; ++i) {
           const uint32_t* v = rec + (size_t)min(r0 + i, R - 1) * kCodeGroup * kCodeWords;
           wv[i][0] = v[0];
           wv[i][1] = v[1];
-          wv[i][2] = v[2];
         }
 #pragma unroll
         for (int i = 0; i < kRowBatch; ++i) {
-          const float w = r0 + i < R ? wt[tl][r0 + i] : 0.f;  // includes 2^kCodeScaleLog2
-          const uint32_t w0 = wv[i][0], w1 = wv[i][1], w2 = wv[i][2];
+          const float w = r0 + i < R ? wt[tl][r0 + i] : 0.f;
+          const uint32_t x = wv[i][0], y = wv[i][1];
           constexpr uint32_t M = 0x0fff0000u;
-          const uint32_t f[8] = {(w0 << 16) & M, (w0 << 4) & M, __builtin_amdgcn_alignbit(w1, w0, 8) & M,
-                                 (w1 << 12) & M, w1 & M, __builtin_amdgcn_alignbit(w2, w1, 12) & M,
-                                 (w2 << 8) & M, (w2 >> 4) & M};
-#pragma unroll
-          for (int j = 0; j < 8; ++j) a[j] = fmaf(w, __uint_as_float(f[j]), a[j]);
+          const uint32_t f0 = h ? x & M : (x << 16) & M;
+          const uint32_t f1 = h ? __builtin_amdgcn_alignbit(y, x, 12) & M : (x << 4) & M;
+          const uint32_t f2 = h ? (y << 8) & M : __builtin_amdgcn_alignbit(y, x, 8) & M;
+          const uint32_t f3 = h ? (y >> 4) & M : (y << 12) & M;
+          a[0] = fmaf(w, __uint_as_float(f0), a[0]);
+          a[1] = fmaf(w, __uint_as_float(f1), a[1]);
+          a[2] = fmaf(w, __uint_as_float(f2), a[2]);
+          a[3] = fmaf(w, __uint_as_float(f3), a[3]);
         }
       }
-      float* dst = scores + bkv * score_stride + tile * kSub + 4 * g4;
-      const bool vec = ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) && tile * kSub + kSub <= S;
-      if (vec) {
+      float* dst = scores + bkv * score_stride + pos;
+      if (((reinterpret_cast<uintptr_t>(dst) & 15) == 0) && pos + 4 <= S) {
         *reinterpret_cast<float4*>(dst) = make_float4(a[0], a[1], a[2], a[3]);
-        *reinterpret_cast<float4*>(dst + 16) = make_float4(a[4], a[5], a[6], a[7]);
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int pj = (j & 3) + 16 * (j >> 2);
-          if (pos + pj < S) dst[pj] = a[j];
-        }
+        for (int j = 0; j < 4; ++j)
+          if (pos + j < S) dst[j] = a[j];
       }
     }
   } else {
@@ -1081,14 +1077,14 @@ hipError_t launch_verify(int dtype, int D, const void* q, const void* kp, const 
   if (pages && !p.mfma && now) {
     // generic path: position scores into the workspace, then their page sums
     float* pos = (float*)(ws + p.off_tmp);
-    e = launch_finalize(p, D, seq_len, npairs, k, Hkv, 0, nblk_o + ceil_div(p.ntile_cap, fin_tiles(false)), out, lse, pos,
+    e = launch_finalize(p, D, seq_len, npairs, k, Hkv, 0, nblk_o + ceil_div(p.ntile_cap, kFinTiles), out, lse, pos,
                         max_seq_len, ws, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(page_sum_kernel, dim3(ceil_div(ceil_div(max_seq_len, kPage), 256), npairs), dim3(256), 0,
                        stream, pos, max_seq_len, seq_len, Hkv, scores, score_stride);
     return hipGetLastError();
   }
-  const int nblk_s = !now ? 0 : (pages ? ceil_div(2 * p.ntile_cap, kVerThreads) : ceil_div(p.ntile_cap, fin_tiles(p.mfma)));
+  const int nblk_s = !now ? 0 : (pages ? ceil_div(2 * p.ntile_cap, kVerThreads) : ceil_div(p.ntile_cap, kFinTiles));
   return launch_finalize(p, D, seq_len, npairs, k, Hkv, 0, nblk_o + nblk_s, out, lse, now ? scores : nullptr,
                          score_stride, ws, stream);
 }
@@ -1098,7 +1094,7 @@ hipError_t launch_verify_scores(int dtype, int D, const int* seq_len, int B, int
                                 hipStream_t stream) {
   const VerifyPlan p = verify_plan(B, k, Hq, Hkv, D, dtype, max_seq_len, false);
   const int nblk_o = ceil_div(p.R * D, kVerThreads);
-  return launch_finalize(p, D, seq_len, B * Hkv, k, Hkv, nblk_o, ceil_div(p.ntile_cap, fin_tiles(p.mfma)), nullptr,
+  return launch_finalize(p, D, seq_len, B * Hkv, k, Hkv, nblk_o, ceil_div(p.ntile_cap, kFinTiles), nullptr,
                          nullptr, scores, score_stride, (const char*)ws, stream);
 }
 
