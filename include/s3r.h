@@ -267,7 +267,10 @@ s3r_status s3r_length_order(const int32_t* len, int32_t B, int32_t* order, hipSt
  * probability):
  *   scores[b][kv][j] = sum_{h in group(kv)} sum_{i : j <= P_i} prob_{b,i,h}(j)
  * for j < seq_len[b]; entries at and beyond seq_len[b] are not written. The
- * scores of one (b, kv) sum to G (k + 1).
+ * scores of one (b, kv) sum to G (k + 1). Precision: with bf16 K/V and
+ * head_dim 128 each probability enters the scores as the bf16 value that also
+ * weights V (relative step 2^-8; probabilities under 2^-22 of the row's running
+ * maximum may come out anywhere below that fraction); otherwise float32.
  *
  *   q         device [B][k+1][Hq][head_dim] in kv->dtype.
  *   seq_len   device i32 [B]: cache length including the block,
@@ -297,7 +300,10 @@ s3r_status s3r_verify_attn(const void* q, const s3r_paged_kv* kv, const int32_t*
  *   page_scores[b][kv][p] = sum_{j in page p, j < seq_len[b]} scores[b][kv][j],
  * for p < ceil(seq_len[b] / 16); later entries are not written. The split
  * pass keeps one value per (page, query row) instead of one per (position,
- * query row), so the pass writes 16x fewer partial bytes.
+ * query row), so the pass writes 16x fewer partial bytes. Precision: with
+ * bf16 K/V, head_dim 128 and at most 32 query rows per KV head the page
+ * masses are kept as bf16 relative to the split's row maxima (relative step
+ * 2^-8); otherwise float32.
  *
  *   page_scores device f32 [B][Hkv][page_stride], required;
  *   page_stride >= ceil(max_seq_len / 16);
