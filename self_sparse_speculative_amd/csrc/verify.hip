@@ -5,8 +5,9 @@
 // complete historical KV cache. [listing] "S^3R: Fast and Faithful RL Rollouts
 // via Self-Sparse Speculative Decoding", Table 7: verification (T_V) is one
 // eager pass over the whole cache. [explainer] "S3R - Self-sparse speculative
-// rollouts for RL - What does it mean?", mechanism paragraph: the selector's
-// scores come from the verifier's last attention pass.
+// rollouts for RL - What does it mean?", mechanism paragraph: what the
+// selector ranks is the attention the previous verification paid to each
+// position.
 //
 // Work split: one workgroup per (split, KV head, sequence); a split is a fixed
 // chunk of the context (at most 4096 positions on the MFMA path, sized evenly). The (k+1) * G query
