@@ -64,8 +64,12 @@ __device__ __forceinline__ void exp64_init(Exp64Table& tab) {
 
 __device__ __forceinline__ double exp64(double x, const Exp64Table& tab) {
   x = fmax(x, -1000.0);
-  const double kf = rint(x * (kExpTab / 0.6931471805599453));
-  const int ki = (int)kf;
+  // m = round(x 128 / ln2): adding 1.5 * 2^52 leaves the integer in the low
+  // word of the sum (round to nearest even), and subtracting it again gives m
+  constexpr double kShift = 6755399441055744.0;
+  const double t = fma(x, kExpTab / 0.6931471805599453, kShift);
+  const int ki = __double2loint(t);
+  const double kf = t - kShift;
   const double r = fma(-kf, 0.6931471805599453 / kExpTab, x);
   double p = fma(r, 1.0 / 24.0, 1.0 / 6.0);
   p = fma(r, p, 0.5);
