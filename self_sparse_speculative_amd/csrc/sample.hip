@@ -144,7 +144,9 @@ __device__ __forceinline__ void stat_add(Stat& st, float z, int y, double invT, 
   st.m = up ? z : st.m;
 }
 
-template <bool GREEDY>
+// UNIT: temperature 1, where the exponent's factor 1 / T is 1 and its
+// multiply is dropped (the same values: the product is exact).
+template <bool GREEDY, bool UNIT>
 __global__ __launch_bounds__(kSmpThreads) void row_stats_kernel(
     const float* __restrict__ zt, const float* __restrict__ zd, int k, int V, double invT,
     float* __restrict__ smax, double* __restrict__ ssum, int* __restrict__ sarg) {
@@ -157,6 +159,7 @@ __global__ __launch_bounds__(kSmpThreads) void row_stats_kernel(
   const float* z = logit_row(zt, zd, b, r, k, V);
   Stat st = {kNegInf, 0.0, 0x7fffffff};
   constexpr bool gr = GREEDY;
+  auto sc = [&](double x) { return UNIT ? x : x * invT; };
   if ((V & 3) == 0) {
     const float4* z4 = reinterpret_cast<const float4*>(z);
     const int n4 = V >> 2;
@@ -185,14 +188,14 @@ __global__ __launch_bounds__(kSmpThreads) void row_stats_kernel(
         if (__any(gm > st.m)) {
           const bool up = gm > st.m;
           const int gi = v.x == gm ? 0 : (v.y == gm ? 1 : (v.z == gm ? 2 : 3));
-          const double a = st.m == kNegInf ? 0.0 : exp64(((double)st.m - (double)gm) * invT, tab);
+          const double a = st.m == kNegInf ? 0.0 : exp64(sc(((double)st.m - (double)gm)), tab);
           st.s = up ? st.s * a : st.s;
           st.i = up ? 4 * t + gi : st.i;
           st.m = up ? gm : st.m;
         }
         const double m = (double)st.m;
-        st.s += exp64(((double)v.x - m) * invT, tab) + exp64(((double)v.y - m) * invT, tab) +
-                exp64(((double)v.z - m) * invT, tab) + exp64(((double)v.w - m) * invT, tab);
+        st.s += exp64(sc((double)v.x - m), tab) + exp64(sc((double)v.y - m), tab) +
+                exp64(sc((double)v.z - m), tab) + exp64(sc((double)v.w - m), tab);
       }
     }
   } else {
@@ -223,8 +226,10 @@ __global__ __launch_bounds__(kSmpThreads) void row_stats_kernel(
 
 // Probability of logit z in a row with maximum m and normaliser s, given as
 // inv_s = 1 / s (one division per row instead of one per token).
+template <bool UNIT = false>
 __device__ __forceinline__ double prob(float z, float m, double inv_s, double invT, const Exp64Table& tab) {
-  return exp64(((double)z - (double)m) * invT, tab) * inv_s;
+  const double x = (double)z - (double)m;
+  return exp64(UNIT ? x : x * invT, tab) * inv_s;
 }
 
 __global__ __launch_bounds__(kWave) void decide_kernel(
@@ -273,6 +278,7 @@ __global__ __launch_bounds__(kWave) void decide_kernel(
   }
 }
 
+template <bool UNIT>
 __global__ __launch_bounds__(kSmpThreads) void chunk_sum_kernel(
     const float* __restrict__ zt, const float* __restrict__ zd, int k, int V, double invT,
     const float* __restrict__ smax, const double* __restrict__ ssum, const int* __restrict__ desc,
@@ -307,9 +313,9 @@ __global__ __launch_bounds__(kSmpThreads) void chunk_sum_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (y0u + u * kSmpThreads >= y1) continue;
-      const double p = prob(zt_v[u], mt, inv_st, invT, tab);
+      const double p = prob<UNIT>(zt_v[u], mt, inv_st, invT, tab);
       double w = p;
-      if (resid) w = fmax(0.0, p - prob(zd_v[u], md, inv_sd, invT, tab));
+      if (resid) w = fmax(0.0, p - prob<UNIT>(zd_v[u], md, inv_sd, invT, tab));
       aw += w;
       ap += p;
     }
@@ -471,11 +477,15 @@ hipError_t launch_spec_sample(const float* zt, const float* zd, const int* dtok,
   SampleWs w = sample_ws(ws, B, k, nullptr);
   const int greedy = temperature == 0.f;
   const double invT = greedy ? 0.0 : 1.0 / (double)temperature;
+  const bool unit = temperature == 1.f;
   if (greedy)
-    hipLaunchKernelGGL(row_stats_kernel<true>, dim3(2 * k + 1, B), dim3(kSmpThreads), 0, stream, zt, zd,
-                       k, V, invT, w.smax, w.ssum, w.sarg);
+    hipLaunchKernelGGL((row_stats_kernel<true, false>), dim3(2 * k + 1, B), dim3(kSmpThreads), 0, stream, zt,
+                       zd, k, V, invT, w.smax, w.ssum, w.sarg);
+  else if (unit)
+    hipLaunchKernelGGL((row_stats_kernel<false, true>), dim3(2 * k + 1, B), dim3(kSmpThreads), 0, stream, zt,
+                       zd, k, V, invT, w.smax, w.ssum, w.sarg);
   else
-    hipLaunchKernelGGL(row_stats_kernel<false>, dim3(2 * k + 1, B), dim3(kSmpThreads), 0, stream, zt,
+    hipLaunchKernelGGL((row_stats_kernel<false, false>), dim3(2 * k + 1, B), dim3(kSmpThreads), 0, stream, zt,
                        zd, k, V, invT, w.smax, w.ssum, w.sarg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -483,8 +493,12 @@ hipError_t launch_spec_sample(const float* zt, const float* zd, const int* dtok,
                      greedy, w.smax, w.ssum, w.sarg, tokens, n_out, accepted, w.desc);
   e = hipGetLastError();
   if (e != hipSuccess || greedy) return e;
-  hipLaunchKernelGGL(chunk_sum_kernel, dim3(kSmpChunks, B), dim3(kSmpThreads), 0, stream, zt, zd, k,
-                     V, invT, w.smax, w.ssum, w.desc, w.csum);
+  if (unit)
+    hipLaunchKernelGGL(chunk_sum_kernel<true>, dim3(kSmpChunks, B), dim3(kSmpThreads), 0, stream, zt, zd, k,
+                       V, invT, w.smax, w.ssum, w.desc, w.csum);
+  else
+    hipLaunchKernelGGL(chunk_sum_kernel<false>, dim3(kSmpChunks, B), dim3(kSmpThreads), 0, stream, zt, zd, k,
+                       V, invT, w.smax, w.ssum, w.desc, w.csum);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(final_draw_kernel, dim3(B), dim3(kSmpThreads), 0, stream, zt, zd, u, k, V, invT,
