@@ -181,3 +181,41 @@ def test_read_pattern_kernels_run_in_bounds_and_deterministically():
                                sink=torch.zeros(nd, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(c, d)
+
+
+@pytest.mark.parametrize("cid,ov,lengths", [
+    (3, {"B": 4}, [31, 32, 4093, 9001]),                # two row tiles, ragged tails, 1-3 splits
+    (2, {"B": 3}, [17, 6000, 16390]),                   # one row tile (Qwen3-1.7B rows)
+    (5, {"B": 2, "k": 8}, [5000, 12287]),               # three row tiles
+])
+def test_verify_scores_do_not_depend_on_the_score_stride(cid, ov, lengths):
+    """The finalize writes a score row with vector stores where the row start and the tile allow it
+    and with single stores elsewhere: the same scores, bit for bit, for a ragged stride, a multiple
+    of 4 and a multiple of 32 plus 4, and nothing written at or past a sequence's end."""
+    cfg = get_config(cid, **ov)
+    batch = make_batch(cfg, lengths=np.array(lengths, np.int32), parts=("kv", "q"))
+    t = to_dev(batch)
+    ms = int(batch.seq_len.max())
+    print(f"[stride] config {cid} k={cfg.k} G={cfg.G} lengths {lengths}", flush=True)
+    res = []
+    for stride in (ms, (ms + 3) // 4 * 4, (ms + 31) // 32 * 32 + 4):
+        sc = torch.full((cfg.B, cfg.Hkv, stride), -7.0, dtype=torch.float32, device="cuda")
+        out, lse, _ = s3r.verify_attn(t["q_verify"], t["kv"], t["seq_len"], cfg.k, float(batch.scale), ms,
+                                      scores=sc)
+        torch.cuda.synchronize()
+        sc = sc.cpu().numpy()
+        for b in range(cfg.B):
+            S = int(batch.seq_len[b])
+            assert (sc[b, :, S:] == -7.0).all(), (stride, b)
+        res.append((sc, out.cpu().numpy()))
+    for sc, out in res[1:]:
+        assert np.array_equal(out, res[0][1])
+        for b in range(cfg.B):
+            S = int(batch.seq_len[b])
+            assert np.array_equal(sc[b, :, :S], res[0][0][b, :, :S]), b
+    # and the scores are the oracle's
+    for b in range(cfg.B):
+        S = int(batch.seq_len[b])
+        _, _, rs = oracle.verify(batch.q_verify[b], batch.k_pages, batch.v_pages, batch.block_table[b], S, cfg.k,
+                                 float(batch.scale))
+        assert (np.abs(res[0][0][b, :, :S] - rs).max(axis=1) / rs.max(axis=1)).max() <= 2e-2, b
