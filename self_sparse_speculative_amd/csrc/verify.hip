@@ -538,7 +538,16 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
       dst[t] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)v[0], (__bf16)v[1]});
     }
   }
-  float* obuf = reinterpret_cast<float*>(&vt[0][0]);  // RP x D floats (fits in the V buffers)
+  // The waves' output accumulators are summed in LDS (the V buffers, free
+  // now), rows padded to OS floats so that the 16 rows a wave writes at one
+  // column fall in distinct banks. Up to two row tiles there is room for two
+  // buffers: waves 0 and 1 write them, waves 2 and 3 add into them, and their
+  // sum goes out ((w0 + w2) + (w1 + w3)); with more, one buffer and the waves
+  // in turn. Only the R real rows are written to the split's record.
+  constexpr int OS = D + 4;
+  constexpr bool TWO = NT <= 2;
+  static_assert((TWO ? 2 : 1) * RP * OS * sizeof(float) <= sizeof(vt), "merge buffers exceed the V buffers");
+  float* obuf = reinterpret_cast<float*>(&vt[0][0]);
   float fac[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -548,27 +557,43 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
     const float base = M == kNegInf ? 0.f : M;
     fac[nt] = exp2f_fast(m_run[nt] - base);
   }
-  for (int w = 0; w < kVerWaves; ++w) {
-    if (wave == w) {
+  auto put = [&](float* buf, bool add) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int o = (nt * 16 + n16) * D + dt * 16 + g4 * 4 + v;
-            const float val = oacc[nt][dt][v] * fac[nt];
-            obuf[o] = (w == 0) ? val : obuf[o] + val;
-          }
+      for (int dt = 0; dt < 8; ++dt) {
+        float4* dst = reinterpret_cast<float4*>(buf + (nt * 16 + n16) * OS + dt * 16 + g4 * 4);
+        float4 val = make_float4(oacc[nt][dt][0] * fac[nt], oacc[nt][dt][1] * fac[nt], oacc[nt][dt][2] * fac[nt],
+                                 oacc[nt][dt][3] * fac[nt]);
+        if (add) {
+          const float4 o = *dst;
+          val = make_float4(o.x + val.x, o.y + val.y, o.z + val.z, o.w + val.w);
         }
+        *dst = val;
       }
     }
-    __syncthreads();
-  }
+  };
   const size_t rec = (bkv * nsplit + split) * RP;
   float4* po = reinterpret_cast<float4*>(part_o + rec * D);
-  const float4* ob4 = reinterpret_cast<const float4*>(obuf);
-  for (int t = tid; t < RP * D / 4; t += kVerThreads) po[t] = ob4[t];
+  constexpr int C4 = D / 4;
+  if constexpr (TWO) {
+    if (wave < 2) put(obuf + wave * RP * OS, false);
+    __syncthreads();
+    if (wave >= 2) put(obuf + (wave - 2) * RP * OS, true);
+    __syncthreads();
+    for (int t = tid; t < R * C4; t += kVerThreads) {
+      const float4 a = *reinterpret_cast<const float4*>(obuf + (t / C4) * OS + (t % C4) * 4);
+      const float4 c = *reinterpret_cast<const float4*>(obuf + RP * OS + (t / C4) * OS + (t % C4) * 4);
+      po[t] = make_float4(a.x + c.x, a.y + c.y, a.z + c.z, a.w + c.w);
+    }
+  } else {
+    for (int w = 0; w < kVerWaves; ++w) {
+      if (wave == w) put(obuf, w > 0);
+      __syncthreads();
+    }
+    for (int t = tid; t < R * C4; t += kVerThreads)
+      po[t] = *reinterpret_cast<const float4*>(obuf + (t / C4) * OS + (t % C4) * 4);
+  }
   if (tid < RP) {
     float M = kNegInf;
     for (int w = 0; w < kVerWaves; ++w) M = fmaxf(M, ml_sh[w][0][tid]);
