@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--k", type=int, default=None)
     ap.add_argument("--sigma", type=float, default=None)
     ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--heads", type=str, default=None,
+                    help="query/KV heads as HQ/HKV, e.g. 16/4: one tensor-parallel rank's share of the model")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--layers", type=int, default=None,
                     help="stacked layers (the rollout workload has 28; 1 times one layer of it)")
@@ -958,6 +960,9 @@ def main():
         ov["noise_std"] = args.sigma
     if args.batch is not None:
         ov["B"] = args.batch
+    if args.heads is not None:
+        hq, hkv = args.heads.split("/")
+        ov["Hq"], ov["Hkv"] = int(hq), int(hkv)
     if args.layers is not None:
         ov["layers"] = args.layers
     cfg = get_config(args.config, **ov)

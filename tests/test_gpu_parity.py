@@ -623,3 +623,30 @@ def test_full_size_24k_round_sampled():
     idx2, n2 = run_select(cfg, batch, t, scores=torch.from_numpy(vsc).cuda())
     torch.cuda.synchronize()
     _check_select(cfg, batch, vsc, idx2, n2, units[:8])
+
+
+def test_tp2_rank_share_at_24k():
+    """One tensor-parallel rank's share of Qwen3-8B at the 24K workload: 16 query heads over 4 KV heads
+    (half of 32 / 8), the shape one GPU holds when the heads are split over two; every step of the
+    round against the oracle on sampled units, sampling on every sequence."""
+    cfg, batch, t = _batch("c5tp2", 5, Hq=16, Hkv=4, B=16)
+    order = torch.empty((cfg.B,), dtype=torch.int32, device="cuda")
+    idx, n_sel = run_select(cfg, batch, t, order=order)
+    outs = run_draft_steps(cfg, batch, t, idx, n_sel, order=order)
+    vout, vlse, vsc = run_verify(cfg, batch, t)
+    toks, nout, acc = run_sample(cfg, batch, t)
+    torch.cuda.synchronize()
+    _check_select(cfg, batch, batch.scores, idx, n_sel, [(b, kv) for b in range(0, cfg.B, 5) for kv in range(cfg.Hkv)])
+    idx_np, ns = idx.cpu().numpy(), n_sel.cpu().numpy()
+    vout, vsc = vout.cpu().numpy(), vsc.cpu().numpy()
+    for b in [0, cfg.B - 1]:
+        L, S = int(batch.ctx_len[b]), int(batch.seq_len[b])
+        for j in (1, cfg.k):
+            ro, _ = oracle.sparse_decode(batch.q_draft[j - 1, b], batch.k_pages, batch.v_pages, batch.block_table[b],
+                                         idx_np[b], int(ns[b]), L, L + j, float(batch.scale))
+            assert rel_err_rows(outs[j - 1][0][b].cpu().numpy(), ro) <= TOL_BF16
+        ro, rl, rs = oracle.verify(batch.q_verify[b], batch.k_pages, batch.v_pages, batch.block_table[b], S, cfg.k,
+                                   float(batch.scale))
+        assert rel_err_rows(vout[b], ro) <= TOL_BF16
+        assert (np.abs(vsc[b, :, :S] - rs).max(axis=1) / rs.max(axis=1)).max() <= TOL_BF16
+    _check_sample(cfg, batch, toks, nout, acc, batch.temperature, range(cfg.B))
