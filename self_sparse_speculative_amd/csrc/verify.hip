@@ -890,7 +890,7 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
       const int ngrp = ceil_div(ntile_cap, kCodeGroup);
       const uint32_t* rec = sc_val + code_record(bkv, ngrp, R, tile, 0) + 3 * g4 + h;
       float a[4] = {0.f, 0.f, 0.f, 0.f};
-      constexpr int kRowBatch = 8;
+      constexpr int kRowBatch = 7;  // divides R at G = 2 and 4 with k = 6 (14, 28 rows)
       for (int r0 = 0; r0 < R; r0 += kRowBatch) {
         uint32_t wv[kRowBatch][2];
 #pragma unroll
