@@ -712,7 +712,7 @@ __global__ __launch_bounds__(kVerThreads) void verify_generic_kernel(
 }
 
 // Merge the splits of each (sequence, KV head) pair and normalise the score
-// partials. Blocks [0, nblk_o) each write 256 outputs of the merged rows;
+// partials. Blocks [0, nblk_o) each write 256 (page form: 512) outputs of the merged rows;
 // the remaining blocks each normalise kFinTiles tiles of position partials
 // (4 positions per thread: float partials, or a lane group's codes on one
 // page of a subtile) or, PAGES, kVerThreads pages of page masses, one page
@@ -771,26 +771,38 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
   }
   __syncthreads();
   if (x < nblk_o) {
-    const int t0 = x * kVerThreads + tid;
-    const int t1 = min(R * D, (x + 1) * kVerThreads);
-    for (int t = t0; t < t1; t += kVerThreads) {
+    // EPT neighbouring elements (r, d .. d + EPT - 1) per thread: two for the
+    // page form, whose finalize is mostly this merge (one measured slower for
+    // the position form, whose score blocks dominate)
+    constexpr int EPT = PAGES ? 2 : 1;
+    const int t = (x * kVerThreads + tid) * EPT;
+    if (t < R * D) {
       const int r = t / D, d = t % D;
-      float A = 0.f;
+      float A[EPT];
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) A[e] = 0.f;
       // splits in order, loads of 8 splits issued together
       for (int c0 = 0; c0 < used; c0 += 8) {
-        float po[8], pm[8];
+        float po[8][EPT], pm[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const size_t rc = (bkv * nsplit + min(c0 + i, used - 1)) * RP + r;
-          po[i] = part_o[rc * D + d];
+#pragma unroll
+          for (int e = 0; e < EPT; ++e) po[i][e] = part_o[rc * D + d + e];
           pm[i] = part_ml[rc * 2];
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (c0 + i < used) A += po[i] * exp2f_fast(pm[i] - mrow[r]);
+        for (int i = 0; i < 8; ++i) {
+          if (c0 + i < used) {
+            const float w = exp2f_fast(pm[i] - mrow[r]);
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) A[e] += po[i][e] * w;
+          }
+        }
       }
       const int i = r / G, h = kv * G + r % G;
-      out[(((size_t)b * (k + 1) + i) * Hq + h) * D + d] = A / lrow[r];
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) out[(((size_t)b * (k + 1) + i) * Hq + h) * D + d + e] = A[e] / lrow[r];
       if (lse != nullptr && d == 0) lse[((size_t)b * (k + 1) + i) * Hq + h] = l2row[r] * kLn2;
     }
     return;
@@ -950,6 +962,11 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Output-merge blocks of the finalize (two elements per thread in the page form).
+static int fin_out_blocks(const VerifyPlan& p, int D) {
+  return ceil_div(p.R * D, kVerThreads * ((p.mfma && p.pages) ? 2 : 1));
+}
+
 // Page scores of the generic path: the position scores (staged in the
 // workspace, row stride `stride`) summed over each page in slot order.
 __global__ __launch_bounds__(256) void page_sum_kernel(const float* __restrict__ pos_scores, int stride,
@@ -1037,7 +1054,7 @@ static hipError_t launch_finalize(const VerifyPlan& p, int D, const int* seq_len
                                   int Hkv, int x0, int nx, float* out, float* lse, float* scores,
                                   int score_stride, const char* ws, hipStream_t stream) {
   if (nx <= 0) return hipSuccess;
-  const int nblk_o = ceil_div(p.R * D, kVerThreads);
+  const int nblk_o = fin_out_blocks(p, D);
   const dim3 grid(nx, npairs);
 #define S3R_FIN(VT, DD, PG)                                                                          \
   hipLaunchKernelGGL((verify_finalize_kernel<VT, DD, PG>), grid, dim3(kVerThreads), 0, stream,      \
@@ -1098,7 +1115,7 @@ hipError_t launch_verify(int dtype, int D, const void* q, const void* kp, const 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nblk_o = ceil_div(p.R * D, kVerThreads);
+  const int nblk_o = fin_out_blocks(p, D);
   const bool now = scores != nullptr && !defer_scores;
   if (pages && !p.mfma && now) {
     // generic path: position scores into the workspace, then their page sums
@@ -1119,7 +1136,7 @@ hipError_t launch_verify_scores(int dtype, int D, const int* seq_len, int B, int
                                 int max_seq_len, float* scores, int score_stride, const void* ws,
                                 hipStream_t stream) {
   const VerifyPlan p = verify_plan(B, k, Hq, Hkv, D, dtype, max_seq_len, false);
-  const int nblk_o = ceil_div(p.R * D, kVerThreads);
+  const int nblk_o = fin_out_blocks(p, D);
   return launch_finalize(p, D, seq_len, B * Hkv, k, Hkv, nblk_o, ceil_div(p.ntile_cap, kFinTiles), nullptr,
                          nullptr, scores, score_stride, (const char*)ws, stream);
 }
