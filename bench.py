@@ -110,8 +110,15 @@ def source_sha(path):
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
-def load_traffic(kernel_src, key):
-    """Counter-measured HBM bytes per launch from the committed summary, if it is current.
+def workload_shape(cfg):
+    """The fields of a workload that fix the verification's traffic."""
+    return {"config": cfg.cid, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "D": cfg.D, "k": cfg.k,
+            "lengths": list(cfg.lengths)}
+
+
+def load_traffic(kernel_src, key, cfg):
+    """Counter-measured HBM bytes per launch from the committed summary, if it is current and was
+    measured on this workload's shape.
 
     key: "one_call" (s3r_verify_attn), "pages" (s3r_verify_attn_pages), "rows" (split pass + output
     merge, the deferred call) or "rollout_layer" (s3r_verify_attn on one rollout layer)."""
@@ -120,6 +127,9 @@ def load_traffic(kernel_src, key):
         return None
     rec = json.load(open(path))
     if rec.get("source_sha") != source_sha(kernel_src):
+        return None
+    shapes = rec.get("workload_shapes", {})
+    if shapes.get(key) != json.loads(json.dumps(workload_shape(cfg))):
         return None
     per = rec.get("bytes_per_launch")
     return per.get(key) if isinstance(per, dict) else None
@@ -629,7 +639,7 @@ def run_rollout(args, cfg, torch, s3r):
             "unit": "GB/s",
             "frac": round(gbs(ver_uni_launch, t_ver_launch) / HBM_PEAK_GBS, 4),
             "traffic": None if pages else load_traffic(
-                os.path.join(ROOT, "self_sparse_speculative_amd", "csrc", "verify.hip"), "rollout_layer"),
+                os.path.join(ROOT, "self_sparse_speculative_amd", "csrc", "verify.hip"), "rollout_layer", cfg),
             "algorithmic_bytes_per_launch": int(ver_uni_launch),
             "logical_bytes_per_launch": int(ver_log_launch),
             "ms_per_launch": round(t_ver_launch, 4),
@@ -988,7 +998,7 @@ def main():
         return
     r = measure_round(args, cfg, batch, t, s3r, torch)
     traffic = load_traffic(os.path.join(ROOT, "self_sparse_speculative_amd", "csrc", "verify.hip"),
-                           "pages" if args.page_scores else ("rows" if args.overlap_scores else "one_call"))
+                           "pages" if args.page_scores else ("rows" if args.overlap_scores else "one_call"), cfg)
     copy_gbs, read_gbs = reference_rates(args, torch)
     cpu = None
     if not args.no_cpu:

@@ -77,3 +77,25 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_counter_traffic_is_reported_only_for_the_profiled_source_and_shape(tmp_path, monkeypatch):
+    import json
+
+    import bench
+    from s3r_inputs import get_config
+
+    src = os.path.join(bench.ROOT, "self_sparse_speculative_amd", "csrc", "verify.hip")
+    c5 = get_config(5)
+    rec = {"source_sha": bench.source_sha(src), "bytes_per_launch": {"one_call": 123},
+           "workload_shapes": {"one_call": bench.workload_shape(c5)}}
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "verify_traffic.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.load_traffic(src, "one_call", c5) == 123
+    assert bench.load_traffic(src, "one_call", get_config(5, Hq=16, Hkv=4)) is None   # another shape
+    assert bench.load_traffic(src, "one_call", get_config(5, k=8)) is None
+    assert bench.load_traffic(src, "pages", c5) is None                                # no record
+    rec["source_sha"] = "0" * 16                                                       # another source
+    (tmp_path / "profiles" / "verify_traffic.json").write_text(json.dumps(rec))
+    assert bench.load_traffic(src, "one_call", c5) is None
