@@ -121,7 +121,7 @@ def load_traffic(kernel_src, key, cfg):
     measured on this workload's shape.
 
     key: "one_call" (s3r_verify_attn), "pages" (s3r_verify_attn_pages), "rows" (split pass + output
-    merge, the deferred call) or "rollout_layer" (s3r_verify_attn on one rollout layer)."""
+    merge, the deferred call), "rollout_layer" or "rollout_layer_pages" (one rollout layer)."""
     path = os.path.join(ROOT, "profiles", "verify_traffic.json")
     if not os.path.exists(path):
         return None
@@ -638,8 +638,8 @@ def run_rollout(args, cfg, torch, s3r):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gbs(ver_uni_launch, t_ver_launch) / HBM_PEAK_GBS, 4),
-            "traffic": None if pages else load_traffic(
-                os.path.join(ROOT, "self_sparse_speculative_amd", "csrc", "verify.hip"), "rollout_layer", cfg),
+            "traffic": load_traffic(os.path.join(ROOT, "self_sparse_speculative_amd", "csrc", "verify.hip"),
+                                    "rollout_layer_pages" if pages else "rollout_layer", cfg),
             "algorithmic_bytes_per_launch": int(ver_uni_launch),
             "logical_bytes_per_launch": int(ver_log_launch),
             "ms_per_launch": round(t_ver_launch, 4),
