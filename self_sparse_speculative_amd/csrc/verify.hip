@@ -89,8 +89,9 @@ __device__ __forceinline__ uint32_t u4_word(const uint4& v, int i) {
 constexpr uint32_t kCodeBias = 0x3400u;  // bf16 pattern of 2^-23
 constexpr int kCodeWords = kSub * 12 / 32;  // words per (subtile, row) record
 // Records are grouped by 16 consecutive tiles: group, then row, then the 16
-// tiles' records side by side, so the finalize's wave (one group, lane =
-// (tile, lane group)) reads each row's 16 records as one contiguous run.
+// tiles' records side by side, so a finalize wave (8 tiles of a group; lane =
+// tile, lane group, page) reads each row's records of its tiles as one
+// contiguous run.
 constexpr int kCodeGroup = 16;
 __host__ __device__ __forceinline__ size_t code_record(size_t bkv, int ngrp, int R, int tile, int r) {
   return ((bkv * ngrp + (tile >> 4)) * R + r) * (kCodeGroup * kCodeWords) + (tile & 15) * kCodeWords;
@@ -122,12 +123,14 @@ __device__ __forceinline__ void pack_codes(const bf16x8_t& p, uint32_t& w0, uint
 constexpr float kCodeScaleLog2 = 104.f;
 
 // Page records are gathered in LDS (and written as bf16) for up to two row
-// tiles; with more, the LDS holds the Q fragments and they go out as floats.
+// tiles; with three the LDS already holds the Q fragments, with four the
+// buffer would take 64 KB, and they go out as floats as they are formed.
 __host__ __device__ constexpr bool page_records_bf16(int NT) { return NT <= 2 && kVerPageBurst; }
 
 // Score partials the split kernel writes (SM): none; per position (coded
 // probabilities relative to the row's reference maximum, plus that maximum per
-// tile); or per page (the log2 of the page's probability mass in the row).
+// tile); or per page (the page's probability mass in the row: bf16 relative
+// to the split's row base, or its float log2 beyond two row tiles).
 constexpr int kScoresNone = 0, kScoresPositions = 1, kScoresPages = 2;
 
 template <int NT, bool QL, int SM>
