@@ -349,6 +349,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
 
   for (int st = wave; st < nsub; st += kWaves) {
     const int j0 = st * kDsub;  // subtile start within the split
+    // the gathered K and V rows are read once: nontemporal loads
     dbf16x8_t kf[2][4];
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
       const size_t row = (size_t)rows[jj < cnt ? jj : j0];
       const bf16_t* kb = kp + row * D + g4 * 8;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) kf[pt][kk] = *reinterpret_cast<const dbf16x8_t*>(kb + kk * 32);
+      for (int kk = 0; kk < 4; ++kk) kf[pt][kk] = __builtin_bit_cast(dbf16x8_t, load_nt16(kb + kk * 32));
     }
     uint4 vraw[2][4];
 #pragma unroll
@@ -369,7 +370,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
       for (int v = 0; v < 4; ++v) {
         const int jj = j0 + pbase + v;
         const size_t row = (size_t)rows[jj < cnt ? jj : j0];
-        vraw[tt][v] = *reinterpret_cast<const uint4*>(vp + row * D + c * 8);
+        vraw[tt][v] = load_nt16_u4(vp + row * D + c * 8);
       }
     }
     df32x4_t s[2];

@@ -4,7 +4,9 @@
 // subtiles of two pages; the kept rows of one draft step), in the same launch
 // shape (workgroups of 256 threads, the verification's splits of at most 4096
 // positions on the XCD-grouped 1-D grid, the draft's splits of at most 2048
-// positions), and fold the loaded words into one 32-bit checksum per
+// positions), with the same cache hints (nontemporal loads for the
+// verification's V rows and for every row of a draft step, ordinary loads for
+// the verification's K rows), and fold the loaded words into one 32-bit checksum per
 // workgroup so that no load is dropped. Their time is the read ceiling the
 // attention kernels are measured against; nothing in the method uses them.
 
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(kRpThreads, 2) void read_verify_pattern_kernel(
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         w[pt * 8 + kk] = *reinterpret_cast<const uint4*>(kp + row + kk * 32);
-        w[pt * 8 + 4 + kk] = *reinterpret_cast<const uint4*>(vp + row + kk * 32);
+        w[pt * 8 + 4 + kk] = load_nt16_u4(vp + row + kk * 32);
       }
     }
 #pragma unroll
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(kRpThreads, 2) void read_draft_pattern_kernel(
     // a wave takes 4 rows per step (16 lanes per row, 16 B per lane)
     for (int j = wave * 4 + g4; j < p1 - p0; j += kRpWaves * 4) {
       const size_t row = (size_t)rows[j] * D + n16 * 8;
-      acc ^= fold4(*reinterpret_cast<const uint4*>(kp + row)) ^ fold4(*reinterpret_cast<const uint4*>(vp + row));
+      acc ^= fold4(load_nt16_u4(kp + row)) ^ fold4(load_nt16_u4(vp + row));
     }
   }
   for (int m = 32; m >= 1; m >>= 1) acc ^= __shfl_xor(acc, m, kWave);

@@ -170,7 +170,12 @@ __global__ __launch_bounds__(kSmpThreads) void row_stats_kernel(
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int t = t0 + u * kSmpThreads;
-        vv[u] = t < n4 ? z4[t] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+        if (t < n4) {
+          const u32x4_t w = load_nt16(z4 + t);
+          vv[u] = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
+        } else {
+          vv[u] = make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+        }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {

@@ -243,6 +243,8 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
     page_a = pages_sh[2 * st];
     page_b = (c0 + st * kSub + 16 < S) ? pages_sh[2 * st + 1] : page_a;
   };
+  // K with ordinary loads (two instructions complete each line), V with
+  // nontemporal ones (8 rows x 128 B per instruction, read once)
   auto load_k = [&](int st, Sub& d) {
     int page_a, page_b;
     sub_pages(st, page_a, page_b);
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
       const int page = a < 4 ? page_a : page_b;
       const bf16_t* vb = vp + (((size_t)page * Hkv + kv) * kPage + (a & 3) * 4) * D + c * 8;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) d.vraw[tt][v] = *reinterpret_cast<const uint4*>(vb + v * D);
+      for (int v = 0; v < 4; ++v) d.vraw[tt][v] = load_nt16_u4(vb + v * D);
     }
   };
 
@@ -478,17 +480,18 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
       for (int st = g0 + wave; st < g0 + gn; st += kVerWaves) run_subtile(st);
       __syncthreads();
       // 16 B chunks of codes, row-major over (row, tile) so neighbouring
-      // threads write neighbouring tiles of a row
+      // threads write neighbouring tiles of a row; nontemporal stores, since
+      // the finalize reads them only after the rest of the split pass
       uint32_t* pd = static_cast<uint32_t*>(sc_val);
       constexpr int kChunks = kCodeWords / 4;
       for (int t = tid; t < R * gn * kChunks; t += kVerThreads) {
         const int part = t % kChunks, rt = t / kChunks, r = rt / gn, tl = rt % gn;
-        *reinterpret_cast<uint4*>(pd + code_record(bkv, ngrp, R, tile0 + g0 + tl, r) + 4 * part) =
-            *reinterpret_cast<const uint4*>(qbuf + (r * kPosGroup + tl) * kCodeWords + 4 * part);
+        store_nt16(pd + code_record(bkv, ngrp, R, tile0 + g0 + tl, r) + 4 * part,
+                   *reinterpret_cast<const u32x4_t*>(qbuf + (r * kPosGroup + tl) * kCodeWords + 4 * part));
       }
       for (int t = tid; t < gn * R; t += kVerThreads) {
         const int tl = t / R, r = t % R;
-        sc_max[(bkv * ntile_cap + tile0 + g0 + tl) * ms + r] = qmax[tl * RP + r];
+        __builtin_nontemporal_store(qmax[tl * RP + r], sc_max + (bkv * ntile_cap + tile0 + g0 + tl) * ms + r);
       }
       __syncthreads();
     }
