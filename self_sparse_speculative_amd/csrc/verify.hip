@@ -17,7 +17,8 @@
 // bf16, head_dim 128 (verify_mfma_kernel): the rows are the N side of
 // 16x16x32 bf16 MFMA tiles; a 1-D grid puts consecutive splits of one
 // (sequence, KV head) pair on one XCD. Per 32-position subtile a wave
-//   - loads K straight from the page into A fragments (16 B per lane) and
+//   - loads each page's K block with whole lines per instruction (1 KB per
+//     wave), reshapes it into A fragments through its LDS buffer, and
 //     computes S^T = K Q^T (positions x rows) with Q^T resident in registers
 //     (read from LDS for three row tiles, see kVerQLds);
 //   - keeps the online-softmax state per row in the lanes that hold that row
@@ -236,23 +237,25 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
   const int nsub = ceil_div(c1 - c0, kSub);
 
   struct Sub {
-    bf16x8_t kf[2][4];  // K rows as A fragments: lane (n16 = position in the 16-row tile, g4 = k group)
+    bf16x8_t kf[2][4];  // K chunks as loaded: page pt, chunk 64 i + lane of its 4 KB block
     uint4 vraw[2][4];   // V rows for the LDS transpose: task = (4 positions a, 8-wide d chunk c)
   };
   auto sub_pages = [&](int st, int& page_a, int& page_b) {
     page_a = pages_sh[2 * st];
     page_b = (c0 + st * kSub + 16 < S) ? pages_sh[2 * st + 1] : page_a;
   };
-  // K with ordinary loads (two instructions complete each line), V with
-  // nontemporal ones (8 rows x 128 B per instruction, read once)
+  // K: each page's 4 KB block with 1 KB contiguous per wave instruction
+  // (whole lines; ordinary loads), reshaped into the operand fragments through
+  // LDS at the start of the subtile. V: nontemporal loads (8 rows x 128 B per
+  // instruction, read once).
   auto load_k = [&](int st, Sub& d) {
     int page_a, page_b;
     sub_pages(st, page_a, page_b);
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
-      const bf16_t* kb = kp + (((size_t)(pt ? page_b : page_a) * Hkv + kv) * kPage + n16) * D + g4 * 8;
+      const bf16_t* kb = kp + ((size_t)(pt ? page_b : page_a) * Hkv + kv) * kPage * D + lane * 8;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) d.kf[pt][kk] = *reinterpret_cast<const bf16x8_t*>(kb + kk * 32);
+      for (int i = 0; i < 4; ++i) d.kf[pt][i] = *reinterpret_cast<const bf16x8_t*>(kb + i * 512);
     }
   };
   auto load_v = [&](int st, Sub& d) {
@@ -282,8 +285,27 @@ __global__ __launch_bounds__(kVerThreads, (NT <= 2 || QL) ? 2 : 1) void verify_m
   auto subtile = [&](int st, auto edge_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
     const int pos0 = c0 + st * kSub;
-    const auto& kf = cur.kf;
     const auto& vraw = cur.vraw;
+    // K through the wave's LDS buffer: the chunks go in as loaded (row
+    // 16 pt + 4 i + lane / 16, 16 B chunk lane % 16; rows padded to 272 B so
+    // the fragment reads of 16 rows hit distinct banks), the A fragments come
+    // out: lane (n16 = position in the 16-row tile, g4 = k group)
+    constexpr int kKStride = D + 8;
+    static_assert(2 * kPage * kKStride <= D * kVtStride, "K subtile exceeds the wave's LDS buffer");
+    wave_lds_sync();  // the previous subtile's reads of the buffer precede these writes
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<bf16x8_t*>(my_vt + (pt * 16 + i * 4 + (lane >> 4)) * kKStride + (lane & 15) * 8) =
+            cur.kf[pt][i];
+    wave_lds_sync();  // each lane reads rows written by other lanes
+    bf16x8_t kf[2][4];
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        kf[pt][kk] = *reinterpret_cast<const bf16x8_t*>(my_vt + (pt * 16 + n16) * kKStride + kk * 32 + g4 * 8);
 
     // S^T = K Q^T: s[pt][nt][v] is position pos0 + pt*16 + 4*g4 + v, row nt*16 + n16
     f32x4_t s[2][NT];
