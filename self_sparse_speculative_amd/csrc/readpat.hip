@@ -4,9 +4,10 @@
 // subtiles of two pages; the kept rows of one draft step), in the same launch
 // shape (workgroups of 256 threads, the verification's splits of at most 4096
 // positions on the XCD-grouped 1-D grid, the draft's splits of at most 2048
-// positions), with the same cache hints (nontemporal loads for the
-// verification's V rows and for every row of a draft step, ordinary loads for
-// the verification's K rows), and fold the loaded words into one 32-bit checksum per
+// positions), with the same per-instruction layout and cache hints
+// (nontemporal loads for the verification's V rows and for every row of a
+// draft step, ordinary whole-line loads for the verification's K pages), and
+// fold the loaded words into one 32-bit checksum per
 // workgroup so that no load is dropped. Their time is the read ceiling the
 // attention kernels are measured against; nothing in the method uses them.
 
@@ -22,7 +23,8 @@ constexpr int kRpSub = 32;
 __device__ __forceinline__ uint32_t fold4(uint4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
 
 // Verification pattern: K and V of every position [0, seq_len[b]) of each
-// (sequence, KV head), 16 B per lane per load, waves on alternate subtiles.
+// (sequence, KV head), 16 B per lane per load in the verification's own
+// per-instruction layout, waves on alternate subtiles.
 __global__ __launch_bounds__(kRpThreads, 2) void read_verify_pattern_kernel(
     const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp, const int* __restrict__ bt, int max_pages,
     int npairs, int Hkv, const int* __restrict__ seq_len, int chunk, int nsplit, uint32_t* __restrict__ sink) {
@@ -38,7 +40,6 @@ __global__ __launch_bounds__(kRpThreads, 2) void read_verify_pattern_kernel(
   if (c0 >= S) return;
   const int c1 = min(S, c0 + ch);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n16 = lane & 15, g4 = lane >> 4;
   const int npg = ceil_div(c1 - c0, kPage);
   const int* bt_row = bt + (size_t)b * max_pages;
   for (int t = tid; t < npg; t += kRpThreads) pages_sh[t] = bt_row[(c0 >> 4) + t];
@@ -49,14 +50,24 @@ __global__ __launch_bounds__(kRpThreads, 2) void read_verify_pattern_kernel(
     const int page_a = pages_sh[2 * st];
     const int page_b = (c0 + st * kRpSub + 16 < S) ? pages_sh[2 * st + 1] : page_a;
     uint4 w[16];
+    // K as the verification loads it: each page's 4 KB block, 1 KB
+    // contiguous per wave instruction, ordinary loads
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
-      const size_t row = (((size_t)(pt ? page_b : page_a) * Hkv + kv) * kPage + n16) * D + g4 * 8;
+      const bf16_t* kb = kp + ((size_t)(pt ? page_b : page_a) * Hkv + kv) * kPage * D + lane * 8;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        w[pt * 8 + kk] = *reinterpret_cast<const uint4*>(kp + row + kk * 32);
-        w[pt * 8 + 4 + kk] = load_nt16_u4(vp + row + kk * 32);
-      }
+      for (int i = 0; i < 4; ++i) w[pt * 4 + i] = *reinterpret_cast<const uint4*>(kb + i * 512);
+    }
+    // V as the verification loads it for its transpose: lane task (4 positions
+    // a, 16 B chunk c), 8 rows x 128 B per instruction, nontemporal loads
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int task = lane + 64 * tt;
+      const int a = task & 7, c = task >> 3;
+      const int page = a < 4 ? page_a : page_b;
+      const bf16_t* vb = vp + (((size_t)page * Hkv + kv) * kPage + (a & 3) * 4) * D + c * 8;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) w[8 + tt * 4 + v] = load_nt16_u4(vb + v * D);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc ^= fold4(w[i]);

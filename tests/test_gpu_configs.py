@@ -181,6 +181,47 @@ def test_read_pattern_kernels_run_in_bounds_and_deterministically():
                                sink=torch.zeros(nd, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(c, d)
+    # each workgroup's word is the xor of every 32-bit word it must read: pins the bytes each
+    # pattern covers (the K and V blocks of a verification subtile's two pages, the rows of a
+    # draft split's kept positions), computed here from the same cache arrays
+    kw = batch.k_pages.view(np.uint32)
+    vw = batch.v_pages.view(np.uint32)
+    page_x = np.bitwise_xor.reduce(kw.reshape(kw.shape[0], cfg.Hkv, -1), axis=2) ^ \
+        np.bitwise_xor.reduce(vw.reshape(vw.shape[0], cfg.Hkv, -1), axis=2)  # [page][KV head]
+    chunk_v, nsplit = 4096, -(-ms // 4096)
+    want = np.zeros(nv, np.uint32)
+    for pair in range(cfg.B * cfg.Hkv):
+        bb, kv = divmod(pair, cfg.Hkv)
+        S = int(batch.seq_len[bb])
+        ch = -(-(-(-S // -(-S // chunk_v))) // 32) * 32
+        for split in range(nsplit):
+            c0 = split * ch
+            if c0 >= S:
+                continue
+            acc = np.uint32(0)
+            for st in range(-(-(min(S, c0 + ch) - c0) // 32)):
+                pa = batch.block_table[bb, (c0 >> 4) + 2 * st]
+                pb = batch.block_table[bb, (c0 >> 4) + 2 * st + 1] if c0 + st * 32 + 16 < S else pa
+                acc ^= page_x[pa, kv] ^ page_x[pb, kv]
+            want[((pair // 8) * nsplit + split) * 8 + pair % 8] = acc
+    assert np.array_equal(a.cpu().numpy().view(np.uint32), want)
+    idx_h, ns_h = idx.cpu().numpy(), n_sel.cpu().numpy()
+    krow = kw.reshape(kw.shape[0], cfg.Hkv, 16, -1)
+    vrow = vw.reshape(vw.shape[0], cfg.Hkv, 16, -1)
+    nsd = -(-(cap + 1) // 2048)
+    chunk_d = -(-(-(-(cap + 1) // nsd)) // 32) * 32
+    want_d = np.zeros(nd, np.uint32)
+    for bb in range(cfg.B):
+        L, ns = int(batch.ctx_len[bb]), int(ns_h[bb])  # kept positions per KV head of the sequence
+        for kv in range(cfg.Hkv):
+            pos = np.concatenate([idx_h[bb, kv, :ns], [L]]).astype(np.int64)  # kept positions + [L, L + 1)
+            for split in range(nsd):
+                acc = np.uint32(0)
+                for p_ in pos[split * chunk_d:(split + 1) * chunk_d]:
+                    pg = batch.block_table[bb, p_ >> 4]
+                    acc ^= np.bitwise_xor.reduce(krow[pg, kv, p_ & 15]) ^ np.bitwise_xor.reduce(vrow[pg, kv, p_ & 15])
+                want_d[(bb * cfg.Hkv + kv) * nsd + split] = acc
+    assert np.array_equal(c.cpu().numpy().view(np.uint32), want_d)
 
 
 @pytest.mark.parametrize("cid,ov,lengths", [
