@@ -14,7 +14,10 @@ N(0, 3) target logits and draft logits = target + N(0, 0.3). Inputs are
 seeded synthetic data resident in HBM before timing starts.
 
 A step is one round over the batch. Each round's selection reads the scores
-the previous round's verification wrote. Prints one JSON line.
+the previous round's verification wrote. Prints one JSON line; the default
+line (position scores, the headline) also carries the same workload's round
+with page scores (s3r_verify_attn_pages + s3r_select_pages), timed on the same
+resident inputs after it, as "page_scores_round".
 """
 
 import argparse
@@ -74,6 +77,8 @@ def parse():
                     help="read ceiling of the attention kernels on the workload: the verification's and a draft "
                          "step's read patterns with no arithmetic (s3r_read_*_pattern), beside the verification "
                          "without scores, with page scores and with position scores, and the draft step")
+    ap.add_argument("--no-page-line", action="store_true",
+                    help="skip the page-score round the default line carries beside the position-score headline")
     ap.add_argument("--copy-gib", type=float, default=2.0,
                     help="size of the device-to-device copy timed as the HBM reference (0 to skip)")
     return ap.parse_args()
@@ -996,7 +1001,30 @@ def main():
     if args.read_ceiling:
         print(json.dumps(run_read_ceiling(args, cfg, batch, t, torch, s3r)))
         return
+    headline_form = (args.select_unit == 1 and not args.select_all_heads and not args.page_scores
+                     and not args.overlap_scores)
+    scores0 = t["scores"].clone() if headline_form and not args.no_page_line else None
     r = measure_round(args, cfg, batch, t, s3r, torch)
+    page_line = None
+    if scores0 is not None:
+        # The same workload with page scores (s3r_verify_attn_pages + s3r_select_pages), on the
+        # same resident inputs, first-round scores restored: reported beside the headline, never
+        # as its value.
+        print("[bench] timing the page-score round on the same inputs", file=sys.stderr, flush=True)
+        t["scores"].copy_(scores0)
+        del scores0
+        rp = measure_round(argparse.Namespace(**{**vars(args), "page_scores": True}), cfg, batch, t, s3r, torch)
+        bp = rp["breakdown"]
+        page_line = {
+            "form": "s3r_verify_attn_pages + s3r_select_pages (one score per page of 16 positions, whole pages kept)",
+            "value": round(rp["value"], 1), "unit": "verified tokens/s", "ms_per_step": round(rp["ms_step"], 4),
+            "verify_ms": round(rp["t_ver"], 4), "verify_algorithmic_bytes_per_launch": rp["ver_bytes"],
+            "verify_frac_of_hbm_peak": round(rp["ver_gbs"] / HBM_PEAK_GBS, 4),
+            "verify_traffic": load_traffic(os.path.join(ROOT, "self_sparse_speculative_amd", "csrc", "verify.hip"),
+                                           "pages", cfg),
+            "draft_plus_verify_frac_of_hbm_peak": bp["draft_plus_verify_frac_of_hbm_peak"],
+            "verified_tokens_per_round": bp["verified_tokens_per_round"], "ms": bp["ms"],
+        }
     traffic = load_traffic(os.path.join(ROOT, "self_sparse_speculative_amd", "csrc", "verify.hip"),
                            "pages" if args.page_scores else ("rows" if args.overlap_scores else "one_call"), cfg)
     copy_gbs, read_gbs = reference_rates(args, torch)
@@ -1051,6 +1079,8 @@ def main():
         "cpu_baseline": cpu,
         "breakdown": breakdown,
     }
+    if page_line is not None:
+        res["page_scores_round"] = page_line
     print(json.dumps(res))
 
 

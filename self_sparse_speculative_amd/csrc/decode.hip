@@ -268,14 +268,16 @@ __device__ __forceinline__ uint32_t du4_word(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-__global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
+template <int NW>
+__global__ __launch_bounds__(NW * kWave, 2) void sparse_decode_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
     const int* __restrict__ bt, int max_pages, int Hkv, int G, const int* __restrict__ idx,
     int nsel_cap, const int* __restrict__ n_sel, const int* __restrict__ sel_len,
     const int* __restrict__ cur_len, const int* __restrict__ order, float scale_log2, int chunk, int nsplit,
     float* __restrict__ part, float* __restrict__ out, float* __restrict__ lse) {
   constexpr int D = 128;
-  constexpr int kWaves = kDecThreads / kWave;
+  constexpr int kWaves = NW;
+  constexpr int kThreads = NW * kWave;
   __shared__ __attribute__((aligned(16))) uint16_t vt[kWaves][D * kDvtStride];
   __shared__ float ml_sh[kWaves][2][16];
   __shared__ int rows[kDecChunkMfma];
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
   const int Hq = Hkv * G;
   if (p0 >= total) {
     if (nsplit == 1) {  // nothing attended: zero output, lse = -inf
-      for (int t = tid; t < G * D; t += kDecThreads) {
+      for (int t = tid; t < G * D; t += kThreads) {
         out[((size_t)b * Hq + kv * G + t / D) * D + t % D] = 0.f;
         if (lse != nullptr && t % D == 0) lse[(size_t)b * Hq + kv * G + t / D] = kNegInf;
       }
@@ -321,21 +323,21 @@ __global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
   // so the two dependent round trips are paid once, not once per position.
   const int* idx_row = idx + ((size_t)b * Hkv + kv) * nsel_cap;
   const int* bt_row = bt + (size_t)b * max_pages;
-  constexpr int kRes = kDecChunkMfma / kDecThreads;
+  constexpr int kRes = kDecChunkMfma / kThreads;
   int rpos[kRes], rpg[kRes];
 #pragma unroll
   for (int u = 0; u < kRes; ++u) {
-    const int j = p0 + tid + u * kDecThreads;
+    const int j = p0 + tid + u * kThreads;
     rpos[u] = j < p1 ? (j < ns ? idx_row[j] : L + (j - ns)) : 0;
   }
 #pragma unroll
   for (int u = 0; u < kRes; ++u) {
-    const int j = p0 + tid + u * kDecThreads;
+    const int j = p0 + tid + u * kThreads;
     rpg[u] = j < p1 ? bt_row[rpos[u] >> 4] : 0;
   }
 #pragma unroll
   for (int u = 0; u < kRes; ++u) {
-    const int j = p0 + tid + u * kDecThreads;
+    const int j = p0 + tid + u * kThreads;
     if (j < p1) rows[j - p0] = (rpg[u] * Hkv + kv) * kPage + (rpos[u] & 15);
   }
   __syncthreads();
@@ -469,7 +471,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
   if (nsplit == 1) {
     // The only split: normalise here (same arithmetic as the split merge with
     // one split, whose weight is exp2(0) = 1).
-    for (int t = tid; t < G * D; t += kDecThreads) {
+    for (int t = tid; t < G * D; t += kThreads) {
       const int g = t / D, d = t % D;
       float Mg = kNegInf;
       for (int w = 0; w < kWaves; ++w) Mg = fmaxf(Mg, ml_sh[w][0][g]);
@@ -482,7 +484,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void sparse_decode_mfma_kernel(
     }
     return;
   }
-  for (int t = tid; t < G * D; t += kDecThreads) {
+  for (int t = tid; t < G * D; t += kThreads) {
     const int g = t / D, d = t % D;
     float* rec = part + (((size_t)b * Hq + kv * G + g) * nsplit + split) * (D + 2);
     rec[2 + d] = obuf[g * D + d];
@@ -590,7 +592,8 @@ hipError_t launch_sparse_decode(int dtype, int D, int G, const void* q, const vo
     const int att = max_attend < 1 ? 1 : max_attend;
     const int ns = ceil_div(att, kDecChunkMfma);
     const int chunk = kDecBalance ? ceil_div(ceil_div(att, ns), kDsub) * kDsub : kDecChunkMfma;
-    hipLaunchKernelGGL(sparse_decode_mfma_kernel, dim3(ns, Hkv, B), dim3(kDecThreads), 0, stream,
+    hipLaunchKernelGGL(sparse_decode_mfma_kernel<kDecMfmaWaves>, dim3(ns, Hkv, B), dim3(kDecMfmaWaves * kWave), 0,
+                       stream,
                        (const bf16_t*)q, (const bf16_t*)kp, (const bf16_t*)vp, bt, max_pages, Hkv, G, idx,
                        nsel_cap, n_sel, sel_len, cur_len, order, sl2, chunk, ns, part, out, lse);
     hipError_t e = hipGetLastError();

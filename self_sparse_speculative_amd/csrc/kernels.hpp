@@ -18,6 +18,15 @@ constexpr int kDecChunk = 256;         // attended positions per draft split (ve
 #define S3R_DRAFT_CHUNK 2048
 #endif
 constexpr int kDecChunkMfma = S3R_DRAFT_CHUNK;  // most attended positions per draft split (bf16 x 128 MFMA path)
+#ifndef S3R_DRAFT_WAVES
+#define S3R_DRAFT_WAVES 4
+#endif
+// Waves per draft workgroup (bf16 x 128 MFMA path). With 4, three workgroups
+// share a CU (VGPRs and LDS), so the 1024 (sequence, KV head) pairs of a
+// 128-sequence batch run in one and a third rounds; 2 or 1 waves (every pair
+// resident at once, fewer waves per CU) measured the same at 24K and 4 % /
+// 20 % slower on mixed lengths (4K-24K).
+constexpr int kDecMfmaWaves = S3R_DRAFT_WAVES;
 #ifndef S3R_DRAFT_BALANCE
 #define S3R_DRAFT_BALANCE 1
 #endif
