@@ -772,23 +772,53 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
                             : min(nsplit, ceil_div(S, chunk));
   const int R = (k + 1) * G, Hq = Hkv * G;
   const size_t bkv = (size_t)pair;
+  // Position-form score blocks: the first tile maxima the block's weights need
+  // do not depend on the row statistics, so they are loaded first and arrive
+  // while the statistics are formed. (Loading the code words up front as well
+  // costs more occupancy than the round trip it saves.)
+  float pmv[4];
+  if constexpr (CODES) {
+    if (x >= nblk_o) {
+      const int ms = max_stride(R), tend = min(ceil_div(S, kSub), tile_beg + kFinTiles);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = tid + i * kVerThreads, et = e / R, r = e % R, tile = tile_beg + et;
+        pmv[i] = (e < kFinTiles * R && tile < tend) ? sc_max[(bkv * ntile_cap + tile) * ms + r] : kNegInf;
+      }
+    }
+  }
   // Row statistics: 4 lanes per row, each over every 4th split, then a fixed
-  // butterfly over the 4 lanes (same order in every block).
+  // butterfly over the 4 lanes (same order in every block). Up to 8 splits
+  // each lane loads its (max, sum) pairs once.
   for (int r0 = 0; r0 < R; r0 += kVerThreads / 4) {
     const int r = r0 + tid / 4, c4 = tid & 3;
     float m = kNegInf, l = 0.f;
-    if (r < R) {
-      for (int c = c4; c < used; c += 4) m = fmaxf(m, part_ml[((bkv * nsplit + c) * RP + r) * 2]);
-    }
-    m = fmaxf(m, __shfl_xor(m, 1, kWave));
-    m = fmaxf(m, __shfl_xor(m, 2, kWave));
-    const float base = m == kNegInf ? 0.f : m;
-    if (r < R) {
-      for (int c = c4; c < used; c += 4) {
-        const size_t rc = (bkv * nsplit + c) * RP + r;
-        l += part_ml[rc * 2 + 1] * exp2f_fast(part_ml[rc * 2] - base);
+    if (used <= 8) {
+      float2 ml0 = make_float2(kNegInf, 0.f), ml1 = make_float2(kNegInf, 0.f);
+      if (r < R && c4 < used) ml0 = *reinterpret_cast<const float2*>(part_ml + ((bkv * nsplit + c4) * RP + r) * 2);
+      if (r < R && c4 + 4 < used)
+        ml1 = *reinterpret_cast<const float2*>(part_ml + ((bkv * nsplit + c4 + 4) * RP + r) * 2);
+      m = fmaxf(ml0.x, ml1.x);
+      m = fmaxf(m, __shfl_xor(m, 1, kWave));
+      m = fmaxf(m, __shfl_xor(m, 2, kWave));
+      const float base = m == kNegInf ? 0.f : m;
+      if (r < R && c4 < used) l += ml0.y * exp2f_fast(ml0.x - base);
+      if (r < R && c4 + 4 < used) l += ml1.y * exp2f_fast(ml1.x - base);
+    } else {
+      if (r < R) {
+        for (int c = c4; c < used; c += 4) m = fmaxf(m, part_ml[((bkv * nsplit + c) * RP + r) * 2]);
+      }
+      m = fmaxf(m, __shfl_xor(m, 1, kWave));
+      m = fmaxf(m, __shfl_xor(m, 2, kWave));
+      const float base = m == kNegInf ? 0.f : m;
+      if (r < R) {
+        for (int c = c4; c < used; c += 4) {
+          const size_t rc = (bkv * nsplit + c) * RP + r;
+          l += part_ml[rc * 2 + 1] * exp2f_fast(part_ml[rc * 2] - base);
+        }
       }
     }
+    const float base = m == kNegInf ? 0.f : m;
     l += __shfl_xor(l, 1, kWave);
     l += __shfl_xor(l, 2, kWave);
     if (r < R && c4 == 0) {
@@ -912,7 +942,10 @@ __global__ __launch_bounds__(kVerThreads) void verify_finalize_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = e0 + i * kVerThreads, et = e / R, r = e % R, tile = tile_beg + et;
-      mv[i] = (e < kFinTiles * R && tile < tile_end) ? sc_max[(bkv * ntile_cap + tile) * ms + r] : kNegInf;
+      if (CODES && e0 == tid)
+        mv[i] = pmv[i];  // loaded before the row statistics
+      else
+        mv[i] = (e < kFinTiles * R && tile < tile_end) ? sc_max[(bkv * ntile_cap + tile) * ms + r] : kNegInf;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
