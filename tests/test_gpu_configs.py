@@ -1,12 +1,14 @@
 """GPU parity at the launch shapes the sweep and rollout measurements time.
 
-* verification at k = 2, 4 and 8 on the fixed 24576-position context (7 splits
-  per (sequence, KV head); 12, 20 and 36 query rows per KV head: one, two and
-  three MFMA row tiles, the last with its queries in LDS);
+* verification at every draft length k = 1..8 (the sweep's 2, 4, 6, 8 and the
+  adaptive draft length's rounds) on the fixed 24576-position context (7
+  splits per (sequence, KV head); 8 to 36 query rows per KV head: one, two
+  and three MFMA row tiles, the last with its queries in LDS);
 * selection and draft steps at the sweep's largest budget (s = 1/5, k = 8:
   4916 kept positions, three draft splits merged);
-* speculative sampling on every sequence of every workload (configs 1-4 and
-  the sweep's draft-noise and draft-length points), bit-exact, with the
+* speculative sampling on every sequence of every workload (configs 1-4, the
+  sweep's draft-noise and draft-length points, and the adaptive draft
+  length's noise rising along the draft), bit-exact, with the
   oracle's decision margins reported per workload and required to exceed
   1e-12 (the float64 agreement of the kernel's exponential and summation
   order with the oracle's);
@@ -25,6 +27,7 @@ import torch
 import oracle
 import self_sparse_speculative_amd as s3r
 from s3r_inputs import get_config, make_batch
+from s3r_inputs.configs import DEGRADING_NOISE
 from tests.gpu_util import nsel_cap, rel_err_rows, run_draft_steps, run_select, run_verify, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -45,7 +48,7 @@ def _check_verify(cfg, batch, out, lse, sc, seqs):
         print(f"  seq {b}: out {eo:.3g}, scores {es:.3g}", flush=True)
 
 
-@pytest.mark.parametrize("k", [2, 4, 8])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_verify_sweep_draft_lengths_at_24k(k):
     cfg = get_config(5, B=2, k=k)
     print(f"[sweep verify] k={k} R={(k + 1) * cfg.G} B=2 L=24576", flush=True)
@@ -85,8 +88,11 @@ SAMPLING_WORKLOADS = [
     ("config 5 sigma=0.1", 5, {"noise_std": 0.1}),
     ("config 5 sigma=0.3", 5, {}),
     ("config 5 sigma=0.6", 5, {"noise_std": 0.6}),
+    ("config 5 k=1", 5, {"k": 1}),
     ("config 5 k=2", 5, {"k": 2}),
+    ("config 5 k=4", 5, {"k": 4}),
     ("config 5 k=8", 5, {"k": 8}),
+    ("config 5 k=8, noise rising along the draft", 5, {"k": 8, "noise_by_position": DEGRADING_NOISE}),
 ]
 
 
