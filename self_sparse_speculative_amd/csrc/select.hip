@@ -129,6 +129,10 @@ constexpr int kSpCapMax = 8192;
 #define S3R_SELECT_SEG 4
 #endif
 constexpr int kSpSeg = S3R_SELECT_SEG;  // consecutive keys per thread per step of the collecting pass
+#ifndef S3R_SELECT_PREFETCH
+#define S3R_SELECT_PREFETCH 1
+#endif
+constexpr bool kSpPrefetch = S3R_SELECT_PREFETCH != 0;  // next step's keys loaded during this step's scan
 
 // Sample rank of t0 for `ntop` wanted keys out of `ncand`, sampling `ns` keys.
 __host__ __device__ __forceinline__ int sampled_want(int ntop, int ncand, int ns) {
@@ -221,11 +225,26 @@ __device__ bool sampled_select(const float* __restrict__ row, int ncand, int nto
   // 2. ordered collection of the keys >= t0: each thread takes kSpSeg
   // consecutive positions per step, so thread order is position order
   int total = 0;
+  // the next step's scores are loaded before this step's scan (kSpPrefetch),
+  // so each step's loads are in flight during the previous step's scan
+  float nxt[kSpSeg];
+  auto load_step = [&](int base) {
+    const int j0 = base + kSpSeg * tid;
+#pragma unroll
+    for (int v = 0; v < kSpSeg; ++v) nxt[v] = j0 + v < ncand ? row[j0 + v] : 0.f;
+  };
+  if (kSpPrefetch) load_step(0);
   for (int base = 0; base < ncand; base += kSpSeg * kFsThreads) {
     const int j0 = base + kSpSeg * tid;
     uint32_t kk[kSpSeg];
+    if (kSpPrefetch) {
 #pragma unroll
-    for (int v = 0; v < kSpSeg; ++v) kk[v] = j0 + v < ncand ? score_key(row[j0 + v]) : 0u;
+      for (int v = 0; v < kSpSeg; ++v) kk[v] = j0 + v < ncand ? score_key(nxt[v]) : 0u;
+      if (base + kSpSeg * kFsThreads < ncand) load_step(base + kSpSeg * kFsThreads);
+    } else {
+#pragma unroll
+      for (int v = 0; v < kSpSeg; ++v) kk[v] = j0 + v < ncand ? score_key(row[j0 + v]) : 0u;
+    }
     int c = 0;
 #pragma unroll
     for (int v = 0; v < kSpSeg; ++v) c += (j0 + v < ncand && kk[v] >= t0) ? 1 : 0;
