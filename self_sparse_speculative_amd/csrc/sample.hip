@@ -303,19 +303,28 @@ __global__ __launch_bounds__(kSmpThreads) void chunk_sum_kernel(
   const float* zr = zt + ((size_t)b * (k + 1) + istar) * V;
   const float* dr = resid ? zd + ((size_t)b * k + istar) * V : nullptr;
   const float mt = smax[so + istar];
-  const double inv_st = 1.0 / ssum[so + istar];
+  const double st = ssum[so + istar];
   const float md = resid ? smax[so + k + 1 + istar] : 0.f;
-  const double inv_sd = resid ? 1.0 / ssum[so + k + 1 + istar] : 1.0;
+  const double sd = resid ? ssum[so + k + 1 + istar] : 1.0;
   double aw = 0.0, ap = 0.0;
-  constexpr int U = 4;  // loads in flight per thread
-  for (int y0u = y0 + tid; y0u < y1; y0u += U * kSmpThreads) {
-    float zt_v[U], zd_v[U];
+  // Loads in flight per thread: a whole chunk of the vocabulary in one step
+  // for V up to 64 x 256 x U, issued before the row statistics are waited on,
+  // so a workgroup pays two memory round trips (descriptor, then statistics
+  // and logits together).
+  constexpr int U = 10;
+  float zt_v[U], zd_v[U];
+  auto load_step = [&](int y0u) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int y = y0u + u * kSmpThreads;
       zt_v[u] = y < y1 ? zr[y] : 0.f;
       zd_v[u] = (resid && y < y1) ? dr[y] : 0.f;
     }
+  };
+  load_step(y0 + tid);
+  const double inv_st = 1.0 / st, inv_sd = resid ? 1.0 / sd : 1.0;
+  for (int y0u = y0 + tid; y0u < y1; y0u += U * kSmpThreads) {
+    if (y0u != y0 + tid) load_step(y0u);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (y0u + u * kSmpThreads >= y1) continue;
