@@ -25,6 +25,9 @@ CASES = [
     ("k=8 36 rows (queries in LDS)", 5, {"B": 2, "k": 8}, ("uniform", 900, 3000)),
     ("k=15 64 rows", 3, {"B": 2, "k": 15}, ("uniform", 100, 2100)),
     ("24K, 7 splits", 5, {"B": 2}, None),
+    ("24K k=2, 7 splits", 5, {"B": 2, "k": 2}, None),
+    ("24K k=4, 7 splits", 5, {"B": 2, "k": 4}, None),
+    ("24K k=8, 7 splits (queries in LDS)", 5, {"B": 2, "k": 8}, None),
     ("62K-66K, 16 splits", 3, {"B": 2}, ("uniform", 62000, 66000)),
 ]
 
