@@ -101,12 +101,9 @@ s3r_status s3r_select_grouped(const float* scores, int32_t score_stride, const i
   const size_t need = s3r::grouped_select_plan(B, Hkv, max_ctx_len, s_num, s_den, window, unit,
                                                all_heads ? 1 : 0).bytes;
   if (ws_bytes < need || ws == nullptr) return S3R_ERR_WORKSPACE;
-  if (order != nullptr) {
-    const hipError_t e = s3r::launch_length_order(ctx_len, B, order, stream);
-    if (e != hipSuccess) return from_hip(e);
-  }
   return from_hip(s3r::launch_select_grouped(scores, score_stride, ctx_len, B, Hkv, max_ctx_len, s_num, s_den,
-                                             window, unit, all_heads ? 1 : 0, idx, nsel_cap, n_sel, ws, stream));
+                                             window, unit, all_heads ? 1 : 0, idx, nsel_cap, n_sel, order, ws,
+                                             stream));
 }
 
 s3r_status s3r_select_pages(const float* page_scores, int32_t page_stride, const int32_t* ctx_len, int32_t B,
@@ -122,12 +119,8 @@ s3r_status s3r_select_pages(const float* page_scores, int32_t page_stride, const
   const size_t need = s3r::grouped_select_plan(B, Hkv, max_ctx_len, s_num, s_den, window, 16,
                                                all_heads ? 1 : 0).bytes;
   if (ws_bytes < need || ws == nullptr) return S3R_ERR_WORKSPACE;
-  if (order != nullptr) {
-    const hipError_t e = s3r::launch_length_order(ctx_len, B, order, stream);
-    if (e != hipSuccess) return from_hip(e);
-  }
   return from_hip(s3r::launch_select_pages(page_scores, page_stride, ctx_len, B, Hkv, max_ctx_len, s_num, s_den,
-                                           window, all_heads ? 1 : 0, idx, nsel_cap, n_sel, ws, stream));
+                                           window, all_heads ? 1 : 0, idx, nsel_cap, n_sel, order, ws, stream));
 }
 
 size_t s3r_sparse_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head_dim, int32_t max_attend) {

@@ -129,12 +129,13 @@ GroupedSelectPlan grouped_select_plan(int B, int Hkv, int max_ctx_len, int s_num
                                       int unit, int all_heads);
 int grouped_select_capacity(int max_ctx_len, int s_num, int s_den, int window, int unit);
 // Whole-page selection from scores given per page (stride >= max_ctx_len / 16).
+// order (nullable): the draft steps' dispatch order, written by the last kernel.
 hipError_t launch_select_pages(const float* page_scores, int stride, const int* ctx_len, int B, int Hkv,
                                int max_ctx_len, int s_num, int s_den, int window, int all_heads, int* idx,
-                               int nsel_cap, int* n_sel, void* ws, hipStream_t stream);
+                               int nsel_cap, int* n_sel, int* order, void* ws, hipStream_t stream);
 hipError_t launch_select_grouped(const float* scores, int stride, const int* ctx_len, int B, int Hkv,
                                  int max_ctx_len, int s_num, int s_den, int window, int unit, int all_heads,
-                                 int* idx, int nsel_cap, int* n_sel, void* ws, hipStream_t stream);
+                                 int* idx, int nsel_cap, int* n_sel, int* order, void* ws, hipStream_t stream);
 
 // Measurement: the read patterns of the verification and of a draft step.
 size_t read_verify_pattern_words(int B, int Hkv, int max_seq_len);

@@ -645,11 +645,33 @@ __global__ __launch_bounds__(256) void page_keys_kernel(
   keys[((size_t)b * gridDim.z + g) * kstride + u] = v;
 }
 
+// Also, when order is given, the draft steps' dispatch order (longest context
+// first, ties by index; as s3r_length_order): the KV-head-0 workgroup of
+// sequence b writes order[rank of b] = b, so no kernel of its own runs for it.
 template <bool PAGES>
 __global__ __launch_bounds__(256) void expand_kernel(
     const int* __restrict__ sel_u, int cap_u, int G, const int* __restrict__ n_u, const int* __restrict__ units,
-    const int* __restrict__ wcount, int Hkv, int* __restrict__ idx, int nsel_cap, int* __restrict__ n_sel) {
+    const int* __restrict__ wcount, int Hkv, int* __restrict__ idx, int nsel_cap, int* __restrict__ n_sel,
+    const int* __restrict__ ctx_len, int* __restrict__ order) {
   const int h = blockIdx.x, b = blockIdx.y;
+  if (order != nullptr && h == 0) {
+    __shared__ int wrank[256 / kWave];
+    const int B = gridDim.y, L = ctx_len[b];
+    int c = 0;
+    for (int j = threadIdx.x; j < B; j += 256) {
+      const int lj = ctx_len[j];
+      c += (lj > L || (lj == L && j < b)) ? 1 : 0;
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, kWave);
+    if ((threadIdx.x & (kWave - 1)) == 0) wrank[threadIdx.x / kWave] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int rank = 0;
+      for (int w = 0; w < 256 / kWave; ++w) rank += wrank[w];
+      order[rank] = b;
+    }
+  }
   const int g = G == 1 ? 0 : h;
   const int* src = sel_u + ((size_t)b * G + g) * cap_u;
   const int nt = n_u[b];
@@ -702,7 +724,7 @@ int grouped_select_capacity(int max_ctx_len, int s_num, int s_den, int window, i
 
 hipError_t launch_select_pages(const float* page_scores, int stride, const int* ctx_len, int B, int Hkv,
                                int max_ctx_len, int s_num, int s_den, int window, int all_heads, int* idx,
-                               int nsel_cap, int* n_sel, void* ws, hipStream_t stream) {
+                               int nsel_cap, int* n_sel, int* order, void* ws, hipStream_t stream) {
   const GroupedSelectPlan p = grouped_select_plan(B, Hkv, max_ctx_len, s_num, s_den, window, kPage, all_heads);
   char* w = static_cast<char*>(ws);
   float* keys = reinterpret_cast<float*>(w + p.off_keys);
@@ -723,13 +745,13 @@ hipError_t launch_select_pages(const float* page_scores, int stride, const int* 
                      p.kstride, units, p.G, s_num, s_den, 0, sel, p.cap_u, nsel_u, (const int*)top, cap,
                      (int*)nullptr);
   hipLaunchKernelGGL(expand_kernel<true>, dim3(Hkv, B), dim3(256), 0, stream, sel, p.cap_u, p.G, nsel_u, units, wc,
-                     Hkv, idx, nsel_cap, n_sel);
+                     Hkv, idx, nsel_cap, n_sel, ctx_len, order);
   return hipGetLastError();
 }
 
 hipError_t launch_select_grouped(const float* scores, int stride, const int* ctx_len, int B, int Hkv,
                                  int max_ctx_len, int s_num, int s_den, int window, int unit, int all_heads,
-                                 int* idx, int nsel_cap, int* n_sel, void* ws, hipStream_t stream) {
+                                 int* idx, int nsel_cap, int* n_sel, int* order, void* ws, hipStream_t stream) {
   const GroupedSelectPlan p = grouped_select_plan(B, Hkv, max_ctx_len, s_num, s_den, window, unit, all_heads);
   char* w = static_cast<char*>(ws);
   float* keys = reinterpret_cast<float*>(w + p.off_keys);
@@ -749,7 +771,7 @@ hipError_t launch_select_grouped(const float* scores, int stride, const int* ctx
                        p.kstride, ctx_len, 1, s_num, s_den, window, sel, p.cap_u, nsel_u, (const int*)nullptr, cap,
                        (int*)nullptr);
     hipLaunchKernelGGL(expand_kernel<false>, dim3(Hkv, B), dim3(256), 0, stream, sel, p.cap_u, 1, nsel_u, units,
-                       wc, Hkv, idx, nsel_cap, n_sel);
+                       wc, Hkv, idx, nsel_cap, n_sel, ctx_len, order);
   } else {
     if (all_heads)
       hipLaunchKernelGGL((group_keys_kernel<true, true>), kgrid, dim3(256), 0, stream, scores, stride, ctx_len,
@@ -762,7 +784,7 @@ hipError_t launch_select_grouped(const float* scores, int stride, const int* ctx
                        p.kstride, units, p.G, s_num, s_den, 0, sel, p.cap_u, nsel_u, (const int*)top, cap,
                        (int*)nullptr);
     hipLaunchKernelGGL(expand_kernel<true>, dim3(Hkv, B), dim3(256), 0, stream, sel, p.cap_u, p.G, nsel_u, units,
-                       wc, Hkv, idx, nsel_cap, n_sel);
+                       wc, Hkv, idx, nsel_cap, n_sel, ctx_len, order);
   }
   return hipGetLastError();
 }

@@ -23,10 +23,13 @@ def _check(cfg, scores_np, ctx_np, unit, all_heads, s_num=None, s_den=None, wind
     window = cfg.window if window is None else window
     B, Hkv, _ = scores_np.shape
     max_ctx = int(ctx_np.max())
+    order = torch.full((B,), -1, dtype=torch.int32, device="cuda")
     idx, n_sel = s3r.select_grouped(torch.from_numpy(scores_np).cuda(), torch.from_numpy(ctx_np).cuda(), max_ctx,
-                                    s_num, s_den, window, unit=unit, all_heads=all_heads)
+                                    s_num, s_den, window, unit=unit, all_heads=all_heads, order=order)
     torch.cuda.synchronize()
     idx, n_sel = idx.cpu().numpy(), n_sel.cpu().numpy()
+    # the draft steps' dispatch order, written in the same launch: longest first, ties by index
+    assert np.array_equal(order.cpu().numpy(), np.argsort(-ctx_np.astype(np.int64), kind="stable"))
     for b in range(B):
         L = int(ctx_np[b])
         ref = oracle.select_grouped(scores_np[b], L, s_num, s_den, window, unit, all_heads)
@@ -50,7 +53,7 @@ def test_variants_match_oracle_on_generator_scores(cid, ov, unit, all_heads):
 def test_variants_tie_heavy_and_edge_lengths(unit, all_heads):
     cfg = get_config(1, B=9, Hkv=3)
     rng = np.random.default_rng(11)
-    ctx = np.array([1, 7, 15, 16, 17, 40, 100, 511, 2000], dtype=np.int32)
+    ctx = np.array([1, 7, 15, 16, 17, 40, 17, 511, 2000], dtype=np.int32)  # a tie: the order keeps index order
     sc = rng.integers(0, 4, size=(9, 3, 2000)).astype(np.float32)  # equal page sums everywhere
     sc[0, :, :5] = -0.0
     for (sn, sd, W) in ((1, 20, 16), (1, 5, 0), (1, 1, 16), (1, 3, 40)):
