@@ -242,7 +242,8 @@ s3r_status s3r_sparse_decode_attn(const void* q, const s3r_paged_kv* kv, const i
  * is the sequence of rank r when the sequences are sorted by descending
  * len[b], ties by ascending b (a stable sort). Not part of the method's
  * arithmetic: it only arranges when each sequence's workgroups run.
- * s3r_select forms the same order in its own launch.
+ * s3r_select, s3r_select_grouped and s3r_select_pages form the same order in
+ * their own launches when given an order array.
  *
  *   len    device i32 [B] (e.g. the context lengths L_b of the round);
  *   order  device i32 [B], written.
