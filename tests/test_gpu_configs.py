@@ -126,6 +126,32 @@ def test_spec_sample_every_sequence_with_margins(name, cid, ov):
     assert rmin > MARGIN_FLOOR and dmin > MARGIN_FLOOR
 
 
+def test_spec_sample_vocabulary_not_a_multiple_of_four():
+    # V = 4099: the row statistics take their scalar path (no float4 loads) and the last
+    # vocabulary chunk is ragged; N(0, 3) target logits, draft = target + N(0, 0.6)
+    rng = np.random.default_rng(32)
+    B, k, V = 64, 6, 4099
+    zt = (3.0 * rng.standard_normal((B, k + 1, V))).astype(np.float32)
+    zd = (zt[:, :k] + 0.6 * rng.standard_normal((B, k, V))).astype(np.float32)
+    q_rows = [[oracle.softmax_t(zd[b, i], 1.0) for i in range(k)] for b in range(B)]
+    d = np.array([[oracle.invcdf(q_rows[b][i], rng.random()) for i in range(k)] for b in range(B)], np.int32)
+    u = rng.random((B, k + 1), dtype=np.float32)
+    dev = torch.device("cuda")
+    toks, nout, acc = s3r.spec_sample(torch.from_numpy(zt).to(dev), torch.from_numpy(zd).to(dev),
+                                      torch.from_numpy(d).to(dev), torch.from_numpy(u).to(dev), 1.0)
+    torch.cuda.synchronize()
+    toks, nout, acc = toks.cpu().numpy(), nout.cpu().numpy(), acc.cpu().numpy()
+    rmin = dmin = np.inf
+    for b in range(B):
+        p_rows = [oracle.softmax_t(zt[b, i], 1.0) for i in range(k + 1)]
+        rt, rn, ra = oracle.spec_decide(p_rows, q_rows[b], d[b], u[b])
+        assert nout[b] == rn and np.array_equal(toks[b], rt) and np.array_equal(acc[b], ra), b
+        rm, dm = oracle.decide_margins(p_rows, q_rows[b], d[b], u[b])
+        rmin, dmin = min(rmin, rm), min(dmin, dm)
+    print(f"[margins] V=4099: {B} sequences bit-exact; min ratio-test margin {rmin:.3e}, min draw margin {dmin:.3e}")
+    assert rmin > MARGIN_FLOOR and dmin > MARGIN_FLOOR
+
+
 def test_rollout_benchmark_inputs_middle_layer():
     """The rollout workload exactly as the benchmark times it: full batch of 256 (32 prompts x 8
     responses, 1024-token prompt pages shared), pages drawn on the device, layer 14."""

@@ -437,6 +437,33 @@ def test_spec_sample_greedy_and_identical():
     assert (acc.cpu().numpy() == 1).all()
 
 
+def test_spec_sample_greedy_with_tied_maxima():
+    # integer logits: every row's maximum is taken by several tokens, so the greedy decisions
+    # and outputs rest on the first-index rule alone; drafts are the first argmax, a later tied
+    # token or a random one
+    rng = np.random.default_rng(31)
+    B, k, V = 48, 6, 4099
+    zt = rng.integers(0, 3, (B, k + 1, V)).astype(np.float32)
+    zd = rng.integers(0, 3, (B, k, V)).astype(np.float32)
+    d = np.empty((B, k), np.int32)
+    for b in range(B):
+        for i in range(k):
+            tied = np.flatnonzero(zt[b, i] == zt[b, i].max())
+            d[b, i] = (tied[0], tied[-1], rng.integers(0, V))[rng.integers(0, 3) if b % 4 else 0]
+    u = rng.random((B, k + 1), dtype=np.float32)
+    dev = torch.device("cuda")
+    toks, nout, acc = s3r.spec_sample(torch.from_numpy(zt).to(dev), torch.from_numpy(zd).to(dev),
+                                      torch.from_numpy(d).to(dev), torch.from_numpy(u).to(dev), 0.0)
+    torch.cuda.synchronize()
+    toks, nout = toks.cpu().numpy(), nout.cpu().numpy()
+    full = 0
+    for b in range(B):
+        rt, rn, _ = oracle.spec_sample(zt[b], zd[b], d[b], u[b], np.float32(0.0))
+        assert nout[b] == rn and np.array_equal(toks[b], rt), (b, toks[b], rt)
+        full += int(rn == k + 1)
+    assert full > 0 and int(nout.min()) == 1  # both whole acceptance and an early rejection occur
+
+
 def test_spec_sample_chi_square_on_gpu():
     from scipy import stats
     V, k, n = 16, 3, 400_000
