@@ -378,6 +378,36 @@ def test_ragged_short_contexts():
     _check_select(cfg, batch, batch.scores, idx, n_sel, [(b, kv) for b in range(cfg.B) for kv in range(cfg.Hkv)])
 
 
+def test_split_and_selection_path_boundaries():
+    # verification lengths S = L + 7 at and around the split size (4096: one split or two;
+    # 8192 and 8193: two even splits or three; 12288), and selection rows of 2047, 2048 and
+    # 2049 candidates (L - 64), where the sampled-threshold path begins
+    L = [4088, 4089, 4090, 8185, 8186, 12281, 2111, 2112, 2113]
+    cfg = get_config(3, B=len(L))
+    batch = make_batch(cfg, lengths=np.array(L, np.int32))
+    t = to_dev(batch)
+    print(f"[boundaries] S = {list(batch.seq_len)}", flush=True)
+    _verify_case(cfg, batch, t, range(cfg.B), False)
+    _draft_case(cfg, batch, t, [1, cfg.k], range(cfg.B), TOL_BF16, False)
+    idx, n_sel = run_select(cfg, batch, t)
+    torch.cuda.synchronize()
+    _check_select(cfg, batch, batch.scores, idx, n_sel, [(b, kv) for b in range(cfg.B) for kv in range(cfg.Hkv)])
+    # the page-score form on the same lengths: its rows equal the position form's, bit for bit
+    ms = int(batch.seq_len.max())
+    o1, l1, _ = run_verify(cfg, batch, t)
+    o2, l2, pg = s3r.verify_attn_pages(t["q_verify"], t["kv"], t["seq_len"], cfg.k, float(batch.scale), ms)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    pg = pg.cpu().numpy()
+    for b in range(cfg.B):
+        S = int(batch.seq_len[b])
+        _, _, rs = oracle.verify(batch.q_verify[b], batch.k_pages, batch.v_pages, batch.block_table[b], S, cfg.k,
+                                 float(batch.scale))
+        ref = oracle.page_scores(rs, S)
+        err = float((np.abs(pg[b, :, :ref.shape[1]] - ref).max(axis=1) / ref.max(axis=1)).max())
+        assert err <= TOL_BF16, (b, err)
+
+
 # ----------------------------------------------------------------- sampling
 
 def _check_sample(cfg, batch, toks, nout, acc, T, seqs):
