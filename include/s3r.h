@@ -363,7 +363,9 @@ s3r_status s3r_verify_scores(const s3r_paged_kv* kv, const int32_t* seq_len, int
  *   of target row i; correction and bonus are that argmax.
  *
  *   target_logits device f32 [B][k+1][V]; draft_logits device f32 [B][k][V]
- *   (may be NULL when k = 0); draft_tokens device i32 [B][k] in [0, V);
+ *   (may be NULL when k = 0); a logit of -inf is a token of probability 0 (a
+ *   masked or padded vocabulary entry); NaN or +inf logits, or a row with no
+ *   finite logit, are undefined behaviour; draft_tokens device i32 [B][k] in [0, V);
  *   uniforms device f32 [B][k+1] in [0, 1); temperature >= 0 (host).
  *   tokens    device i32 [B][k+1] output: the n_out[b] emitted tokens, then -1.
  *   n_out     device i32 [B] output: accepted drafts + 1.

@@ -152,6 +152,38 @@ def test_spec_sample_vocabulary_not_a_multiple_of_four():
     assert rmin > MARGIN_FLOOR and dmin > MARGIN_FLOOR
 
 
+def test_spec_sample_with_masked_tokens():
+    # -inf logits (tokens that cannot be drawn: a masked or padded vocabulary) in the target
+    # and draft rows, a different third of the vocabulary per row; exact as elsewhere
+    rng = np.random.default_rng(33)
+    B, k, V = 48, 6, 2048
+    zt = (3.0 * rng.standard_normal((B, k + 1, V))).astype(np.float32)
+    zd = (zt[:, :k] + 0.6 * rng.standard_normal((B, k, V))).astype(np.float32)
+    zt[rng.random(zt.shape) < 1 / 3] = -np.inf
+    zd[rng.random(zd.shape) < 1 / 3] = -np.inf
+    zt[:, :, V - 256:] = -np.inf  # a padded tail in every target row
+    q_rows = [[oracle.softmax_t(zd[b, i], 1.0) for i in range(k)] for b in range(B)]
+    d = np.array([[oracle.invcdf(q_rows[b][i], rng.random()) for i in range(k)] for b in range(B)], np.int32)
+    u = rng.random((B, k + 1), dtype=np.float32)
+    dev = torch.device("cuda")
+    toks, nout, acc = s3r.spec_sample(torch.from_numpy(zt).to(dev), torch.from_numpy(zd).to(dev),
+                                      torch.from_numpy(d).to(dev), torch.from_numpy(u).to(dev), 1.0)
+    torch.cuda.synchronize()
+    toks, nout, acc = toks.cpu().numpy(), nout.cpu().numpy(), acc.cpu().numpy()
+    rmin = dmin = np.inf
+    for b in range(B):
+        p_rows = [oracle.softmax_t(zt[b, i], 1.0) for i in range(k + 1)]
+        rt, rn, ra = oracle.spec_decide(p_rows, q_rows[b], d[b], u[b])
+        assert nout[b] == rn and np.array_equal(toks[b], rt) and np.array_equal(acc[b], ra), b
+        emitted = toks[b, :rn]
+        assert np.isfinite(zt[b, np.arange(rn), emitted][-1:]).all()  # the drawn token is never masked
+        rm, dm = oracle.decide_margins(p_rows, q_rows[b], d[b], u[b])
+        rmin, dmin = min(rmin, rm), min(dmin, dm)
+    print(f"[margins] masked tokens: {B} sequences bit-exact; min ratio-test margin {rmin:.3e}, "
+          f"min draw margin {dmin:.3e}")
+    assert rmin > MARGIN_FLOOR and dmin > MARGIN_FLOOR
+
+
 def test_rollout_benchmark_inputs_middle_layer():
     """The rollout workload exactly as the benchmark times it: full batch of 256 (32 prompts x 8
     responses, 1024-token prompt pages shared), pages drawn on the device, layer 14."""
